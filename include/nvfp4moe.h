@@ -1,0 +1,218 @@
+/*
+ * nvfp4moe.h — C ABI of the NVFP4 block-scaled MoE expert forward for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method: the "NVFP4 MegaMoE Kernel" README (sections "What We Have",
+ * "Fused SwiGLU — How It Works", "Correctness Bugs Fixed", "Key Lessons") and
+ * the "CURRENT_BUG.md" page (section "What Works").
+ *
+ * NVFP4 tensor of R rows and C columns (C % 16 == 0), row-major:
+ *   codes  uint8[R][C/2]   two E2M1 codes per byte along the row, element 2j
+ *                          in the low nibble, bit 3 of a code is the sign;
+ *   scales uint8[R][C/16]  one OCP E4M3 (bias 7, max 448) per 16 elements;
+ *   gs     float           global scale; a value is E2M1 * E4M3 / gs.
+ * BF16 tensors are passed as raw 16-bit patterns (uint16_t / void*).
+ *
+ * Common rules for every entry point:
+ *   - all data pointers are DEVICE pointers owned by the caller; the library
+ *     never frees or retains them;
+ *   - work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
+ *     null stream); nothing allocates memory, synchronises the host or reads
+ *     device data on the host, so every call can be captured in a hipGraph;
+ *   - arguments are validated on the host BEFORE any HIP call; a failed check
+ *     returns an error status and enqueues nothing; nvfp4_last_error()
+ *     returns a thread-local description of the last failure;
+ *   - the current HIP device must be a gfx950 (else NVFP4_ERR_ARCH);
+ *   - inputs must be finite (no NaN/Inf in BF16 data).
+ */
+#ifndef NVFP4MOE_H
+#define NVFP4MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int nvfp4_status;
+#define NVFP4_OK               0
+#define NVFP4_ERR_INVALID_ARG (-1) /* null pointer, bad enum value         */
+#define NVFP4_ERR_SHAPE       (-2) /* a size breaks the shape rules        */
+#define NVFP4_ERR_WORKSPACE   (-3) /* workspace missing or too small       */
+#define NVFP4_ERR_ARCH        (-4) /* current device is not gfx950         */
+#define NVFP4_ERR_HIP         (-5) /* a HIP call failed (text in last_error) */
+
+/* Static description of a status code. */
+const char* nvfp4_status_string(nvfp4_status status);
+/* Thread-local text of the last failure in this thread ("" if none). */
+const char* nvfp4_last_error(void);
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int nvfp4_version(void);
+
+/* ------------------------------------------------------------------------
+ * Weight layout (untimed preparation).
+ * README "What We Have", bridge layer: gate/up interleave of the L1 weight
+ * at granularity 8 and conversion of B to K-major; "Fused SwiGLU — How It
+ * Works": interleaved output columns read [gate0-7, up0-7, gate8-15, ...].
+ *
+ * For each of `groups` matrices src[g] (rows x cols, BF16, row-major),
+ * writes dst[g] = transpose (cols x rows).  With interleave_gate_up != 0 the
+ * src columns are [gate | up] (cols = 2I, I % 8 == 0) and dst row n holds
+ * src column  8*(n/16) + n%8        for n%16 <  8  (gate),
+ *             I + 8*(n/16) + n%8 - 8 for n%16 >= 8 (up).
+ * Shapes: groups >= 0, rows >= 1, cols >= 1; with interleave cols % 16 == 0.
+ * src and dst must not overlap.
+ * ---------------------------------------------------------------------- */
+nvfp4_status nvfp4_weight_layout(const void* src_bf16, int64_t groups, int64_t rows,
+                                 int64_t cols, int interleave_gate_up, void* dst_bf16,
+                                 void* stream);
+
+/* ------------------------------------------------------------------------
+ * Quantise BF16 -> NVFP4.
+ * README "What We Have", bridge layer: BF16 -> NVFP4 with a global scale,
+ * a variant with a pre-computed global scale, weights quantised along K;
+ * README "Correctness Bugs Fixed": an all-zero 16-block gets scale exactly 0
+ * (bug 3); a block whose amax after the global scale is below 6*2^-9 is
+ * zeroed, scale 0 (bug 4); CURRENT_BUG.md "What Works": the activation global
+ * scale is recomputed per call.
+ *
+ * x: BF16 [groups*rows_per_group][cols]; every group is quantised along its
+ * rows (the contiguous axis) with its own global scale:
+ *   gs_in == NULL: gs[g] = fl32(2688 / amax(group g)), or 1 for an all-zero
+ *                  group, computed on the device and written to gs_out[g];
+ *   gs_in != NULL: device float[groups] used as given and copied to gs_out.
+ * Per 16-block (fp32, round-to-nearest-even everywhere):
+ *   a_s = amax*gs; zero/underflow (amax == 0 or a_s < 6*2^-9): scale 0x00 and
+ *   codes 0; else sf = E4M3(min(a_s/6, 448)), r = gs/sf,
+ *   code = signbit(x) << 3 | E2M1(min(|x*r|, 6)).
+ * Outputs: q uint8 [groups*rows][cols/2], sf uint8 [groups*rows][cols/16],
+ *   gs_out float [groups] (all device).
+ * Shapes: groups >= 0, rows_per_group >= 0, cols >= 16, cols % 16 == 0.
+ * Workspace: nvfp4_quantize_workspace_size() bytes (0 allowed with NULL).
+ * ---------------------------------------------------------------------- */
+size_t nvfp4_quantize_workspace_size(int64_t groups, int64_t rows_per_group, int64_t cols);
+nvfp4_status nvfp4_quantize(const void* x_bf16, int64_t groups, int64_t rows_per_group,
+                            int64_t cols, const float* gs_in, uint8_t* q, uint8_t* sf,
+                            float* gs_out, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Expert offsets and expert-order permutation.
+ * README "Correctness Bugs Fixed", bug 5: a histogram, not an O(n x E) mask;
+ * README "Key Lessons" 4: quantise compact rows, then place them.
+ *
+ * topk_ids: device int32 [T][k].  Flat index f = t*k + j.
+ * Outputs (device int32):
+ *   expert_offsets [E+1]: rows of expert e are [off[e], off[e+1]);
+ *                         off[E] = number of valid pairs;
+ *   perm [T*k]:           perm[d] = f of row d; rows are ordered by expert,
+ *                         and by increasing f inside an expert (stable);
+ *   inv_perm [T*k]:       inv_perm[f] = d;
+ *   invalid_count [1]:    (nullable) number of ids outside [0, E); those
+ *                         pairs are placed after off[E] in increasing f and
+ *                         are skipped by the GEMMs and the combine.
+ * Shapes: T >= 0, 1 <= k <= 64, 1 <= E <= 4096, T*k < 2^31.
+ * Workspace: nvfp4_moe_route_workspace_size() bytes.
+ * ---------------------------------------------------------------------- */
+size_t nvfp4_moe_route_workspace_size(int64_t T, int k, int E);
+nvfp4_status nvfp4_moe_route(const int32_t* topk_ids, int64_t T, int k, int E,
+                             int32_t* expert_offsets, int32_t* perm, int32_t* inv_perm,
+                             int32_t* invalid_count, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Expert-grouped NVFP4 GEMM.
+ * README "What We Have", grouped GEMM: A(M,K) x B(E,K,N) -> C(M,N), per-16
+ * FP8 scales on A and B, per-expert global scales; "Fused SwiGLU — How It
+ * Works": SwiGLU epilogue over columns interleaved at 8; "Remaining Steps" 2:
+ * NVFP4 quantise in the epilogue (per-16 amax, FP8 scale, FP4 pack).
+ *
+ * Row d of the grouped operand (0 <= d < off[E], off = expert_offsets) is
+ * A row  a_row_src[d] / a_row_div  (a_row_src != NULL, gather), or A row d.
+ * For e in [0, E) and d in [off[e], off[e+1]):
+ *   acc[d][n] = sum_k dec(A)[d][k] * dec(B[e])[n][k] / (gs_a[0] * gs_b[e]),
+ *   dec = E2M1 * E4M3 (exact), fp32 accumulation.
+ * A: a_q uint8 [rows_a][K/2], a_sf uint8 [rows_a][K/16], gs_a float[1].
+ * B: b_q uint8 [E][N][K/2], b_sf uint8 [E][N][K/16], gs_b float[E]
+ *    (K-major, i.e. the weight's N rows each hold K elements).
+ * epilogue NVFP4_EPI_BF16: c_bf16 [M][N] = bf16_rne(acc).
+ * epilogue NVFP4_EPI_SWIGLU_NVFP4: N = 2I interleaved at 8 (see
+ *   nvfp4_weight_layout); h[d][c] = silu(gate) * up in fp32 with
+ *   gate = acc[d][16*(c/8) + c%8], up = acc[d][16*(c/8) + 8 + c%8];
+ *   h is quantised along c with the pre-computed global scale gs_out[0]
+ *   (same block rule as nvfp4_quantize) into c_q uint8 [M][I/2] and
+ *   c_sf uint8 [M][I/16]; c_debug_f32 (nullable) [M][I] receives h.
+ * Rows d >= off[E] are not written.  Requires off[E] <= M (M = rows of C).
+ * Shapes: E >= 1, M >= 0, K % 128 == 0, K >= 128, N % 32 == 0, N >= 32;
+ *   SwiGLU: N % 32 == 0 (I % 16 == 0).
+ * Unused output pointers of the other epilogue may be NULL.
+ * Workspace: none (ws may be NULL; ws_bytes ignored).
+ * ---------------------------------------------------------------------- */
+#define NVFP4_EPI_BF16 0
+#define NVFP4_EPI_SWIGLU_NVFP4 1
+nvfp4_status nvfp4_grouped_gemm(int epilogue, const uint8_t* a_q, const uint8_t* a_sf,
+                                const float* gs_a, const int32_t* a_row_src, int a_row_div,
+                                const int32_t* expert_offsets, int E, int64_t M, int64_t N,
+                                int64_t K, const uint8_t* b_q, const uint8_t* b_sf,
+                                const float* gs_b, const float* gs_out, void* c_bf16,
+                                uint8_t* c_q, uint8_t* c_sf, float* c_debug_f32, void* ws,
+                                size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Routing-weighted combine.
+ * README "What We Have", MoE runner step 6: scatter with routing weights.
+ *
+ * out[t][n] = bf16_rne( sum_{j=0..k-1} w[t][j] * y[inv_perm[t*k+j]][n] ),
+ * fp32 sum in slot order j; rows inv_perm >= expert_offsets[E] (invalid
+ * expert ids) contribute nothing.
+ * y: BF16 [T*k][H] in expert order; topk_w float [T][k]; out BF16 [T][H].
+ * Shapes: T >= 0, 1 <= k <= 64, E >= 1, H >= 8, H % 8 == 0.
+ * ---------------------------------------------------------------------- */
+nvfp4_status nvfp4_moe_combine(const void* y_bf16, const int32_t* inv_perm,
+                               const float* topk_w, const int32_t* expert_offsets, int64_t T,
+                               int k, int E, int64_t H, void* out_bf16, void* stream);
+
+/* ------------------------------------------------------------------------
+ * The whole expert forward.
+ * README "What We Have", MoE runner: quantise -> L1 -> SiLU(gate)*up ->
+ * requantise -> L2 -> weighted scatter; here L1, SwiGLU and the requantise
+ * are one fused kernel.
+ *
+ * x BF16 [T][H]; topk_ids int32 [T][k]; topk_w float [T][k];
+ * w1_q [E][2I][H/2], w1_sf [E][2I][H/16], gs_w1 [E]  (interleaved, K-major);
+ * w2_q [E][H][I/2],  w2_sf [E][H][I/16],  gs_w2 [E]  (K-major);
+ * gs_h float[1]: global scale of the requantised L2 input (pre-computed);
+ * out BF16 [T][H].
+ * Steps on `stream`: nvfp4_quantize(x, per-call gs) -> nvfp4_moe_route ->
+ *   grouped GEMM L1 (SwiGLU + NVFP4 epilogue, A rows gathered by perm/k) ->
+ *   grouped GEMM L2 (BF16) -> combine.
+ * taps (nullable): every non-NULL member receives that intermediate (the
+ *   kernels write straight into it instead of the workspace).
+ * Shapes: T >= 0, H % 128 == 0, I % 128 == 0, 1 <= k <= 64, 1 <= E <= 4096.
+ * Workspace: moe_expert_forward_workspace_size() bytes.
+ * ---------------------------------------------------------------------- */
+typedef struct nvfp4_moe_taps {
+    uint8_t* a_q;            /* [T][H/2]   */
+    uint8_t* a_sf;           /* [T][H/16]  */
+    float* gs_a;             /* [1]        */
+    int32_t* expert_offsets; /* [E+1]      */
+    int32_t* perm;           /* [T*k]      */
+    int32_t* inv_perm;       /* [T*k]      */
+    int32_t* invalid_count;  /* [1]        */
+    float* h_f32;            /* [T*k][I]   */
+    uint8_t* h_q;            /* [T*k][I/2] */
+    uint8_t* h_sf;           /* [T*k][I/16]*/
+    void* y_bf16;            /* [T*k][H]   */
+} nvfp4_moe_taps;
+
+size_t moe_expert_forward_workspace_size(int64_t T, int64_t H, int64_t I, int E, int k);
+nvfp4_status moe_expert_forward(const void* x_bf16, int64_t T, int64_t H, int64_t I, int E,
+                                int k, const int32_t* topk_ids, const float* topk_w,
+                                const uint8_t* w1_q, const uint8_t* w1_sf, const float* gs_w1,
+                                const uint8_t* w2_q, const uint8_t* w2_sf, const float* gs_w2,
+                                const float* gs_h, void* out_bf16, const nvfp4_moe_taps* taps,
+                                void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* NVFP4MOE_H */

@@ -1,0 +1,291 @@
+"""Thin ctypes binding of libnvfp4moe.so (the C ABI in include/nvfp4moe.h).
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+contiguity, outputs and workspaces are allocated with torch (device memory
+and the current stream are all torch provides), and every step of the path
+runs in the HIP kernels behind the C ABI.  There is no fallback: if the
+library is missing or the device is not a gfx950 the call raises.
+"""
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libnvfp4moe.so")
+
+EPI_BF16 = 0
+EPI_SWIGLU_NVFP4 = 1
+
+_lib = None
+_lock = threading.Lock()
+
+c_void_p, c_int64, c_int, c_size_t = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+
+# name -> (restype, argtypes); mirrors include/nvfp4moe.h
+SIGNATURES = {
+    "nvfp4_status_string": (ctypes.c_char_p, [c_int]),
+    "nvfp4_last_error": (ctypes.c_char_p, []),
+    "nvfp4_version": (c_int, []),
+    "nvfp4_weight_layout": (c_int, [c_void_p, c_int64, c_int64, c_int64, c_int, c_void_p, c_void_p]),
+    "nvfp4_quantize_workspace_size": (c_size_t, [c_int64, c_int64, c_int64]),
+    "nvfp4_quantize": (c_int, [c_void_p, c_int64, c_int64, c_int64, c_void_p, c_void_p, c_void_p,
+                               c_void_p, c_void_p, c_size_t, c_void_p]),
+    "nvfp4_moe_route_workspace_size": (c_size_t, [c_int64, c_int, c_int]),
+    "nvfp4_moe_route": (c_int, [c_void_p, c_int64, c_int, c_int, c_void_p, c_void_p, c_void_p,
+                                c_void_p, c_void_p, c_size_t, c_void_p]),
+    "nvfp4_grouped_gemm": (c_int, [c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_void_p,
+                                   c_int, c_int64, c_int64, c_int64, c_void_p, c_void_p, c_void_p,
+                                   c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                   c_size_t, c_void_p]),
+    "nvfp4_moe_combine": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_int64, c_int, c_int,
+                                  c_int64, c_void_p, c_void_p]),
+    "moe_expert_forward_workspace_size": (c_size_t, [c_int64, c_int64, c_int64, c_int, c_int]),
+    "moe_expert_forward": (c_int, [c_void_p, c_int64, c_int64, c_int64, c_int, c_int, c_void_p,
+                                   c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                   c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
+                                   c_void_p]),
+}
+
+
+class Taps(ctypes.Structure):
+    """nvfp4_moe_taps: optional device pointers for the intermediates."""
+    _fields_ = [(n, c_void_p) for n in ("a_q", "a_sf", "gs_a", "expert_offsets", "perm", "inv_perm",
+                                        "invalid_count", "h_f32", "h_q", "h_sf", "y_bf16")]
+
+
+def lib():
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                                   "`python -m nvfp4_block_scaled_04_amd.build`")
+            handle = ctypes.CDLL(LIB_PATH)
+            for name, (res, args) in SIGNATURES.items():
+                fn = getattr(handle, name)
+                fn.restype, fn.argtypes = res, args
+            _lib = handle
+    return _lib
+
+
+class Nvfp4Error(RuntimeError):
+    def __init__(self, status, where):
+        L = lib()
+        self.status = status
+        super().__init__(f"{where}: {L.nvfp4_status_string(status).decode()} "
+                         f"({status}): {L.nvfp4_last_error().decode()}")
+
+
+def _check(status, where):
+    if status != 0:
+        raise Nvfp4Error(status, where)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device):
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _dev(t, dtype, name, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    return t
+
+
+def _workspace(nbytes, device):
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+# ------------------------------------------------------------------ entry points
+
+def weight_layout(w, interleave_gate_up):
+    """(G, R, C) bf16 -> (G, C, R) bf16: K-major, optionally gate/up interleaved."""
+    _dev(w, torch.bfloat16, "w")
+    G, R, C = w.shape
+    out = torch.empty((G, C, R), dtype=torch.bfloat16, device=w.device)
+    _check(lib().nvfp4_weight_layout(_ptr(w), G, R, C, int(bool(interleave_gate_up)), _ptr(out),
+                                     _stream(w.device)), "nvfp4_weight_layout")
+    return out
+
+
+def quantize(x, groups=1, gs_in=None, out=None):
+    """x (R, C) bf16 -> (q (R, C/2) u8, sf (R, C/16) u8, gs (groups,) f32)."""
+    _dev(x, torch.bfloat16, "x")
+    R, C = x.shape
+    if groups < 1 or R % groups:
+        raise ValueError("rows must divide evenly into groups")
+    dev = x.device
+    if out is None:
+        q = torch.empty((R, C // 2), dtype=torch.uint8, device=dev)
+        sf = torch.empty((R, C // 16), dtype=torch.uint8, device=dev)
+        gs = torch.empty((groups,), dtype=torch.float32, device=dev)
+    else:
+        q, sf, gs = out
+    if gs_in is not None:
+        _dev(gs_in, torch.float32, "gs_in", (groups,))
+    L = lib()
+    nbytes = L.nvfp4_quantize_workspace_size(groups, R // groups, C) if gs_in is None else 0
+    ws = _workspace(nbytes, dev)
+    _check(L.nvfp4_quantize(_ptr(x), groups, R // groups, C, _ptr(gs_in), _ptr(q), _ptr(sf),
+                            _ptr(gs), _ptr(ws), nbytes, _stream(dev)), "nvfp4_quantize")
+    return q, sf, gs
+
+
+def moe_route(topk_ids, E):
+    """topk_ids (T, k) int32 -> (offsets (E+1,), perm (T*k,), inv_perm (T*k,), invalid (1,))."""
+    _dev(topk_ids, torch.int32, "topk_ids")
+    T, k = topk_ids.shape
+    dev = topk_ids.device
+    off = torch.empty((E + 1,), dtype=torch.int32, device=dev)
+    perm = torch.empty((T * k,), dtype=torch.int32, device=dev)
+    inv = torch.empty((T * k,), dtype=torch.int32, device=dev)
+    bad = torch.empty((1,), dtype=torch.int32, device=dev)
+    L = lib()
+    nbytes = L.nvfp4_moe_route_workspace_size(T, k, E)
+    ws = _workspace(nbytes, dev)
+    _check(L.nvfp4_moe_route(_ptr(topk_ids), T, k, E, _ptr(off), _ptr(perm), _ptr(inv), _ptr(bad),
+                             _ptr(ws), nbytes, _stream(dev)), "nvfp4_moe_route")
+    return off, perm, inv, bad
+
+
+def grouped_gemm(epilogue, a_q, a_sf, gs_a, offsets, b_q, b_sf, gs_b, M, a_row_src=None,
+                 a_row_div=1, gs_out=None, debug=False, out=None):
+    """Expert-grouped NVFP4 GEMM.  BF16 epilogue returns c (M, N) bf16; the
+    SwiGLU epilogue returns (c_q (M, N/4), c_sf (M, N/32), h f32 (M, N/2) or None)."""
+    E, N, Kh = b_q.shape
+    K = Kh * 2
+    dev = b_q.device
+    _dev(a_q, torch.uint8, "a_q")
+    _dev(a_sf, torch.uint8, "a_sf")
+    _dev(b_sf, torch.uint8, "b_sf", (E, N, K // 16))
+    _dev(gs_a, torch.float32, "gs_a")
+    _dev(gs_b, torch.float32, "gs_b", (E,))
+    _dev(offsets, torch.int32, "offsets", (E + 1,))
+    if a_row_src is not None:
+        _dev(a_row_src, torch.int32, "a_row_src")
+    if epilogue == EPI_BF16:
+        c = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        c_q = c_sf = dbg = None
+    else:
+        I = N // 2
+        c = None
+        if out is not None:
+            c_q, c_sf, dbg = out
+        else:
+            c_q = torch.empty((M, I // 2), dtype=torch.uint8, device=dev)
+            c_sf = torch.empty((M, I // 16), dtype=torch.uint8, device=dev)
+            dbg = torch.empty((M, I), dtype=torch.float32, device=dev) if debug else None
+        _dev(gs_out, torch.float32, "gs_out")
+    _check(lib().nvfp4_grouped_gemm(epilogue, _ptr(a_q), _ptr(a_sf), _ptr(gs_a), _ptr(a_row_src),
+                                    a_row_div, _ptr(offsets), E, M, N, K, _ptr(b_q), _ptr(b_sf),
+                                    _ptr(gs_b), _ptr(gs_out), _ptr(c), _ptr(c_q), _ptr(c_sf),
+                                    _ptr(dbg), None, 0, _stream(dev)), "nvfp4_grouped_gemm")
+    return c if epilogue == EPI_BF16 else (c_q, c_sf, dbg)
+
+
+def moe_combine(y, inv_perm, topk_w, offsets, out=None):
+    """y (T*k, H) bf16 in expert order -> out (T, H) bf16."""
+    _dev(y, torch.bfloat16, "y")
+    _dev(topk_w, torch.float32, "topk_w")
+    T, k = topk_w.shape
+    H = y.shape[1]
+    E = offsets.shape[0] - 1
+    _dev(inv_perm, torch.int32, "inv_perm", (T * k,))
+    _dev(offsets, torch.int32, "offsets")
+    o = out if out is not None else torch.empty((T, H), dtype=torch.bfloat16, device=y.device)
+    _check(lib().nvfp4_moe_combine(_ptr(y), _ptr(inv_perm), _ptr(topk_w), _ptr(offsets), T, k, E, H,
+                                   _ptr(o), _stream(y.device)), "nvfp4_moe_combine")
+    return o
+
+
+class ExpertWeights:
+    """NVFP4 expert weights as the forward reads them (device tensors)."""
+
+    def __init__(self, w1_q, w1_sf, gs_w1, w2_q, w2_sf, gs_w2):
+        self.w1_q, self.w1_sf, self.gs_w1 = w1_q, w1_sf, gs_w1
+        self.w2_q, self.w2_sf, self.gs_w2 = w2_q, w2_sf, gs_w2
+
+    @property
+    def E(self):
+        return self.w1_q.shape[0]
+
+    @property
+    def I(self):
+        return self.w1_q.shape[1] // 2
+
+    @property
+    def H(self):
+        return self.w1_q.shape[2] * 2
+
+
+def forward_workspace(T, H, I, E, k, device):
+    return _workspace(lib().moe_expert_forward_workspace_size(T, H, I, E, k), device)
+
+
+def moe_expert_forward(x, topk_ids, topk_w, w: ExpertWeights, gs_h, out=None, taps=None,
+                       workspace=None):
+    """The whole expert forward.  ``taps``: dict name -> device tensor to
+    receive intermediates (keys of ``Taps``)."""
+    _dev(x, torch.bfloat16, "x")
+    T, H = x.shape
+    E, I = w.E, w.I
+    k = topk_ids.shape[1]
+    dev = x.device
+    _dev(topk_ids, torch.int32, "topk_ids", (T, k))
+    _dev(topk_w, torch.float32, "topk_w", (T, k))
+    _dev(w.w1_q, torch.uint8, "w1_q", (E, 2 * I, H // 2))
+    _dev(w.w1_sf, torch.uint8, "w1_sf", (E, 2 * I, H // 16))
+    _dev(w.gs_w1, torch.float32, "gs_w1", (E,))
+    _dev(w.w2_q, torch.uint8, "w2_q", (E, H, I // 2))
+    _dev(w.w2_sf, torch.uint8, "w2_sf", (E, H, I // 16))
+    _dev(w.gs_w2, torch.float32, "gs_w2", (E,))
+    _dev(gs_h, torch.float32, "gs_h", (1,))
+    o = out if out is not None else torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    L = lib()
+    nbytes = L.moe_expert_forward_workspace_size(T, H, I, E, k)
+    ws = workspace if workspace is not None else _workspace(nbytes, dev)
+    tp = None
+    if taps:
+        tp = Taps(**{name: t.data_ptr() for name, t in taps.items()})
+    _check(L.moe_expert_forward(_ptr(x), T, H, I, E, k, _ptr(topk_ids), _ptr(topk_w), _ptr(w.w1_q),
+                                _ptr(w.w1_sf), _ptr(w.gs_w1), _ptr(w.w2_q), _ptr(w.w2_sf),
+                                _ptr(w.gs_w2), _ptr(gs_h), _ptr(o),
+                                ctypes.byref(tp) if tp is not None else None, _ptr(ws), ws.numel(),
+                                _stream(dev)), "moe_expert_forward")
+    return o
+
+
+def prepare_expert_weights(w1_list, w2_list, device):
+    """Logical bf16 weights -> ExpertWeights on the device.
+
+    w1_list: iterable of chunks (Ec, H, 2I) bf16 ([gate | up]); w2_list of
+    (Ec, I, H).  Each chunk goes through nvfp4_weight_layout (interleave +
+    K-major) and nvfp4_quantize (one global scale per expert)."""
+    w1q, w1s, g1, w2q, w2s, g2 = [], [], [], [], [], []
+    for w1c, w2c in zip(w1_list, w2_list):
+        Ec = w1c.shape[0]
+        l1 = weight_layout(w1c, True)                     # (Ec, 2I, H)
+        q, s, g = quantize(l1.view(-1, l1.shape[2]), groups=Ec)
+        w1q.append(q.view(Ec, l1.shape[1], -1)); w1s.append(s.view(Ec, l1.shape[1], -1)); g1.append(g)
+        del l1
+        l2 = weight_layout(w2c, False)                    # (Ec, H, I)
+        q, s, g = quantize(l2.view(-1, l2.shape[2]), groups=Ec)
+        w2q.append(q.view(Ec, l2.shape[1], -1)); w2s.append(s.view(Ec, l2.shape[1], -1)); g2.append(g)
+        del l2
+    cat = lambda xs: xs[0] if len(xs) == 1 else torch.cat(xs)
+    return ExpertWeights(cat(w1q), cat(w1s), cat(g1), cat(w2q), cat(w2s), cat(g2))

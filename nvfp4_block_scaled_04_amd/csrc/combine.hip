@@ -1,0 +1,60 @@
+// Routing-weighted combine of expert outputs back to tokens (gfx950).
+//
+// README "NVFP4 MegaMoE Kernel", "What We Have", MoE runner step 6: scatter
+// with routing weights.  Written as a gather so no atomics are needed and the
+// result is deterministic:
+//   out[t][n] = bf16( sum_{j<k} w[t][j] * y[inv_perm[t*k+j]][n] ),
+// fp32 accumulation in slot order; rows d >= offsets[E] (invalid expert ids)
+// contribute nothing.  One block per token; each thread moves 16 bytes
+// (8 BF16) per row, so every wave reads 1 KiB contiguous spans.
+#include "internal.hpp"
+#include "device.hpp"
+
+namespace nvfp4 {
+
+namespace {
+
+constexpr int kThreads = 128;
+
+__global__ __launch_bounds__(kThreads) void combine_kernel(
+    const uint4* __restrict__ y, const int32_t* __restrict__ inv_perm,
+    const float* __restrict__ topk_w, const int32_t* __restrict__ offsets, int k, int E,
+    int64_t H, uint4* __restrict__ out) {
+  const int64_t t = blockIdx.x;
+  const int64_t hv = H / 8;                 // 16-byte vectors per row
+  const int32_t n_valid = offsets[E];
+  for (int64_t v = threadIdx.x; v < hv; v += kThreads) {
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int j = 0; j < k; ++j) {
+      const int32_t d = inv_perm[t * k + j];
+      if (d >= n_valid) continue;
+      const float w = topk_w[t * k + j];
+      const uint4 r = y[(int64_t)d * hv + v];
+      const uint32_t p[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] = fmaf(w, bf16_to_f32(p[i] & 0xFFFFu), acc[2 * i]);
+        acc[2 * i + 1] = fmaf(w, bf16_to_f32(p[i] >> 16), acc[2 * i + 1]);
+      }
+    }
+    uint4 o;
+    o.x = f32_to_bf16_rne(acc[0]) | (f32_to_bf16_rne(acc[1]) << 16);
+    o.y = f32_to_bf16_rne(acc[2]) | (f32_to_bf16_rne(acc[3]) << 16);
+    o.z = f32_to_bf16_rne(acc[4]) | (f32_to_bf16_rne(acc[5]) << 16);
+    o.w = f32_to_bf16_rne(acc[6]) | (f32_to_bf16_rne(acc[7]) << 16);
+    out[t * hv + v] = o;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const void* y, const int32_t* inv_perm, const float* topk_w,
+                          const int32_t* offsets, int64_t T, int k, int E, int64_t H, void* out,
+                          hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  combine_kernel<<<(unsigned)T, kThreads, 0, stream>>>(
+      static_cast<const uint4*>(y), inv_perm, topk_w, offsets, k, E, H, static_cast<uint4*>(out));
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4

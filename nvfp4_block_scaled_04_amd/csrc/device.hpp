@@ -1,0 +1,85 @@
+// Device-side helpers shared by the NVFP4 kernels (gfx950 only).
+//
+// NVFP4 as used here (README "NVFP4 MegaMoE Kernel", "What We Have", grouped
+// GEMM): E2M1 element codes (bit 3 = sign, magnitudes 0 .5 1 1.5 2 3 4 6),
+// one OCP E4M3 scale (bias 7, max 448, subnormal step 2^-9) per 16 elements,
+// fp32 global scale.  The encoders below are written from the bit layouts of
+// the formats; every operation rounds to nearest even.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+constexpr float kUnderflow = 0.01171875f;   // 6 * 2^-9: E2M1 max * E4M3 min subnormal
+constexpr float kGsNumerator = 2688.0f;     // 448 * 6: E4M3 max * E2M1 max
+constexpr float kE4m3Max = 448.0f;
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even (inputs finite).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// E4M3 byte of t, 2^-9 <= t <= 448, nearest with ties to even.
+// Normal range (t >= 2^-6): round the fp32 mantissa to 3 bits on the bit
+// pattern (the carry moves into the exponent) and rebias 127 -> 7.
+// Subnormal range: t = k * 2^-9 with k = rint(t * 512) in 1..8 (k = 8 is the
+// smallest normal, byte 0x08, so the two ranges meet without a seam).
+__device__ __forceinline__ uint32_t e4m3_encode(float t) {
+  if (t < 0.015625f) {
+    return (uint32_t)__builtin_rintf(t * 512.0f);
+  }
+  uint32_t u = __float_as_uint(t);
+  u += 0x7FFFFu + ((u >> 20) & 1u);
+  return (u >> 20) - (120u << 3);
+}
+
+// value of an E4M3 byte with sign bit clear (never the NaN byte here)
+__device__ __forceinline__ float e4m3_decode(uint32_t b) {
+  uint32_t e = (b >> 3) & 15u, m = b & 7u;
+  if (e == 0) return (float)m * 0.001953125f;   // m * 2^-9, exact
+  return __uint_as_float(((e + 120u) << 23) | (m << 20));
+}
+
+// E2M1 magnitude code of v, 0 <= v <= 6, nearest with ties to the even code.
+// Each comparison counts one grid step passed; at a midpoint the strict (>)
+// or non-strict (>=) form keeps the even neighbour.
+__device__ __forceinline__ uint32_t e2m1_encode(float v) {
+  return (uint32_t)(v > 0.25f) + (uint32_t)(v >= 0.75f) + (uint32_t)(v > 1.25f) +
+         (uint32_t)(v >= 1.75f) + (uint32_t)(v > 2.5f) + (uint32_t)(v >= 3.5f) +
+         (uint32_t)(v > 5.0f);
+}
+
+// One 16-element block -> (8 bytes of packed codes, scale byte).
+// x[i] are the fp32 values, sgn the sign bits (bit i = sign of element i).
+// gs is the global scale.  Operation order: a_s = amax*gs; zero/underflow
+// (amax == 0 or a_s < 6*2^-9) -> all zero; t = a_s/6; sf = E4M3(min(t,448));
+// r = gs/dec(sf); code_i = sign_i | E2M1(min(|x_i*r|, 6)).
+__device__ __forceinline__ void quantize_block16(const float (&x)[16], uint32_t sgn, float gs,
+                                                 uint32_t& lo, uint32_t& hi, uint32_t& sf) {
+#pragma clang fp contract(off)
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(x[i]));
+  const float a_s = amax * gs;
+  lo = 0u; hi = 0u; sf = 0u;
+  if (amax == 0.0f || a_s < kUnderflow) return;
+  const float t = fminf(a_s / 6.0f, kE4m3Max);
+  sf = e4m3_encode(t);
+  const float r = gs / e4m3_decode(sf);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float v = fminf(fabsf(x[i] * r), 6.0f);
+    const uint32_t c = e2m1_encode(v) | (((sgn >> i) & 1u) << 3);
+    if (i < 8) lo |= c << (4 * i);
+    else       hi |= c << (4 * (i - 8));
+  }
+}
+
+}  // namespace nvfp4

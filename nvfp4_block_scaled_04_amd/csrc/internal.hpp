@@ -1,0 +1,62 @@
+// Internal launch interface between the C ABI (api.hip) and the kernels.
+// Every launch_* enqueues on `stream`, allocates nothing and assumes its
+// arguments were validated by the caller.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "nvfp4moe.h"
+
+namespace nvfp4 {
+
+// small utility kernels (layout.hip); fills instead of hipMemsetAsync so the
+// sequence stays correct under hipGraph replay
+void fill_f32(float* p, float v, int64_t n, hipStream_t stream);
+void fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t stream);
+
+// quantize.hip
+int quantize_parts(int64_t groups, int64_t rows_per_group, int64_t cols);
+hipError_t launch_quantize(const void* x, int64_t groups, int64_t rows_per_group, int64_t cols,
+                           const float* gs_in, uint8_t* q, uint8_t* sf, float* gs_out, float* ws,
+                           hipStream_t stream);
+
+// route.hip
+int64_t route_chunks(int64_t T, int k);
+size_t route_ws_bytes(int64_t T, int k, int E);
+hipError_t launch_route(const int32_t* topk_ids, int64_t T, int k, int E, int32_t* offsets,
+                        int32_t* perm, int32_t* inv_perm, int32_t* invalid_count, void* ws,
+                        hipStream_t stream);
+
+// layout.hip
+hipError_t launch_weight_layout(const void* src, int64_t groups, int64_t rows, int64_t cols,
+                                int interleave, void* dst, hipStream_t stream);
+
+// gemm.hip
+struct GemmArgs {
+  int epilogue;
+  const uint8_t* a_q;
+  const uint8_t* a_sf;
+  const float* gs_a;
+  const int32_t* a_row_src;
+  int a_row_div;
+  const int32_t* offsets;
+  int E;
+  int64_t M, N, K;
+  const uint8_t* b_q;
+  const uint8_t* b_sf;
+  const float* gs_b;
+  const float* gs_out;
+  void* c_bf16;
+  uint8_t* c_q;
+  uint8_t* c_sf;
+  float* c_debug;
+};
+hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t stream);
+
+// combine.hip
+hipError_t launch_combine(const void* y, const int32_t* inv_perm, const float* topk_w,
+                          const int32_t* offsets, int64_t T, int k, int E, int64_t H, void* out,
+                          hipStream_t stream);
+
+}  // namespace nvfp4

@@ -1,0 +1,139 @@
+// BF16 -> NVFP4 quantisation kernels (gfx950).
+//
+// README "NVFP4 MegaMoE Kernel", "What We Have" (bridge layer): BF16 -> NVFP4
+// with a global scale, and a variant with a pre-computed global scale;
+// "Correctness Bugs Fixed" bugs 3 and 4: zero blocks get scale 0, underflow
+// blocks are zeroed; CURRENT_BUG.md "What Works": the activation global scale
+// is recomputed per call.
+//
+// Three launches for the per-call global scale, one with a given scale:
+//   amax_partial   grid (P, groups): chunk maxima of |x| -> ws[g][P]
+//   gs_finalize    grid (groups):    gs[g] = 2688 / max(ws[g][:]) (1 if 0)
+//   quantize       one thread per 16-element block: 32 B in, 9 B out.
+// Max is exact, so the partial split cannot change the result.
+#include "internal.hpp"
+#include "device.hpp"
+
+namespace nvfp4 {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+__global__ __launch_bounds__(kThreads) void amax_partial_kernel(
+    const uint4* __restrict__ x, int64_t vec_per_group, int parts, float* __restrict__ partial) {
+  const int g = blockIdx.y;
+  const int p = blockIdx.x;
+  const uint4* xg = x + (int64_t)g * vec_per_group;
+  const int64_t per = (vec_per_group + parts - 1) / parts;
+  const int64_t lo = (int64_t)p * per;
+  const int64_t hi = lo + per < vec_per_group ? lo + per : vec_per_group;
+  float m = 0.0f;
+  for (int64_t i = lo + threadIdx.x; i < hi; i += kThreads) {
+    const uint4 v = xg[i];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      m = fmaxf(m, fabsf(bf16_to_f32(w[j] & 0xFFFFu)));
+      m = fmaxf(m, fabsf(bf16_to_f32(w[j] >> 16)));
+    }
+  }
+  // wave reduction, then across the 4 waves
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  __shared__ float red[kThreads / 64];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float r = red[0];
+    for (int i = 1; i < kThreads / 64; ++i) r = fmaxf(r, red[i]);
+    partial[(int64_t)g * parts + p] = r;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void gs_finalize_kernel(const float* __restrict__ partial,
+                                                               int parts, float* __restrict__ gs_out) {
+  const int g = blockIdx.x;
+  float m = 0.0f;
+  for (int i = threadIdx.x; i < parts; i += kThreads) m = fmaxf(m, partial[(int64_t)g * parts + i]);
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  __shared__ float red[kThreads / 64];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float r = red[0];
+    for (int i = 1; i < kThreads / 64; ++i) r = fmaxf(r, red[i]);
+    gs_out[g] = (r == 0.0f) ? 1.0f : kGsNumerator / r;
+  }
+}
+
+// One thread per 16-element block.  blocks_per_group = rows_per_group*cols/16.
+__global__ __launch_bounds__(kThreads) void quantize_kernel(
+    const uint4* __restrict__ x, int64_t nblocks, int64_t blocks_per_group,
+    const float* __restrict__ gs, const float* __restrict__ gs_copy_src, int groups,
+    float* __restrict__ gs_copy_dst, uint2* __restrict__ q, uint8_t* __restrict__ sf) {
+  const int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (gs_copy_dst != nullptr && b < groups) gs_copy_dst[b] = gs_copy_src[b];
+  if (b >= nblocks) return;
+  const float g = gs[b / blocks_per_group];
+  const uint4 v0 = x[2 * b], v1 = x[2 * b + 1];
+  const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+  float xs[16];
+  uint32_t sgn = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    xs[2 * j] = bf16_to_f32(w[j] & 0xFFFFu);
+    xs[2 * j + 1] = bf16_to_f32(w[j] >> 16);
+    sgn |= ((w[j] >> 15) & 1u) << (2 * j);
+    sgn |= (w[j] >> 31) << (2 * j + 1);
+  }
+  uint32_t lo, hi, s;
+  quantize_block16(xs, sgn, g, lo, hi, s);
+  q[b] = make_uint2(lo, hi);
+  sf[b] = (uint8_t)s;
+}
+
+}  // namespace
+
+int quantize_parts(int64_t groups, int64_t rows_per_group, int64_t cols) {
+  // chunks per group for the amax pass: enough blocks to fill the chip,
+  // at most one chunk per 2048 vectors, capped at 1024
+  const int64_t vec = rows_per_group * cols / 8;
+  if (groups <= 0 || vec <= 0) return 0;
+  int64_t p = (2048 + groups - 1) / groups;
+  int64_t cap = (vec + 2047) / 2048;
+  if (p > cap) p = cap;
+  if (p > 1024) p = 1024;
+  if (p < 1) p = 1;
+  return (int)p;
+}
+
+hipError_t launch_quantize(const void* x, int64_t groups, int64_t rows_per_group, int64_t cols,
+                           const float* gs_in, uint8_t* q, uint8_t* sf, float* gs_out, float* ws,
+                           hipStream_t stream) {
+  const int64_t rows = groups * rows_per_group;
+  const int64_t nblocks = rows * (cols / 16);
+  if (groups == 0) return hipSuccess;
+  const float* gs = gs_in;
+  if (gs_in == nullptr) {
+    const int parts = quantize_parts(groups, rows_per_group, cols);
+    if (parts > 0) {
+      amax_partial_kernel<<<dim3(parts, (unsigned)groups), kThreads, 0, stream>>>(
+          static_cast<const uint4*>(x), rows_per_group * cols / 8, parts, ws);
+      gs_finalize_kernel<<<(unsigned)groups, kThreads, 0, stream>>>(ws, parts, gs_out);
+    } else {
+      // empty groups: global scale 1
+      fill_f32(gs_out, 1.0f, groups, stream);
+    }
+    gs = gs_out;
+  }
+  const int64_t need = nblocks > groups ? nblocks : groups;
+  if (need == 0) return hipGetLastError();
+  const unsigned grid = (unsigned)((need + kThreads - 1) / kThreads);
+  const bool copy = gs_in != nullptr && gs_out != gs_in;
+  quantize_kernel<<<grid, kThreads, 0, stream>>>(
+      static_cast<const uint4*>(x), nblocks, rows_per_group * (cols / 16) > 0 ? rows_per_group * (cols / 16) : 1,
+      gs, gs_in, (int)groups, copy ? gs_out : nullptr, reinterpret_cast<uint2*>(q), sf);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4

@@ -1,0 +1,181 @@
+// Expert offsets and the stable expert-order permutation (gfx950).
+//
+// README "NVFP4 MegaMoE Kernel", "Correctness Bugs Fixed" bug 5: experts are
+// counted by a histogram (bincount), not an O(n x E) mask.  "Key Lessons" 4:
+// quantise the compact rows, then place them.
+//
+// The flat pairs f = t*k + j are cut into C chunks of `chunk` entries.
+//   route_hist     grid C:  LDS histogram of each chunk -> ws[c][E+1]
+//                           (bucket E collects ids outside [0, E))
+//   route_scan     1 block: per bucket, exclusive prefix over chunks; then an
+//                           exclusive scan over buckets -> expert offsets;
+//                           ws[c][b] becomes chunk c's first output row of b
+//   route_scatter  grid C, one wave: walks its chunk in order, 64 entries at
+//                           a time; a lane's rank among equal buckets of the
+//                           batch comes from a ballot, so every bucket keeps
+//                           increasing f (a stable counting sort).
+// All integer; integer atomics only in LDS, where order cannot matter.
+#include "internal.hpp"
+
+namespace nvfp4 {
+
+namespace {
+
+constexpr int kHistThreads = 256;
+constexpr int kScanThreads = 1024;
+constexpr int64_t kMinChunk = 1024;
+constexpr int64_t kMaxChunks = 1024;
+
+int64_t chunk_size(int64_t M) {
+  int64_t ch = kMinChunk;
+  if ((M + ch - 1) / ch > kMaxChunks) ch = ((M + kMaxChunks - 1) / kMaxChunks + 63) / 64 * 64;
+  return ch;
+}
+
+__device__ __forceinline__ int bucket_of(int32_t id, int E) {
+  return (id >= 0 && id < E) ? id : E;
+}
+
+__global__ __launch_bounds__(kHistThreads) void route_hist_kernel(
+    const int32_t* __restrict__ ids, int64_t M, int64_t chunk, int E, int32_t* __restrict__ hist) {
+  extern __shared__ int32_t cnt[];
+  const int nb = E + 1;
+  for (int b = threadIdx.x; b < nb; b += kHistThreads) cnt[b] = 0;
+  __syncthreads();
+  const int64_t lo = (int64_t)blockIdx.x * chunk;
+  const int64_t hi = lo + chunk < M ? lo + chunk : M;
+  for (int64_t f = lo + threadIdx.x; f < hi; f += kHistThreads) {
+    atomicAdd(&cnt[bucket_of(ids[f], E)], 1);
+  }
+  __syncthreads();
+  int32_t* h = hist + (int64_t)blockIdx.x * nb;
+  for (int b = threadIdx.x; b < nb; b += kHistThreads) h[b] = cnt[b];
+}
+
+__global__ __launch_bounds__(kScanThreads) void route_scan_kernel(
+    int32_t* __restrict__ hist, int64_t C, int E, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ invalid_count) {
+  extern __shared__ int32_t sm[];        // total[E+1] then part[kScanThreads]
+  const int nb = E + 1;
+  int32_t* total = sm;
+  int32_t* part = sm + nb;
+  // per-bucket exclusive prefix over chunks
+  for (int b = threadIdx.x; b < nb; b += kScanThreads) {
+    int32_t run = 0;
+    for (int64_t c = 0; c < C; ++c) {
+      const int32_t v = hist[c * nb + b];
+      hist[c * nb + b] = run;
+      run += v;
+    }
+    total[b] = run;
+  }
+  __syncthreads();
+  // exclusive scan of total[0..nb): each thread owns a contiguous segment
+  const int seg = (nb + kScanThreads - 1) / kScanThreads;
+  const int s0 = threadIdx.x * seg;
+  int32_t local = 0;
+  for (int i = 0; i < seg; ++i)
+    if (s0 + i < nb) local += total[s0 + i];
+  part[threadIdx.x] = local;
+  __syncthreads();
+  for (int off = 1; off < kScanThreads; off <<= 1) {
+    const int32_t v = threadIdx.x >= (unsigned)off ? part[threadIdx.x - off] : 0;
+    __syncthreads();
+    part[threadIdx.x] += v;
+    __syncthreads();
+  }
+  int32_t run = part[threadIdx.x] - local;  // exclusive prefix of this segment
+  for (int i = 0; i < seg; ++i) {
+    const int b = s0 + i;
+    if (b < nb) {
+      const int32_t t = total[b];
+      total[b] = run;                        // total[] now holds bucket bases
+      run += t;
+    }
+  }
+  __syncthreads();
+  for (int b = threadIdx.x; b < nb; b += kScanThreads) {
+    offsets[b] = total[b];
+    for (int64_t c = 0; c < C; ++c) hist[c * nb + b] += total[b];
+  }
+  if (threadIdx.x == 0 && invalid_count != nullptr) {
+    // bucket E's size: M - offsets[E], recovered from the last segment
+    invalid_count[0] = part[kScanThreads - 1] - total[E];
+  }
+}
+
+__global__ __launch_bounds__(64) void route_scatter_kernel(
+    const int32_t* __restrict__ ids, int64_t M, int64_t chunk, int E,
+    const int32_t* __restrict__ hist, int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm) {
+  extern __shared__ int32_t cur[];
+  const int nb = E + 1;
+  const int lane = threadIdx.x;
+  const int32_t* h = hist + (int64_t)blockIdx.x * nb;
+  for (int b = lane; b < nb; b += 64) cur[b] = h[b];
+  __syncthreads();
+  const int64_t lo = (int64_t)blockIdx.x * chunk;
+  const int64_t hi = lo + chunk < M ? lo + chunk : M;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int64_t base = lo; base < hi; base += 64) {
+    const int64_t f = base + lane;
+    const bool active = f < hi;
+    const int e = active ? bucket_of(ids[f], E) : -1;
+    uint64_t pending = __ballot(active);
+    int rank = 0, cnt = 0;
+    while (pending) {
+      const int leader = __ffsll((unsigned long long)pending) - 1;
+      const int e0 = __builtin_amdgcn_readlane(e, leader);
+      const uint64_t m = __ballot(active && e == e0);
+      if (active && e == e0) {
+        rank = __popcll(m & below);
+        cnt = __popcll(m);
+      }
+      pending &= ~m;
+    }
+    int32_t pos = 0;
+    if (active) {
+      pos = cur[e] + rank;
+      perm[pos] = (int32_t)f;
+      inv_perm[f] = pos;
+    }
+    __syncthreads();
+    if (active && rank == cnt - 1) cur[e] += cnt;
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+int64_t route_chunks(int64_t T, int k) {
+  const int64_t M = T * k;
+  const int64_t ch = chunk_size(M);
+  return (M + ch - 1) / ch;
+}
+
+size_t route_ws_bytes(int64_t T, int k, int E) {
+  const int64_t C = route_chunks(T, k);
+  const int64_t n = (C > 0 ? C : 1) * (int64_t)(E + 1);
+  return (size_t)n * sizeof(int32_t);
+}
+
+hipError_t launch_route(const int32_t* topk_ids, int64_t T, int k, int E, int32_t* offsets,
+                        int32_t* perm, int32_t* inv_perm, int32_t* invalid_count, void* ws,
+                        hipStream_t stream) {
+  const int64_t M = T * k;
+  const int64_t ch = chunk_size(M);
+  const int64_t C = (M + ch - 1) / ch;
+  int32_t* hist = static_cast<int32_t*>(ws);
+  const size_t lds_hist = (size_t)(E + 1) * sizeof(int32_t);
+  if (C > 0) {
+    route_hist_kernel<<<(unsigned)C, kHistThreads, lds_hist, stream>>>(topk_ids, M, ch, E, hist);
+  }
+  route_scan_kernel<<<1, kScanThreads, lds_hist + kScanThreads * sizeof(int32_t), stream>>>(
+      hist, C, E, offsets, invalid_count);
+  if (C > 0) {
+    route_scatter_kernel<<<(unsigned)C, 64, lds_hist, stream>>>(topk_ids, M, ch, E, hist, perm,
+                                                                inv_perm);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4

@@ -1,0 +1,120 @@
+"""The C ABI library on the CPU: it loads, exports every declared symbol, and
+rejects bad arguments on the host before touching HIP (no compute calls)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4moe.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    from nvfp4_block_scaled_04_amd import binding
+    if not os.path.exists(binding.LIB_PATH):
+        from nvfp4_block_scaled_04_amd import build
+        build.build(verbose=False)
+    return binding.lib()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b([a-z_0-9]+)\s*\(", text)
+    skip = {"sizeof", "defined"}
+    return sorted({n for n in names if n not in skip and (n.startswith("nvfp4_") or n.startswith("moe_"))})
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = _declared()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_binding_signatures_cover_header():
+    from nvfp4_block_scaled_04_amd import binding
+    assert set(_declared()) == set(binding.SIGNATURES)
+
+
+def test_status_strings_and_version(L):
+    assert L.nvfp4_status_string(0) == b"ok"
+    for s in (-1, -2, -3, -4, -5):
+        assert L.nvfp4_status_string(s) != b"unknown status"
+    assert L.nvfp4_version() >= 100
+
+
+def test_workspace_sizes(L):
+    assert L.nvfp4_quantize_workspace_size(1, 8192, 7168) > 0
+    assert L.nvfp4_quantize_workspace_size(0, 8, 16) == 0
+    assert L.nvfp4_moe_route_workspace_size(8192, 8, 256) >= 257 * 4
+    small = L.moe_expert_forward_workspace_size(64, 256, 128, 4, 2)
+    big = L.moe_expert_forward_workspace_size(8192, 7168, 2048, 256, 8)
+    assert 0 < small < big
+    # y (M x H bf16) dominates the forward workspace
+    assert big >= 65536 * 7168 * 2
+
+
+FAKE = 0x1000  # never dereferenced: every call below fails validation first
+
+
+@pytest.mark.parametrize("args,status", [
+    ((FAKE, 1, 4, 15, None, FAKE, FAKE, FAKE, FAKE, 1 << 20, None), -2),   # cols % 16
+    ((FAKE, -1, 4, 16, None, FAKE, FAKE, FAKE, FAKE, 1 << 20, None), -2),
+    ((None, 1, 4, 16, None, FAKE, FAKE, FAKE, FAKE, 1 << 20, None), -1),   # null x
+    ((FAKE, 1, 4, 16, None, FAKE, FAKE, FAKE, None, 0, None), -3),         # no workspace
+    ((FAKE + 8, 1, 4, 16, None, FAKE, FAKE, FAKE, FAKE, 1 << 20, None), -1),  # misaligned x
+])
+def test_quantize_rejects(L, args, status):
+    assert L.nvfp4_quantize(*args) == status
+    assert L.nvfp4_last_error() != b""
+
+
+def test_route_rejects(L):
+    assert L.nvfp4_moe_route(FAKE, 4, 0, 8, FAKE, FAKE, FAKE, None, FAKE, 1 << 20, None) == -2
+    assert L.nvfp4_moe_route(FAKE, 4, 2, 0, FAKE, FAKE, FAKE, None, FAKE, 1 << 20, None) == -2
+    assert L.nvfp4_moe_route(FAKE, 4, 2, 8, None, FAKE, FAKE, None, FAKE, 1 << 20, None) == -1
+    assert L.nvfp4_moe_route(FAKE, 4, 2, 8, FAKE, FAKE, FAKE, None, FAKE, 4, None) == -3
+
+
+def _gemm(L, **kw):
+    a = dict(epi=0, a_q=FAKE, a_sf=FAKE, gs_a=FAKE, src=None, div=1, off=FAKE, E=4, M=64, N=256,
+             K=256, b_q=FAKE, b_sf=FAKE, gs_b=FAKE, gs_out=FAKE, c=FAKE, cq=FAKE, csf=FAKE,
+             dbg=None)
+    a.update(kw)
+    return L.nvfp4_grouped_gemm(a["epi"], a["a_q"], a["a_sf"], a["gs_a"], a["src"], a["div"],
+                                a["off"], a["E"], a["M"], a["N"], a["K"], a["b_q"], a["b_sf"],
+                                a["gs_b"], a["gs_out"], a["c"], a["cq"], a["csf"], a["dbg"], None,
+                                0, None)
+
+
+def test_gemm_rejects(L):
+    assert _gemm(L, epi=7) == -1
+    assert _gemm(L, K=200) == -2
+    assert _gemm(L, K=64) == -2
+    assert _gemm(L, N=48) == -2
+    assert _gemm(L, E=0) == -2
+    assert _gemm(L, c=None) == -1
+    assert _gemm(L, epi=1, cq=None) == -1
+    assert _gemm(L, src=FAKE, div=0) == -2
+    assert _gemm(L, off=None) == -1
+
+
+def test_combine_and_forward_reject(L):
+    assert L.nvfp4_moe_combine(FAKE, FAKE, FAKE, FAKE, 4, 2, 4, 12, FAKE, None) == -2
+    assert L.nvfp4_moe_combine(None, FAKE, FAKE, FAKE, 4, 2, 4, 16, FAKE, None) == -1
+    f = lambda **kw: L.moe_expert_forward(
+        FAKE, kw.get("T", 4), kw.get("H", 256), kw.get("I", 128), kw.get("E", 4), kw.get("k", 2),
+        FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, kw.get("gs_h", FAKE), FAKE, None,
+        kw.get("ws", FAKE), kw.get("wsb", 1 << 30), None)
+    assert f(H=200) == -2
+    assert f(I=64) == -2
+    assert f(k=0) == -2
+    assert f(gs_h=None) == -1
+    assert f(wsb=16) == -3
+    assert f(ws=FAKE + 16) == -3
+    assert L.nvfp4_weight_layout(FAKE, 2, 4, 24, 1, FAKE, None) == -2
+    assert L.nvfp4_weight_layout(FAKE, 2, 4, 32, 1, None, None) == -1

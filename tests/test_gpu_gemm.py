@@ -1,0 +1,122 @@
+"""GPU parity of the expert-grouped NVFP4 GEMM (both epilogues) against the
+oracle, from identical quantised operands."""
+
+import numpy as np
+import pytest
+import torch
+
+import nvfp4_block_scaled_04_amd as nv
+from nvfp4_block_scaled_04_amd import inputs as I
+from oracle import quantize as Q
+from oracle import moe as O
+from oracle import route as R
+from parity import host, bf16_values, assert_close, assert_requant_matches
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _randn(shape, seed, std=1.0):
+    g = torch.Generator(device=DEV).manual_seed(seed)
+    return (torch.randn(shape, generator=g, device=DEV) * std).to(torch.bfloat16)
+
+
+def _grouped_case(counts, N, K, seed, epi, gather_k=None, T=0):
+    """Random grouped problem with the given rows per expert, or (gather_k)
+    T tokens routed to gather_k distinct experts each, rows gathered by perm."""
+    E = len(counts)
+    M = T * gather_k if gather_k else int(sum(counts))
+    print(f"[case] gemm epi={epi} counts={counts[:8]}.. E={E} M={M} N={N} K={K} gather={gather_k}",
+          flush=True)
+    if gather_k:
+        rng = np.random.default_rng(seed)
+        ids = np.stack([rng.permutation(E)[:gather_k] for _ in range(T)]).astype(np.int32)
+        off_h, perm_h, _, _ = R.route(ids, E)
+        x = _randn((T, K), seed)
+        a_q, a_sf, gs_a = nv.quantize(x)
+        off = torch.from_numpy(off_h).to(DEV)
+        src = torch.from_numpy(perm_h).to(DEV)
+        a_rows = perm_h // gather_k
+    else:
+        x = _randn((M, K), seed)
+        a_q, a_sf, gs_a = nv.quantize(x)
+        off_h = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+        off = torch.from_numpy(off_h).to(DEV)
+        src = None
+        a_rows = np.arange(M)
+    w = _randn((E * N, K), seed + 1, 0.02)
+    b_q, b_sf, gs_b = nv.quantize(w, groups=E)
+    b_q, b_sf = b_q.view(E, N, K // 2), b_sf.view(E, N, K // 16)
+    gs_out = torch.tensor([64.0], device=DEV)
+    res = nv.grouped_gemm(epi, a_q, a_sf, gs_a, off, b_q, b_sf, gs_b, M, a_row_src=src,
+                          a_row_div=gather_k or 1, gs_out=gs_out, debug=True)
+    torch.cuda.synchronize()
+    # oracle from the same bf16 inputs
+    aq, asf, ga = Q.quantize_nvfp4(host(x))
+    bq, bsf, gb = Q.quantize_nvfp4(host(w), groups=E)
+    bq, bsf = bq.reshape(E, N, K // 2), bsf.reshape(E, N, K // 16)
+    return res, (aq, asf, ga[0], bq, bsf, gb, off_h, a_rows)
+
+
+@pytest.mark.parametrize("counts,N,K", [
+    ([5, 0, 130, 1, 64, 200], 96, 256),
+    ([128, 128], 128, 128),
+    ([0, 0, 3], 32, 384),
+    ([300], 256, 1024),
+])
+def test_grouped_bf16_epilogue(counts, N, K):
+    res, (aq, asf, ga, bq, bsf, gb, off, rows) = _grouped_case(counts, N, K, 11, nv.EPI_BF16)
+    got = bf16_values(host(res))
+    for e in range(len(counts)):
+        lo, hi = off[e], off[e + 1]
+        if hi == lo:
+            continue
+        ref = bf16_values(O.round_to_bf16(
+            O.nvfp4_matmul(aq[rows[lo:hi]], asf[rows[lo:hi]], ga, bq[e], bsf[e], gb[e])))
+        assert_close(got[lo:hi], ref, f"expert {e}")
+
+
+@pytest.mark.parametrize("counts,N,K,gk,T", [
+    ([5, 0, 130, 1, 64, 200], 64, 256, None, 0),
+    ([0, 37, 0, 91], 256, 512, None, 0),
+    ([0] * 8, 128, 256, 3, 45),
+])
+def test_grouped_swiglu_epilogue(counts, N, K, gk, T):
+    res, (aq, asf, ga, bq, bsf, gb, off, rows) = _grouped_case(
+        counts, N, K, 21, nv.EPI_SWIGLU_NVFP4, gather_k=gk, T=T)
+    c_q, c_sf, h_dbg = res
+    gq, gsf, gh = host(c_q), host(c_sf), host(h_dbg)
+    E = bq.shape[0]
+    for e in range(E):
+        lo, hi = off[e], off[e + 1]
+        if hi == lo:
+            continue
+        ref_h = O.l1_swiglu(aq[rows[lo:hi]], asf[rows[lo:hi]], ga, bq[e], bsf[e], gb[e])
+        assert_close(gh[lo:hi], ref_h, f"h expert {e}")
+        assert_requant_matches(gq[lo:hi], gsf[lo:hi], ref_h, 64.0, f"requant expert {e}")
+
+
+def test_dense_linear_config2_sampled_rows():
+    w = I.WORKLOADS["dense"]
+    M, K, N = w.dense_mkn
+    print(f"[case] dense M={M} K={K} N={N}", flush=True)
+    a, b = I.make_dense(w, DEV)
+    a_q, a_sf, gs_a = nv.quantize(a)
+    bk = nv.weight_layout(b.view(1, K, N), False)[0]              # (N, K)
+    b_q, b_sf, gs_b = nv.quantize(bk)
+    off = torch.tensor([0, M], dtype=torch.int32, device=DEV)
+    c = nv.grouped_gemm(nv.EPI_BF16, a_q, a_sf, gs_a, off, b_q.view(1, N, K // 2),
+                        b_sf.view(1, N, K // 16), gs_b, M)
+    torch.cuda.synchronize()
+    ab, bb = host(a), host(b)
+    gsa = Q.global_scale(ab)
+    rows = np.unique(np.concatenate([np.arange(0, M, 61), [M - 1]]))
+    aq, asf = Q.quantize_blocks(ab[rows], gsa)
+    bq, bsf, gsb = Q.quantize_nvfp4(np.ascontiguousarray(bb.T))
+    # the sampled A rows and all of B are bit-exact on the GPU
+    assert np.array_equal(host(a_q)[rows], Q.pack_codes(aq))
+    assert np.array_equal(host(a_sf)[rows], asf)
+    assert np.array_equal(host(b_q), bq) and np.array_equal(host(b_sf), bsf)
+    assert host(gs_a)[0] == gsa and host(gs_b)[0] == gsb[0]
+    ref = bf16_values(O.dense_linear(Q.pack_codes(aq), asf, gsa, bq, bsf, gsb[0]))
+    assert_close(bf16_values(host(c))[rows], ref, "dense linear (sampled rows)")

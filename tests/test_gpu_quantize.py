@@ -1,0 +1,176 @@
+"""GPU parity of quantisation, routing and weight layout: bit-exact against
+the oracle on the same seeded inputs."""
+
+import numpy as np
+import pytest
+import torch
+
+import nvfp4_block_scaled_04_amd as nv
+from nvfp4_block_scaled_04_amd import inputs as I
+from oracle import quantize as Q
+from oracle import route as R
+from oracle import layout as L
+from parity import host
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _bits_to_dev(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(DEV).view(torch.bfloat16)
+
+
+def _check_quant(x_dev, groups=1, gs_in=None, what=""):
+    print(f"[case] quantize {what} shape={tuple(x_dev.shape)} groups={groups}", flush=True)
+    q, sf, gs = nv.quantize(x_dev, groups=groups, gs_in=gs_in)
+    torch.cuda.synchronize()
+    xb = host(x_dev)
+    rq, rsf, rgs = Q.quantize_nvfp4(xb, groups=groups,
+                                    gs_in=None if gs_in is None else host(gs_in))
+    assert np.array_equal(host(gs).view(np.uint32), rgs.view(np.uint32)), what
+    assert np.array_equal(host(sf), rsf), what
+    assert np.array_equal(host(q), rq), what
+    return rq, rsf
+
+
+def test_quantize_tiny_workload_special_blocks():
+    w = I.WORKLOADS["tiny"]
+    x = I.make_x(w, DEV)
+    rq, rsf = _check_quant(x, what="tiny")
+    assert (rsf == 0).sum() >= 1                  # the all-zero block
+
+
+@pytest.mark.parametrize("shape", [(1, 16), (3, 48), (37, 272), (130, 1040), (1000, 7168)])
+def test_quantize_ragged_shapes(shape):
+    g = torch.Generator(device=DEV).manual_seed(shape[0] * 7 + shape[1])
+    x = torch.randn(shape, generator=g, device=DEV).to(torch.bfloat16)
+    _check_quant(x, what=str(shape))
+
+
+def test_quantize_zero_underflow_and_negative_zero_blocks():
+    g = torch.Generator(device=DEV).manual_seed(3)
+    x = torch.randn((64, 256), generator=g, device=DEV)
+    x[1, 0:16] = 0.0
+    x[2, 16:32] = -0.0
+    x[3, 32:48] *= 1e-7                          # far below the underflow threshold
+    x[4, 48:64] *= 3e-5                          # subnormal E4M3 scales
+    x[5, 64:80] = torch.linspace(-1e-4, 1e-4, 16, device=DEV)
+    _check_quant(x.to(torch.bfloat16), what="special")
+
+
+def test_quantize_all_zero_tensor():
+    x = torch.zeros((8, 64), dtype=torch.bfloat16, device=DEV)
+    q, sf, gs = nv.quantize(x)
+    assert host(gs)[0] == 1.0 and not host(q).any() and not host(sf).any()
+
+
+def test_quantize_groups_per_expert_scale():
+    g = torch.Generator(device=DEV).manual_seed(5)
+    x = torch.randn((6 * 32, 256), generator=g, device=DEV)
+    x[32:64] *= 50.0
+    x[128:160] = 0.0                              # an all-zero group: gs = 1
+    _check_quant(x.to(torch.bfloat16), groups=6, what="groups")
+
+
+def test_quantize_precomputed_scale():
+    g = torch.Generator(device=DEV).manual_seed(6)
+    x = torch.randn((96, 512), generator=g, device=DEV).to(torch.bfloat16)
+    gs = torch.tensor([3.0, 700.0, 0.125], device=DEV)
+    _check_quant(x, groups=3, gs_in=gs, what="gs_in")
+
+
+def _all_bf16_in(lo, hi):
+    b = np.arange(1 << 15, dtype=np.uint32)            # non-negative bf16 patterns
+    v = (b << 16).view(np.float32)
+    keep = (v >= lo) & (v <= hi) & np.isfinite(v)
+    return b[keep].astype(np.uint16)
+
+
+def test_e2m1_encoder_exhaustive_over_bf16():
+    # gs = 1 and a leading 6 in every block: scale byte 0x38 (1.0), r = 1, so
+    # every code is E2M1 of the bf16 value itself
+    vals = _all_bf16_in(0.0, 6.0)
+    n = -(-len(vals) // 60) * 4                     # blocks, a multiple of 4 (64-wide rows)
+    pad = np.zeros(n * 15, np.uint16)
+    pad[:len(vals)] = vals
+    blocks = np.concatenate([np.full((n, 1), 0x40C0, np.uint16), pad.reshape(n, 15)], axis=1)
+    signs = np.where(np.arange(n)[:, None] % 2 == 1, np.uint16(0x8000), np.uint16(0))
+    blocks = blocks | signs
+    x = _bits_to_dev(blocks.reshape(-1, 64))
+    _check_quant(x, gs_in=torch.ones(1, device=DEV), what="e2m1 sweep")
+
+
+def test_e4m3_encoder_exhaustive_over_bf16():
+    # gs = 1: a block holding only its amax a gets sf = E4M3(a / 6) for every
+    # bf16 a from the underflow threshold to E4M3's saturation point
+    amax = _all_bf16_in(6 * 2.0 ** -9 * 0.5, 448.0 * 6 * 1.01)
+    blocks = np.zeros((len(amax), 16), np.uint16)
+    blocks[:, 0] = amax
+    blocks[:, 5] = amax ^ 0x8000
+    rows = -(-len(blocks) // 4) * 4
+    full = np.zeros((rows, 16), np.uint16)
+    full[:len(blocks)] = blocks
+    x = _bits_to_dev(full.reshape(-1, 64))
+    _check_quant(x, gs_in=torch.ones(1, device=DEV), what="e4m3 sweep")
+
+
+def test_route_all_workloads_bit_exact():
+    for name in ("tiny", "decode", "prefill", "skewed"):
+        w = I.WORKLOADS[name]
+        ids, _ = I.make_routing(w)
+        print(f"[case] route {name} T={w.T} k={w.k} E={w.E}", flush=True)
+        off, perm, inv, bad = nv.moe_route(torch.from_numpy(ids).to(DEV), w.E)
+        torch.cuda.synchronize()
+        roff, rperm, rinv, rbad = R.route(ids, w.E)
+        assert np.array_equal(host(off), roff), name
+        assert np.array_equal(host(perm), rperm), name
+        assert np.array_equal(host(inv), rinv), name
+        assert host(bad)[0] == rbad == 0
+
+
+@pytest.mark.parametrize("T,k,E,mode", [
+    (0, 4, 8, "uniform"), (1, 1, 1, "uniform"), (5, 3, 7, "uniform"), (3000, 8, 256, "same"),
+    (2000, 6, 384, "uniform"), (777, 2, 16, "invalid"), (40000, 8, 4096, "uniform"),
+])
+def test_route_edge_cases(T, k, E, mode):
+    rng = np.random.default_rng(T + k + E)
+    ids = rng.integers(0, E, size=(T, k)).astype(np.int32)
+    if mode == "same":
+        ids[:] = E - 1
+    if mode == "invalid":
+        ids[rng.random((T, k)) < 0.05] = -3
+        ids[rng.random((T, k)) < 0.05] = E + 2
+    print(f"[case] route edge T={T} k={k} E={E} {mode}", flush=True)
+    off, perm, inv, bad = nv.moe_route(torch.from_numpy(ids).to(DEV), E)
+    torch.cuda.synchronize()
+    roff, rperm, rinv, rbad = R.route(ids, E)
+    assert np.array_equal(host(off), roff)
+    assert np.array_equal(host(perm), rperm)
+    assert np.array_equal(host(inv), rinv)
+    assert host(bad)[0] == rbad
+
+
+@pytest.mark.parametrize("G,Rr,C,inter", [(1, 7, 16, False), (3, 256, 96, True),
+                                          (2, 130, 4096, True), (1, 2048, 7168, False)])
+def test_weight_layout_bit_exact(G, Rr, C, inter):
+    g = torch.Generator(device=DEV).manual_seed(G * Rr + C)
+    w = torch.randn((G, Rr, C), generator=g, device=DEV).to(torch.bfloat16)
+    print(f"[case] layout G={G} R={Rr} C={C} interleave={inter}", flush=True)
+    out = nv.weight_layout(w, inter)
+    torch.cuda.synchronize()
+    wb = host(w)
+    ref = L.interleave_l1(wb) if inter else L.k_major(wb)
+    assert np.array_equal(host(out), ref)
+
+
+def test_expert_weight_prep_bit_exact_tiny():
+    w = I.WORKLOADS["tiny"]
+    from oracle import moe as O
+    w1s, w2s = zip(*[I.make_expert_weights(w, e, DEV) for e in range(w.E)])
+    w1 = torch.stack(w1s)
+    w2 = torch.stack(w2s)
+    ew = nv.prepare_expert_weights([w1], [w2], DEV)
+    torch.cuda.synchronize()
+    ref = O.prepare_weights(host(w1), host(w2))
+    for name in ("w1_q", "w1_sf", "gs_w1", "w2_q", "w2_sf", "gs_w2"):
+        assert np.array_equal(host(getattr(ew, name)), ref[name]), name
