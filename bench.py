@@ -1,0 +1,259 @@
+"""Benchmark of the NVFP4 MoE expert forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill]
+
+A step is one moe_expert_forward over one batch of synthetic, seeded input
+resident in HBM: quantise -> route -> L1 grouped GEMM with the fused SwiGLU +
+NVFP4 requant epilogue -> L2 grouped GEMM -> combine.  W untimed steps, then
+K timed steps between device synchronisations; rank 0 prints one JSON line.
+
+Besides the headline figures the line carries
+  roofline      the dominant kernel (the L1 grouped GEMM) timed with HIP
+                events on the stream the library launches on: algorithmic
+                FLOPs per launch / average launch time vs the FP16 dense MFMA
+                peak (the GEMM's operand dtype);
+  stages        average time of every step of the path, each timed alone;
+  cpu_baseline  the CPU oracle on a bounded sample of the same workload,
+                timed on this host.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import nvfp4_block_scaled_04_amd as nv  # noqa: E402
+from nvfp4_block_scaled_04_amd import inputs as I  # noqa: E402
+
+FP16_MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense FP16 MFMA
+HBM_PEAK_GBS = 8000.0
+# traffic scale: rocprofv3 FETCH_SIZE/WRITE_SIZE of the same command, divided by
+# what they read for a plain copy of known size (see profiles/)
+TRAFFIC = {}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def moe_flops(T, H, Iw, k):
+    """Algorithmic FLOPs of one forward: L1 (2I outputs) + L2 (H outputs)."""
+    return 2.0 * T * k * (H * 2 * Iw + Iw * H)
+
+
+def build_weights(w, dev, chunk=32):
+    w1s, w2s = [], []
+    for e0 in range(0, w.E, chunk):
+        es = range(e0, min(w.E, e0 + chunk))
+        pairs = [I.make_expert_weights(w, e, dev) for e in es]
+        w1s.append(torch.stack([p[0] for p in pairs]))
+        w2s.append(torch.stack([p[1] for p in pairs]))
+        del pairs
+    ew = nv.prepare_expert_weights(w1s, w2s, dev)
+    del w1s, w2s
+    torch.cuda.empty_cache()
+    return ew
+
+
+class Events:
+    """HIP events on the current stream (the one the library launches on)."""
+
+    def __init__(self):
+        self.s = torch.cuda.Event(enable_timing=True)
+        self.e = torch.cuda.Event(enable_timing=True)
+
+    def __enter__(self):
+        self.s.record(torch.cuda.current_stream())
+        return self
+
+    def __exit__(self, *a):
+        self.e.record(torch.cuda.current_stream())
+
+    def ms(self):
+        self.e.synchronize()
+        return self.s.elapsed_time(self.e)
+
+
+def time_loop(fn, steps):
+    torch.cuda.synchronize()
+    ev = Events()
+    with ev:
+        for _ in range(steps):
+            fn()
+    return ev.ms() / steps
+
+
+def bench_moe(w, steps, warmup, dev):
+    log(f"[bench] building weights for {w.name}: E={w.E} H={w.H} I={w.I}")
+    t0 = time.time()
+    ew = build_weights(w, dev)
+    x = I.make_x(w, dev)
+    ids_h, tw_h = I.make_routing(w)
+    ids = torch.from_numpy(ids_h).to(dev)
+    tw = torch.from_numpy(tw_h).to(dev)
+    gs_h = torch.tensor([w.gs_h], dtype=torch.float32, device=dev)
+    out = torch.empty((w.T, w.H), dtype=torch.bfloat16, device=dev)
+    ws = nv.forward_workspace(w.T, w.H, w.I, w.E, w.k, dev)
+    torch.cuda.synchronize()
+    log(f"[bench] inputs ready in {time.time() - t0:.1f}s; warmup {warmup}, timed {steps}")
+
+    step = lambda: nv.moe_expert_forward(x, ids, tw, ew, gs_h, out=out, workspace=ws)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / steps
+    log(f"[bench] forward {ms_step:.3f} ms/step")
+
+    # ---- each step alone, same kernels and arguments, events on the stream
+    T, H, Iw, E, k = w.T, w.H, w.I, w.E, w.k
+    M = T * k
+    a_q, a_sf, gs_a = nv.quantize(x)
+    off, perm, inv, bad = nv.moe_route(ids, E)
+    h_q = torch.empty((M, Iw // 2), dtype=torch.uint8, device=dev)
+    h_sf = torch.empty((M, Iw // 16), dtype=torch.uint8, device=dev)
+    y = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+    qbuf = (a_q, a_sf, gs_a)
+    l1 = lambda: nv.grouped_gemm(nv.EPI_SWIGLU_NVFP4, a_q, a_sf, gs_a, off, ew.w1_q, ew.w1_sf,
+                                 ew.gs_w1, M, a_row_src=perm, a_row_div=k, gs_out=gs_h,
+                                 out=(h_q, h_sf, None))
+    l2 = lambda: nv.grouped_gemm(nv.EPI_BF16, h_q, h_sf, gs_h, off, ew.w2_q, ew.w2_sf, ew.gs_w2,
+                                 M, out=y)
+    stages = {
+        "quantize": lambda: nv.quantize(x, out=qbuf),
+        "route": lambda: nv.moe_route(ids, E),
+        "l1_gemm_swiglu_requant": l1,
+        "l2_gemm": l2,
+        "combine": lambda: nv.moe_combine(y, inv, tw, off, out=out),
+    }
+    st_ms = {}
+    for name, fn in stages.items():
+        fn()
+        st_ms[name] = time_loop(fn, steps)
+    log("[bench] stages (ms): " + ", ".join(f"{n}={v:.4f}" for n, v in st_ms.items()))
+
+    l1_flops = 2.0 * M * (2 * Iw) * H
+    l2_flops = 2.0 * M * H * Iw
+    flops = moe_flops(T, H, Iw, k)
+    achieved = l1_flops / (st_ms["l1_gemm_swiglu_requant"] * 1e-3) / 1e12
+    roof = {"kernel": "grouped_gemm_kernel<SwiGLU+NVFP4 epilogue> (L1)", "bound": "mfma",
+            "achieved": round(achieved, 2), "peak": FP16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / FP16_MFMA_PEAK_TFLOPS, 4),
+            "traffic": TRAFFIC.get((w.name, "l1"))}
+    extra = {
+        "tokens_per_s": T / (ms_step * 1e-3),
+        "l2_gemm_tflops": l2_flops / (st_ms["l2_gemm"] * 1e-3) / 1e12,
+        "quantize_gbs": (2 * T * H + 0.5625 * T * H) / (st_ms["quantize"] * 1e-3) / 1e9,
+        "combine_gbs": (2 * M * H + 12 * M + 2 * T * H) / (st_ms["combine"] * 1e-3) / 1e9,
+        "stages_ms": {n: round(v, 4) for n, v in st_ms.items()},
+    }
+    return flops / (ms_step * 1e-3) / 1e12, ms_step, roof, extra, (x, ids_h, tw_h, ew)
+
+
+def cpu_baseline(w, x, ids_h, tw_h, dev, budget_s=20.0):
+    """The CPU oracle (as it stands) on a bounded sample of the workload:
+    all rows of the first few experts through L1 -> SwiGLU -> requant -> L2,
+    plus quantise and combine for the same share of tokens.  Weight
+    quantisation is preparation on both sides and is not timed."""
+    from threadpoolctl import threadpool_info
+    from oracle import moe as O, quantize as Q, route as R
+
+    xb = x.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    offsets, perm, inv, _ = R.route(ids_h, w.E)
+    done_flops, t_total, experts = 0.0, 0.0, 0
+    per_tok = moe_flops(1, w.H, w.I, w.k)
+    gs_h = np.float32(w.gs_h)
+    t0 = time.perf_counter()
+    gs_a = Q.global_scale(xb)
+    t_total += time.perf_counter() - t0
+    for e in range(w.E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        w1, w2 = I.make_expert_weights(w, e, dev)
+        prep = O.prepare_expert_weights(*[t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+                                          for t in (w1, w2)])
+        tok = perm[lo:hi] // w.k
+        t0 = time.perf_counter()
+        codes, a_sf = Q.quantize_blocks(xb[tok], gs_a)          # this share of the quantise step
+        h = O.l1_swiglu(Q.pack_codes(codes), a_sf, gs_a, prep["w1_q"], prep["w1_sf"], prep["gs_w1"])
+        hc, hsf = Q.quantize_blocks(h, gs_h)
+        y = O.l2(Q.pack_codes(hc), hsf, gs_h, prep["w2_q"], prep["w2_sf"], prep["gs_w2"])
+        t_total += time.perf_counter() - t0
+        done_flops += 2.0 * (hi - lo) * (w.H * 2 * w.I + w.I * w.H)
+        experts += 1
+        if t_total >= budget_s:
+            break
+    rows = int(offsets[experts]) if experts else 0
+    # combine for the same number of rows' tokens (k rows per token)
+    ntok = max(1, rows // w.k)
+    ysim = np.zeros((w.T * w.k, w.H), np.uint16)
+    t0 = time.perf_counter()
+    O.combine(ysim, inv.reshape(w.T, w.k)[:ntok].ravel(), tw_h[:ntok], w.T * w.k)
+    t_total += time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    tflops = done_flops / t_total / 1e12
+    return {"value": round(tflops, 6), "unit": "TFLOPS", "cores": int(threads), "kind": "oracle",
+            "sample": f"{experts} of {w.E} experts ({rows} of {w.T * w.k} expert rows): quantize "
+                      f"+ L1 + SwiGLU + requant + L2 for their rows, combine for {ntok} tokens",
+            "seconds": round(t_total, 2),
+            "tokens_per_s": round(done_flops / per_tok / t_total, 3)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="prefill", choices=["tiny", "decode", "prefill", "skewed"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the expert-parallel "
+              "sharding over several GPUs is a design note, not built.", file=sys.stderr)
+        sys.exit(2)
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    w = I.WORKLOADS[args.workload]
+    value, ms_step, roof, extra, keep = bench_moe(w, args.steps, args.warmup, dev)
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a sample")
+        x, ids_h, tw_h, _ = keep
+        cpu = cpu_baseline(w, x, ids_h, tw_h, dev, args.cpu_budget)
+        log(f"[bench] cpu oracle: {cpu}")
+    line = {
+        "metric": "NVFP4 MoE fwd TFLOPS + tokens/s, T=8192 E=256 top-8; % of MFMA peak",
+        "value": round(value, 3), "unit": "TFLOPS", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp16",
+        "data": "synthetic (seeded; weights N(0,0.02), activations N(0,1))",
+        "config": {"workload": f"{w.name} T={w.T} H={w.H} I={w.I} E={w.E} top-{w.k}",
+                   "tokens": w.T, "hidden": w.H, "intermediate": w.I, "experts": w.E,
+                   "top_k": w.k, "expert_rows": w.M, "parallelism": "single GPU"},
+        "tokens_per_s": round(extra["tokens_per_s"], 1),
+        "frac_fp16_mfma_peak": round(value / FP16_MFMA_PEAK_TFLOPS, 4),
+        "roofline": roof,
+        "stages_ms": extra["stages_ms"],
+        "l2_gemm_tflops": round(extra["l2_gemm_tflops"], 2),
+        "quantize_gbs": round(extra["quantize_gbs"], 1),
+        "combine_gbs": round(extra["combine_gbs"], 1),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
