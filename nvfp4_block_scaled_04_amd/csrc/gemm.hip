@@ -30,9 +30,18 @@
 // and B use the same map, so the dot products are unchanged; each lane reads
 // 32 contiguous bytes of codes per row and stage.
 //
-// Scheduling.  The grid walks (m tile, n tile) pairs; a block finds its
-// expert by scanning the device-side expert offsets (no host sync).  Rows
-// past an expert's count read a clamped valid row and are not stored.
+// Tiling.  A block is 4 waves stacked along N (wave tile 128 N x 128 tokens,
+// 4x4 MFMA blocks, 256 fp32 accumulators per lane); decoding is done per wave
+// from packed codes in LDS, so each decoded element feeds 4 MFMAs.  Stages of
+// 128 K are double-buffered in LDS through registers.  In an expert's last
+// m tile, 32-token column blocks past the expert's rows are skipped.
+//
+// Scheduling.  A persistent grid (a multiple of 8 blocks) walks tiles in
+// windows of gridDim.x; within a window the 8 XCDs each take a contiguous
+// slice, so the blocks of one XCD share an expert's weights and tokens in
+// their L2.  Tiles are ordered expert by expert (device offsets, no host
+// sync); a block finds its expert by binary search of a per-expert tile
+// prefix kept in LDS.
 #include "internal.hpp"
 #include "device.hpp"
 
@@ -44,9 +53,9 @@ typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef _Float16 half8v __attribute__((ext_vector_type(8)));
 typedef float float16v __attribute__((ext_vector_type(16)));
 
-constexpr int BK = 128;          // K elements per stage
+constexpr int BK = 128;            // K elements per stage
 constexpr int ROW_BYTES = BK / 2;  // 64 bytes of codes per row per stage
-constexpr int ROW_STRIDE = 80;   // LDS row stride (64 + 16 pad: conflict-free b128 reads)
+constexpr int ROW_STRIDE = 80;     // LDS row stride (64 + 16 pad: conflict-free b128 reads)
 constexpr int SF_BYTES = BK / 16;  // 8 scale bytes per row per stage
 
 struct Params {
@@ -69,173 +78,177 @@ struct Params {
   int n_tiles;
 };
 
-// decoded value pairs of 8 codes (one dword) times the block scale pair
-__device__ __forceinline__ half8v decode8(uint32_t w, half2v sc) {
-  half2v p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * sc;
-  half2v p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * sc;
-  half2v p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * sc;
-  half2v p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * sc;
+// 8 codes (one dword) -> 8 FP16 values times the block scale
+__device__ __forceinline__ half8v decode8(uint32_t w, _Float16 s) {
+  half2v sc;
+  sc[0] = s;
+  sc[1] = s;
+  const half2v p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * sc;
+  const half2v p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * sc;
+  const half2v p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * sc;
+  const half2v p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * sc;
   half8v r;
   r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
   r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
   return r;
 }
 
-__device__ __forceinline__ half2v scale_pair(uint32_t bytes4, int sel) {
-  float f;
-  switch (sel) {
-    case 0: f = __builtin_amdgcn_cvt_f32_fp8(bytes4, 0); break;
-    case 1: f = __builtin_amdgcn_cvt_f32_fp8(bytes4, 1); break;
-    case 2: f = __builtin_amdgcn_cvt_f32_fp8(bytes4, 2); break;
-    default: f = __builtin_amdgcn_cvt_f32_fp8(bytes4, 3); break;
+// four E4M3 scale bytes -> four FP16 values (exact: E4M3 is a subset of FP16)
+struct Scales4 {
+  half2v lo, hi;
+  __device__ __forceinline__ _Float16 get(int i) const {
+    return i == 0 ? lo[0] : i == 1 ? lo[1] : i == 2 ? hi[0] : hi[1];
   }
-  const _Float16 h = (_Float16)f;   // exact: every E4M3 value is an FP16 value
-  half2v r;
-  r[0] = h; r[1] = h;
-  return r;
+};
+__device__ __forceinline__ Scales4 scales4(uint32_t b) {
+  Scales4 s;
+  s.lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b, 1.0f, false);
+  s.hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b, 1.0f, true);
+  return s;
 }
 
-// LDS row of physical weight row q (0..31) of a 32-row group for SwiGLU:
-// MFMA row 8a+4b+j (a in 0..3, b in 0..1, j in 0..3) reads physical row
-// 16b + 4(a/2) + 8(a%2) + j, so lane half b holds gate/up of h columns
-// 8b..8b+7 of the group's 16-column h block.
-__device__ __forceinline__ int swiglu_lds_row(int q) {
-  const int b = q >> 4, rem = q & 15;
-  const int a = 2 * ((rem & 7) >> 2) + (rem >> 3);
-  return 8 * a + 4 * b + (rem & 3);
+__device__ __forceinline__ uint32_t pick(const uint4& q, int i) {
+  return i == 0 ? q.x : i == 1 ? q.y : i == 2 ? q.z : q.w;
 }
 
-// Block-wide search of the expert owning m tile `tile`: experts are split in
-// contiguous ranges over the threads, range sums of ceil(count/BM) are
-// scanned in LDS, and the owning thread walks its range.  Writes e = -1 when
-// tile is past the last tile.
-template <int NT, int BM>
-__device__ __forceinline__ void find_tile(const int32_t* offsets, int E, int tile, int* scan,
-                                          int& s_expert, int& s_row0, int& s_rows) {
-  const int tid = threadIdx.x;
-  const int per = (E + NT - 1) / NT;
-  const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
-  int local = 0;
-  for (int e = e0; e < e1; ++e) local += (offsets[e + 1] - offsets[e] + BM - 1) / BM;
-  scan[tid] = local;
-  if (tid == 0) s_expert = -1;
-  __syncthreads();
-  for (int off = 1; off < NT; off <<= 1) {
-    const int v = tid >= off ? scan[tid - off] : 0;
-    __syncthreads();
-    scan[tid] += v;
-    __syncthreads();
-  }
-  int acc = scan[tid] - local;
-  if (tile >= acc && tile < acc + local) {
-    for (int e = e0; e < e1; ++e) {
-      const int c = offsets[e + 1] - offsets[e];
-      const int t = (c + BM - 1) / BM;
-      if (tile < acc + t) {
-        s_expert = e;
-        s_row0 = offsets[e] + (tile - acc) * BM;
-        s_rows = min(BM, offsets[e + 1] - s_row0);
-        break;
-      }
-      acc += t;
-    }
-  }
-  __syncthreads();
+// SwiGLU row order inside a 32-row weight group: MFMA row x = 8a+4b+j
+// (a in 0..3, b in 0..1, j in 0..3) reads physical row 16b + 4(a/2) +
+// 8(a%2) + j, so lane half b holds gate and up of h columns 8b..8b+7 of the
+// group's 16-column h block (gate in accumulator rows 8a'+.., up 8 rows on).
+__device__ __forceinline__ int swiglu_phys_row(int x) {
+  const int a = x >> 3, b = (x >> 2) & 1, j = x & 3;
+  return 16 * b + 4 * (a >> 1) + 8 * (a & 1) + j;
 }
 
-template <int BN, int BM, int WN, int WM, int EPI>
-__global__ __launch_bounds__(WN * WM * 64) void grouped_gemm_kernel(Params p) {
-  constexpr int NT = WN * WM * 64;
-  constexpr int TN = BN / WN, TM = BM / WM;    // wave tile
-  constexpr int FN = TN / 32, FM = TM / 32;    // 32x32 MFMA blocks per wave
-  constexpr int ROWS = BN + BM;                // LDS rows per stage (weights then tokens)
-  constexpr int CODE_BYTES = ROWS * ROW_STRIDE;
-  constexpr int STAGE_BYTES = CODE_BYTES + ROWS * SF_BYTES;
-  constexpr int CHUNKS = ROWS * 4;             // 16-byte code chunks per stage
-  constexpr int CPT = (CHUNKS + NT - 1) / NT;  // chunks per thread
-  constexpr int SPT = (ROWS + NT - 1) / NT;    // scale rows per thread
+// LDS layout of one stage: ROWS rows of 64 code bytes (four 16-byte chunks,
+// chunk q of row r stored at position q ^ ((r >> 2) & 3): conflict-free
+// 16-byte reads for 16 consecutive rows), then ROWS rows of 8 scale bytes.
+template <int BN, int BM, int WN, int WM>
+struct Cfg {
+  static constexpr int NT = WN * WM * 64;
+  static constexpr int NW = WN * WM;
+  static constexpr int TN = BN / WN, TM = BM / WM;     // wave tile
+  static constexpr int FN = TN / 32, FM = TM / 32;     // 32x32 MFMA blocks per wave
+  static constexpr int ROWS = BN + BM;                 // LDS rows per stage: weights, tokens
+  static constexpr int CODE_BYTES = ROWS * ROW_BYTES;
+  static constexpr int STAGE_BYTES = CODE_BYTES + ROWS * SF_BYTES;
+  static constexpr int NBUF = 3;                       // LDS stage buffers
+  static constexpr int LDS_BYTES = NBUF * STAGE_BYTES;
+  // direct-to-LDS loads: a code load fills 16 rows, a scale load 32 rows
+  static constexpr int CODE_LOADS = ROWS / 16 / NW;    // per wave per stage
+  static constexpr int CODE_LOADS_W = BN / 16 / NW;    // ... of which weight rows
+  static constexpr int SF_LOADS = ROWS / 32 / NW;
+  static constexpr int SF_LOADS_W = BN / 32 / NW;
   static_assert(TN % 32 == 0 && TM % 32 == 0, "wave tile must be a multiple of 32");
+  static_assert(ROWS % (16 * NW) == 0 && BN % (16 * NW) == 0, "code loads must divide evenly");
+  static_assert(ROWS % (32 * NW) == 0 && BN % (32 * NW) == 0, "scale loads must divide evenly");
+  static_assert(WM == 1, "column-block skipping assumes one wave row");
+};
 
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  __shared__ int s_expert, s_row0, s_rows;
-  __shared__ int s_scan[NT];
+__device__ __forceinline__ int chunk_pos(int row, int q) { return q ^ ((row >> 2) & 3); }
 
+// One tile: the K loop and the epilogue.  JV = number of 32-token column
+// blocks that hold rows (1..FM); the rest are skipped.
+template <int BN, int BM, int WN, int WM, int EPI, int JV>
+__device__ __forceinline__ void run_tile(const Params& p, uint8_t* smem, int e, int row0,
+                                         int nrows, int64_t n0) {
+  using C = Cfg<BN, BM, WN, WM>;
+  constexpr int FN = C::FN, FM = C::FM, TN = C::TN, TM = C::TM;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wn = wave % WN, wm = wave / WN;
+  const int hf = lane >> 5, l32 = lane & 31;
+  const int64_t N = p.N, K = p.K;
+  const uint32_t kb = (uint32_t)(K / 2), ksf = (uint32_t)(K / 16);
+  const uint8_t* wbase = p.b_q + (int64_t)e * N * kb;
+  const uint8_t* wsbase = p.b_sf + (int64_t)e * N * ksf;
 
-  // ---- which expert / m tile is this block? (prefix of ceil(count/BM))
-  const int tile = blockIdx.x / p.n_tiles;
-  const int ntile = blockIdx.x % p.n_tiles;
-  find_tile<NT, BM>(p.offsets, p.E, tile, s_scan, s_expert, s_row0, s_rows);
-  const int e = s_expert;
-  if (e < 0) return;
-  const int row0 = s_row0, nrows = s_rows;
-  const int64_t n0 = (int64_t)ntile * BN;
-  const int64_t K = p.K;
-  const int64_t kb = K / 2, ksf = K / 16;
-
-  // ---- global source rows of this thread's chunks (weights, then tokens)
-  const uint8_t* src_code[CPT];
-  const uint8_t* src_sf[SPT];
-  int lds_code[CPT], lds_sf[SPT];
-  bool has_code[CPT], has_sf[SPT];
-  auto row_ptrs = [&](int r, const uint8_t*& code, const uint8_t*& sf, int& lrow) {
+  // global source row of LDS row r (weights: clamped to N-1, SwiGLU order;
+  // tokens: clamped to the tile's last row, gathered through a_row_src)
+  auto src_row = [&](int r) -> uint32_t {
     if (r < BN) {
-      int64_t n = n0 + r;
-      if (n >= p.N) n = p.N - 1;
-      code = p.b_q + ((int64_t)e * p.N + n) * kb;
-      sf = p.b_sf + ((int64_t)e * p.N + n) * ksf;
-      lrow = (EPI == NVFP4_EPI_SWIGLU_NVFP4) ? ((r & ~31) | swiglu_lds_row(r & 31)) : r;
-    } else {
-      const int i = r - BN;
-      int d = row0 + (i < nrows ? i : nrows - 1);
-      int64_t arow = p.a_row_src ? (int64_t)(p.a_row_src[d] / p.a_row_div) : (int64_t)d;
-      code = p.a_q + arow * kb;
-      sf = p.a_sf + arow * ksf;
-      lrow = r;
+      const int q = (EPI == NVFP4_EPI_SWIGLU_NVFP4) ? ((r & ~31) | swiglu_phys_row(r & 31)) : r;
+      const int64_t n = n0 + q;
+      return (uint32_t)(n < N ? n : N - 1);
     }
+    const int i = r - BN;
+    const int d = row0 + (i < nrows ? i : nrows - 1);
+    return (uint32_t)(p.a_row_src ? p.a_row_src[d] / p.a_row_div : d);
   };
+  // per-lane byte offsets of this wave's direct loads (stage 0)
+  uint32_t coff[C::CODE_LOADS], soff[C::SF_LOADS];
 #pragma unroll
-  for (int c = 0; c < CPT; ++c) {
-    const int chunk = tid + c * NT;
-    has_code[c] = chunk < CHUNKS;
-    const int r = has_code[c] ? chunk >> 2 : 0;
-    const uint8_t* sfp;
-    int lrow;
-    row_ptrs(r, src_code[c], sfp, lrow);
-    src_code[c] += (chunk & 3) * 16;
-    lds_code[c] = lrow * ROW_STRIDE + (chunk & 3) * 16;
+  for (int c = 0; c < C::CODE_LOADS; ++c) {
+    const int g = c * C::NW + wave;                // 16-row group
+    const int r = 16 * g + (lane >> 2);
+    const int q = chunk_pos(r, lane & 3);          // logical chunk stored at this lane's position
+    coff[c] = src_row(r) * kb + 16 * q;
   }
 #pragma unroll
-  for (int c = 0; c < SPT; ++c) {
-    const int r0 = tid + c * NT;
-    has_sf[c] = r0 < ROWS;
-    const uint8_t* cp;
-    int lrow;
-    row_ptrs(has_sf[c] ? r0 : 0, cp, src_sf[c], lrow);
-    lds_sf[c] = CODE_BYTES + lrow * SF_BYTES;
+  for (int c = 0; c < C::SF_LOADS; ++c) {
+    const int g = c * C::NW + wave;                // 32-row group
+    const int r = 32 * g + (lane >> 1);
+    soff[c] = src_row(r) * ksf + 4 * (lane & 1);
   }
 
-  uint4 stage_code[CPT];
-  uint2 stage_sf[SPT];
-  auto gload = [&](int ks) {
-#pragma unroll
-    for (int c = 0; c < CPT; ++c)
-      if (has_code[c]) stage_code[c] = *reinterpret_cast<const uint4*>(src_code[c] + ks * ROW_BYTES);
-#pragma unroll
-    for (int c = 0; c < SPT; ++c)
-      if (has_sf[c]) stage_sf[c] = *reinterpret_cast<const uint2*>(src_sf[c] + ks * SF_BYTES);
-  };
-  auto lstore = [&](int buf) {
-    uint8_t* base = smem + buf * STAGE_BYTES;
-#pragma unroll
-    for (int c = 0; c < CPT; ++c)
-      if (has_code[c]) *reinterpret_cast<uint4*>(base + lds_code[c]) = stage_code[c];
-#pragma unroll
-    for (int c = 0; c < SPT; ++c)
-      if (has_sf[c]) *reinterpret_cast<uint2*>(base + lds_sf[c]) = stage_sf[c];
-  };
+// loads of stage `ks` into LDS buffer `buf`; only the instructions whose
+// index is congruent to `part` mod 4 (so a stage's 15 loads spread over 4 steps)
+#define NVFP4_ISSUE(ks, buf, part)                                                              \
+  do {                                                                                          \
+    uint8_t* sbw = smem + (buf) * C::STAGE_BYTES;                                               \
+    _Pragma("unroll") for (int c = 0; c < C::CODE_LOADS; ++c) {                                 \
+      if ((part) < 0 || (c & 3) == (part)) {                                                    \
+        const uint8_t* b = (c < C::CODE_LOADS_W) ? wbase : p.a_q;                               \
+        __builtin_amdgcn_global_load_lds(b + coff[c] + (uint32_t)(ks) * ROW_BYTES,              \
+                                         sbw + (c * C::NW + wave) * 1024, 16, 0, 0);            \
+      }                                                                                         \
+    }                                                                                           \
+    _Pragma("unroll") for (int c = 0; c < C::SF_LOADS; ++c) {                                   \
+      if ((part) < 0 || ((c + 2) & 3) == (part)) {                                              \
+        const uint8_t* b = (c < C::SF_LOADS_W) ? wsbase : p.a_sf;                               \
+        __builtin_amdgcn_global_load_lds(b + soff[c] + (uint32_t)(ks) * SF_BYTES,               \
+                                         sbw + C::CODE_BYTES + (c * C::NW + wave) * 256, 4, 0, 0); \
+      }                                                                                         \
+    }                                                                                           \
+  } while (0)
+
+// fragment reads: half h (0 or 1) of every A and B block of the stage in
+// buffer `buf`: 16 contiguous code bytes per lane and block
+#define NVFP4_READ_HALF(buf, h, WA, TB)                                                         \
+  do {                                                                                          \
+    const uint8_t* sbr = smem + (buf) * C::STAGE_BYTES;                                         \
+    _Pragma("unroll") for (int i = 0; i < FN; ++i) {                                            \
+      const int r = wn * TN + i * 32 + l32;                                                     \
+      WA[i] = *reinterpret_cast<const uint4*>(sbr + r * ROW_BYTES + 16 * chunk_pos(r, 2 * hf + (h))); \
+    }                                                                                           \
+    _Pragma("unroll") for (int j = 0; j < JV; ++j) {                                            \
+      const int r = BN + wm * TM + j * 32 + l32;                                                \
+      TB[j] = *reinterpret_cast<const uint4*>(sbr + r * ROW_BYTES + 16 * chunk_pos(r, 2 * hf + (h))); \
+    }                                                                                           \
+  } while (0)
+
+#define NVFP4_READ_SF(buf, WS, TS)                                                              \
+  do {                                                                                          \
+    const uint8_t* sbr = smem + (buf) * C::STAGE_BYTES + C::CODE_BYTES;                         \
+    _Pragma("unroll") for (int i = 0; i < FN; ++i)                                              \
+      WS[i] = *reinterpret_cast<const uint32_t*>(sbr + (wn * TN + i * 32 + l32) * SF_BYTES + hf * 4); \
+    _Pragma("unroll") for (int j = 0; j < JV; ++j)                                              \
+      TS[j] = *reinterpret_cast<const uint32_t*>(sbr + (BN + wm * TM + j * 32 + l32) * SF_BYTES + hf * 4); \
+  } while (0)
+
+// one 16-deep K step: decode dword (s & 3) of the half fragments with scale
+// byte (s >> 1), then FN x JV MFMAs
+#define NVFP4_STEP(s, WA, TB, WSC, TSC)                                                         \
+  do {                                                                                          \
+    half8v av[FN], bv[FM];                                                                      \
+    _Pragma("unroll") for (int i = 0; i < FN; ++i)                                              \
+      av[i] = decode8(pick(WA[i], (s) & 3), WSC[i].get((s) >> 1));                              \
+    _Pragma("unroll") for (int j = 0; j < JV; ++j)                                              \
+      bv[j] = decode8(pick(TB[j], (s) & 3), TSC[j].get((s) >> 1));                              \
+    _Pragma("unroll") for (int i = 0; i < FN; ++i)                                              \
+      _Pragma("unroll") for (int j = 0; j < JV; ++j)                                            \
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);   \
+  } while (0)
 
   float16v acc[FN][FM];
 #pragma unroll
@@ -245,107 +258,131 @@ __global__ __launch_bounds__(WN * WM * 64) void grouped_gemm_kernel(Params p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  const int hf = lane >> 5, l32 = lane & 31;
+  // Pipeline (three LDS buffers, stage ks in buffer ks % 3):
+  //   stage ks, steps 0-3: half A fragments (already in registers); the loads
+  //     of stage ks+2 are issued, a quarter per step; half B fragments of
+  //     stage ks are read from LDS;
+  //   steps 4-5: half B;  then wait until stage ks+1 has landed (the loads
+  //     of ks+2 may stay in flight) and synchronise the block;
+  //   the half A fragments and scales of stage ks+1 are read from LDS;
+  //   steps 6-7: half B.
+  // Buffer (ks+2) % 3 was last read before the mid-stage barrier of ks-1.
   const int nks = (int)(K / BK);
-  gload(0);
-  lstore(0);
-  __syncthreads();
-
-  for (int ks = 0; ks < nks; ++ks) {
-    const int buf = ks & 1;
-    if (ks + 1 < nks) gload(ks + 1);
-    const uint8_t* base = smem + buf * STAGE_BYTES;
-    // fragments: 32 bytes of codes + 4 scale bytes per 32-row block per lane
-    uint4 wa[FN][2], tb[FM][2];
-    uint32_t wsf[FN], tsf[FM];
-#pragma unroll
-    for (int i = 0; i < FN; ++i) {
-      const int r = wn * TN + i * 32 + l32;
-      wa[i][0] = *reinterpret_cast<const uint4*>(base + r * ROW_STRIDE + hf * 32);
-      wa[i][1] = *reinterpret_cast<const uint4*>(base + r * ROW_STRIDE + hf * 32 + 16);
-      wsf[i] = *reinterpret_cast<const uint32_t*>(base + CODE_BYTES + r * SF_BYTES + hf * 4);
-    }
-#pragma unroll
-    for (int j = 0; j < FM; ++j) {
-      const int r = BN + wm * TM + j * 32 + l32;
-      tb[j][0] = *reinterpret_cast<const uint4*>(base + r * ROW_STRIDE + hf * 32);
-      tb[j][1] = *reinterpret_cast<const uint4*>(base + r * ROW_STRIDE + hf * 32 + 16);
-      tsf[j] = *reinterpret_cast<const uint32_t*>(base + CODE_BYTES + r * SF_BYTES + hf * 4);
-    }
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      half8v av[FN], bv[FM];
-#pragma unroll
-      for (int i = 0; i < FN; ++i) {
-        const uint4& q = wa[i][s >> 2];
-        const uint32_t w = (s & 3) == 0 ? q.x : (s & 3) == 1 ? q.y : (s & 3) == 2 ? q.z : q.w;
-        av[i] = decode8(w, scale_pair(wsf[i], s >> 1));
-      }
-#pragma unroll
-      for (int j = 0; j < FM; ++j) {
-        const uint4& q = tb[j][s >> 2];
-        const uint32_t w = (s & 3) == 0 ? q.x : (s & 3) == 1 ? q.y : (s & 3) == 2 ? q.z : q.w;
-        bv[j] = decode8(w, scale_pair(tsf[j], s >> 1));
-      }
-#pragma unroll
-      for (int i = 0; i < FN; ++i)
-#pragma unroll
-        for (int j = 0; j < FM; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
-    }
-    if (ks + 1 < nks) lstore(buf ^ 1);
-    __syncthreads();
+  NVFP4_ISSUE(0, 0, -1);
+  if (nks > 1) {
+    NVFP4_ISSUE(1, 1, -1);
+    asm volatile("s_waitcnt vmcnt(15)" ::: "memory");
+  } else {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
+  __syncthreads();
+  static_assert(C::CODE_LOADS + C::SF_LOADS == 15, "vmcnt immediates assume 15 loads per stage");
+
+  uint4 fa[FN], ta[FM], fb[FN], tb[FM];
+  uint32_t wsr[FN], tsr[FM];
+  NVFP4_READ_HALF(0, 0, fa, ta);
+  NVFP4_READ_SF(0, wsr, tsr);
+
+  int buf = 0;
+  for (int ks = 0; ks < nks; ++ks) {
+    Scales4 wsc[FN], tsc[FM];
+#pragma unroll
+    for (int i = 0; i < FN; ++i) wsc[i] = scales4(wsr[i]);
+#pragma unroll
+    for (int j = 0; j < JV; ++j) tsc[j] = scales4(tsr[j]);
+    NVFP4_READ_HALF(buf, 1, fb, tb);
+    const bool more2 = ks + 2 < nks;
+    const int buf2 = buf == 0 ? 2 : buf - 1;           // (ks + 2) % 3
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      if (more2) NVFP4_ISSUE(ks + 2, buf2, s);
+      NVFP4_STEP(s, fa, ta, wsc, tsc);
+    }
+    NVFP4_STEP(4, fb, tb, wsc, tsc);
+    NVFP4_STEP(5, fb, tb, wsc, tsc);
+    if (more2) asm volatile("s_waitcnt vmcnt(15)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    const int buf1 = buf == 2 ? 0 : buf + 1;           // (ks + 1) % 3
+    if (ks + 1 < nks) {
+      NVFP4_READ_HALF(buf1, 0, fa, ta);
+      NVFP4_READ_SF(buf1, wsr, tsr);
+    }
+    NVFP4_STEP(6, fb, tb, wsc, tsc);
+    NVFP4_STEP(7, fb, tb, wsc, tsc);
+    buf = buf1;
+  }
+#undef NVFP4_ISSUE
+#undef NVFP4_READ_HALF
+#undef NVFP4_READ_SF
+#undef NVFP4_STEP
+  __syncthreads();   // every wave is done with the stage buffers (the epilogue reuses LDS)
 
   // ---- epilogue
   const float alpha = 1.0f / (p.gs_a[0] * p.gs_b[e]);
   if constexpr (EPI == NVFP4_EPI_BF16) {
+    // stage the wave's TN x TM tile in LDS as token rows of TN bf16 (a
+    // 256-byte pitch, 16-byte chunk q of row t stored at q ^ (t & 15)), then
+    // write each token row with 16-byte stores
+    constexpr int PITCH = TN * 2;
+    static_assert(PITCH == 256, "the chunk swizzle assumes 16 chunks per row");
+    static_assert(C::NW * TM * PITCH <= C::LDS_BYTES, "epilogue tile must fit the stage buffers");
+    uint8_t* tile = smem + wave * TM * PITCH;
 #pragma unroll
-    for (int i = 0; i < FN; ++i)
+    for (int j = 0; j < JV; ++j) {
+      const int tok = j * 32 + l32;
 #pragma unroll
-      for (int j = 0; j < FM; ++j) {
-        const int tok = wm * TM + j * 32 + l32;
-        if (tok >= nrows) continue;
-        const int64_t d = row0 + tok;
+      for (int i = 0; i < FN; ++i) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int64_t n = n0 + wn * TN + i * 32 + 8 * g + 4 * hf;
-          if (n >= p.N) continue;
           uint2 o;
           o.x = f32_to_bf16_rne(acc[i][j][4 * g + 0] * alpha) |
                 (f32_to_bf16_rne(acc[i][j][4 * g + 1] * alpha) << 16);
           o.y = f32_to_bf16_rne(acc[i][j][4 * g + 2] * alpha) |
                 (f32_to_bf16_rne(acc[i][j][4 * g + 3] * alpha) << 16);
-          *reinterpret_cast<uint2*>(p.c_bf16 + d * p.N + n) = o;
+          const int cb = (i * 32 + 8 * g + 4 * hf) * 2;          // byte column
+          *reinterpret_cast<uint2*>(tile + tok * PITCH + (((cb >> 4) ^ (tok & 15)) << 4) + (cb & 15)) = o;
         }
       }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_wave_barrier();
+    // 16 lanes cover one token row (TN bf16 = 256 bytes); 4 rows per instruction
+    const int64_t nw0 = n0 + wn * TN;
+    const int col = (lane & 15) * 8;           // bf16 column within the wave's TN
+    const bool col_ok = nw0 + col < N;         // N % 32 == 0: a 16-byte piece is all in or out
+    for (int t = lane >> 4; t < JV * 32; t += 4) {
+      if (t >= nrows || !col_ok) continue;
+      const uint4 v = *reinterpret_cast<const uint4*>(tile + t * PITCH + (((lane & 15) ^ (t & 15)) << 4));
+      *reinterpret_cast<uint4*>(p.c_bf16 + (int64_t)(row0 + t) * N + nw0 + col) = v;
+    }
   } else {
     const float gs_h = p.gs_out[0];
-    const int64_t I = p.N / 2;
+    const int64_t I = N / 2;
 #pragma unroll
     for (int i = 0; i < FN; ++i) {
-      // this 32-row N block is h block hb = (n0 + wn*TN + 32 i) / 32
+      // this 32-row N block is h block hb (16 h columns)
       const int64_t nb = n0 + wn * TN + i * 32;
       const int64_t hb = nb / 32;
 #pragma unroll
-      for (int j = 0; j < FM; ++j) {
+      for (int j = 0; j < JV; ++j) {
         const int tok = wm * TM + j * 32 + l32;
         float h[8];
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
-          const int gi = (q < 4) ? q : 8 + (q - 4);      // gate register
+          const int gi = (q < 4) ? q : 8 + (q - 4);      // gate register; up is gi + 4
           const float g = acc[i][j][gi] * alpha;
           const float u = acc[i][j][gi + 4] * alpha;
           h[q] = (g / (1.0f + __expf(-g))) * u;
         }
-        // block amax over 16 h columns: 8 here, 8 in lane l^32
+        // block amax over 16 h columns: 8 in this lane, 8 in lane l^32
         float m = 0.0f;
 #pragma unroll
         for (int q = 0; q < 8; ++q) m = fmaxf(m, fabsf(h[q]));
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m),
-                                                         false, false);
-        const float amax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-        if (tok >= nrows || nb >= p.N) continue;
+        const auto swp = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m),
+                                                          false, false);
+        const float amax = fmaxf(__uint_as_float(swp[0]), __uint_as_float(swp[1]));
+        if (tok >= nrows || nb >= N) continue;
         const int64_t d = row0 + tok;
         uint32_t codes = 0, sfb = 0;
         {
@@ -358,17 +395,16 @@ __global__ __launch_bounds__(WN * WM * 64) void grouped_gemm_kernel(Params p) {
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
               const float v = fminf(fabsf(h[q] * r), 6.0f);
-              const uint32_t c = e2m1_encode(v) | ((__float_as_uint(h[q]) >> 31) << 3);
-              codes |= c << (4 * q);
+              codes |= (e2m1_encode(v) | ((__float_as_uint(h[q]) >> 31) << 3)) << (4 * q);
             }
           }
         }
         *reinterpret_cast<uint32_t*>(p.c_q + d * (I / 2) + hb * 8 + hf * 4) = codes;
         if (hf == 0) p.c_sf[d * (I / 16) + hb] = (uint8_t)sfb;
         if (p.c_debug != nullptr) {
-          float* dst = p.c_debug + d * I + hb * 16 + hf * 8;
-#pragma unroll
-          for (int q = 0; q < 8; ++q) dst[q] = h[q];
+          float4* dst = reinterpret_cast<float4*>(p.c_debug + d * I + hb * 16 + hf * 8);
+          dst[0] = make_float4(h[0], h[1], h[2], h[3]);
+          dst[1] = make_float4(h[4], h[5], h[6], h[7]);
         }
       }
     }
@@ -376,35 +412,112 @@ __global__ __launch_bounds__(WN * WM * 64) void grouped_gemm_kernel(Params p) {
 }
 
 template <int BN, int BM, int WN, int WM, int EPI>
+__global__ __launch_bounds__(WN * WM * 64, 1) void grouped_gemm_kernel(Params p) {
+  using C = Cfg<BN, BM, WN, WM>;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  int* tprefix = reinterpret_cast<int*>(smem + C::LDS_BYTES);   // [E + 1]
+  __shared__ int s_scan[C::NT];
+  const int tid = threadIdx.x;
+
+  // per-expert m-tile prefix (tiles of BM rows), once per block
+  {
+    const int E = p.E;
+    const int per = (E + C::NT - 1) / C::NT;
+    const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
+    int local = 0;
+    for (int e = e0; e < e1; ++e) local += (p.offsets[e + 1] - p.offsets[e] + BM - 1) / BM;
+    s_scan[tid] = local;
+    __syncthreads();
+    for (int off = 1; off < C::NT; off <<= 1) {
+      const int v = tid >= off ? s_scan[tid - off] : 0;
+      __syncthreads();
+      s_scan[tid] += v;
+      __syncthreads();
+    }
+    int acc = s_scan[tid] - local;
+    for (int e = e0; e < e1; ++e) {
+      tprefix[e] = acc;
+      acc += (p.offsets[e + 1] - p.offsets[e] + BM - 1) / BM;
+    }
+    if (tid == C::NT - 1) tprefix[E] = s_scan[C::NT - 1];
+    __syncthreads();
+  }
+  const int total_m = tprefix[p.E];
+  const int G = gridDim.x;                 // a multiple of 8
+  const int slice = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+  for (int base = 0;; base += G) {
+    const int logical = base + slice;
+    const int mt = logical / p.n_tiles;
+    if (mt >= total_m) break;
+    const int nt = logical - mt * p.n_tiles;
+    // expert owning m tile mt: the largest e with tprefix[e] <= mt
+    int lo = 0, hi = p.E - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (tprefix[mid] <= mt) lo = mid; else hi = mid - 1;
+    }
+    const int e = lo;
+    const int row0 = p.offsets[e] + (mt - tprefix[e]) * BM;
+    const int nrows = min(BM, p.offsets[e + 1] - row0);
+    const int64_t n0 = (int64_t)nt * BN;
+    const int jv = (nrows + 31) / 32;      // occupied 32-token column blocks
+    if (jv >= C::FM) {
+      run_tile<BN, BM, WN, WM, EPI, C::FM>(p, smem, e, row0, nrows, n0);
+    } else if constexpr (C::FM > 1) {
+      if (jv == 1) run_tile<BN, BM, WN, WM, EPI, 1>(p, smem, e, row0, nrows, n0);
+      else if constexpr (C::FM > 2) {
+        if (jv == 2) run_tile<BN, BM, WN, WM, EPI, 2>(p, smem, e, row0, nrows, n0);
+        else if constexpr (C::FM > 3) run_tile<BN, BM, WN, WM, EPI, 3>(p, smem, e, row0, nrows, n0);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+int g_cu_count = 0;
+
+template <int BN, int BM, int WN, int WM, int EPI>
 hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
+  using C = Cfg<BN, BM, WN, WM>;
   Params p;
   p.a_q = a.a_q; p.a_sf = a.a_sf; p.gs_a = a.gs_a; p.a_row_src = a.a_row_src;
   p.a_row_div = a.a_row_div; p.offsets = a.offsets; p.E = a.E; p.M = a.M; p.N = a.N; p.K = a.K;
   p.b_q = a.b_q; p.b_sf = a.b_sf; p.gs_b = a.gs_b; p.gs_out = a.gs_out;
   p.c_bf16 = static_cast<uint16_t*>(a.c_bf16); p.c_q = a.c_q; p.c_sf = a.c_sf; p.c_debug = a.c_debug;
   p.n_tiles = (int)((a.N + BN - 1) / BN);
+  if (a.M == 0) return hipSuccess;
+  if (g_cu_count == 0) {
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    err = hipDeviceGetAttribute(&g_cu_count, hipDeviceAttributeMultiprocessorCount, dev);
+    if (err != hipSuccess) return err;
+  }
   const int64_t m_tiles = (a.M + BM - 1) / BM + a.E;   // upper bound on sum ceil(count/BM)
-  const int64_t blocks = m_tiles * p.n_tiles;
-  if (a.M == 0 || blocks == 0) return hipSuccess;
-  constexpr int ROWS = BN + BM;
-  constexpr size_t lds = 2 * (size_t)(ROWS * ROW_STRIDE + ROWS * SF_BYTES);
+  const int64_t tiles = m_tiles * p.n_tiles;
+  int64_t grid = g_cu_count;                              // one block per CU (LDS-limited)
+  if (grid > tiles) grid = tiles;
+  grid = (grid + 7) / 8 * 8;
+  const size_t lds = (size_t)C::LDS_BYTES + sizeof(int) * (size_t)(a.E + 1);
   auto kern = grouped_gemm_kernel<BN, BM, WN, WM, EPI>;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+                                         hipFuncAttributeMaxDynamicSharedMemorySize,
+                                         (int)(C::LDS_BYTES + sizeof(int) * 4097));
     if (err != hipSuccess) return err;
     attr_set = true;
   }
-  kern<<<(unsigned)blocks, WN * WM * 64, lds, stream>>>(p);
+  kern<<<(unsigned)grid, C::NT, lds, stream>>>(p);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t stream) {
-  if (a.epilogue == NVFP4_EPI_SWIGLU_NVFP4) return launch_cfg<128, 128, 2, 2, NVFP4_EPI_SWIGLU_NVFP4>(a, stream);
-  return launch_cfg<128, 128, 2, 2, NVFP4_EPI_BF16>(a, stream);
+  if (a.epilogue == NVFP4_EPI_SWIGLU_NVFP4)
+    return launch_cfg<512, 128, 4, 1, NVFP4_EPI_SWIGLU_NVFP4>(a, stream);
+  return launch_cfg<512, 128, 4, 1, NVFP4_EPI_BF16>(a, stream);
 }
 
 }  // namespace nvfp4
