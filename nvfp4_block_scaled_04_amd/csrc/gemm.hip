@@ -147,6 +147,12 @@ struct Cfg {
 
 __device__ __forceinline__ int chunk_pos(int row, int q) { return q ^ ((row >> 2) & 3); }
 
+// step (0..6) of the K loop that issues stage load L (0..14): 3, then 2 per step
+__host__ __device__ constexpr int load_step(int L) { return L < 3 ? 0 : (L - 1) / 2; }
+// loads issued in steps 0..3, still in flight at the mid-stage wait
+constexpr int kLoadsBeforeBarrier = 9;
+static_assert(load_step(8) == 3 && load_step(9) == 4 && load_step(14) == 6, "load schedule");
+
 // One tile: the K loop and the epilogue.  JV = number of 32-token column
 // blocks that hold rows (1..FM); the rest are skipped.
 template <int BN, int BM, int WN, int WM, int EPI, int JV>
@@ -191,20 +197,21 @@ __device__ __forceinline__ void run_tile(const Params& p, uint8_t* smem, int e, 
     soff[c] = src_row(r) * ksf + 4 * (lane & 1);
   }
 
-// loads of stage `ks` into LDS buffer `buf`; only the instructions whose
-// index is congruent to `part` mod 4 (so a stage's 15 loads spread over 4 steps)
+// loads of stage `ks` into LDS buffer `buf`.  Load L (codes 0..CODE_LOADS-1,
+// then scales) is issued in step load_step(L) of the loop (part = step), or
+// all at once (part = -1).
 #define NVFP4_ISSUE(ks, buf, part)                                                              \
   do {                                                                                          \
     uint8_t* sbw = smem + (buf) * C::STAGE_BYTES;                                               \
     _Pragma("unroll") for (int c = 0; c < C::CODE_LOADS; ++c) {                                 \
-      if ((part) < 0 || (c & 3) == (part)) {                                                    \
+      if ((part) < 0 || load_step(c) == (part)) {                                               \
         const uint8_t* b = (c < C::CODE_LOADS_W) ? wbase : p.a_q;                               \
         __builtin_amdgcn_global_load_lds(b + coff[c] + (uint32_t)(ks) * ROW_BYTES,              \
                                          sbw + (c * C::NW + wave) * 1024, 16, 0, 0);            \
       }                                                                                         \
     }                                                                                           \
     _Pragma("unroll") for (int c = 0; c < C::SF_LOADS; ++c) {                                   \
-      if ((part) < 0 || ((c + 2) & 3) == (part)) {                                              \
+      if ((part) < 0 || load_step(C::CODE_LOADS + c) == (part)) {                               \
         const uint8_t* b = (c < C::SF_LOADS_W) ? wsbase : p.a_sf;                               \
         __builtin_amdgcn_global_load_lds(b + soff[c] + (uint32_t)(ks) * SF_BYTES,               \
                                          sbw + C::CODE_BYTES + (c * C::NW + wave) * 256, 4, 0, 0); \
@@ -236,18 +243,28 @@ __device__ __forceinline__ void run_tile(const Params& p, uint8_t* smem, int e, 
       TS[j] = *reinterpret_cast<const uint32_t*>(sbr + (BN + wm * TM + j * 32 + l32) * SF_BYTES + hf * 4); \
   } while (0)
 
-// one 16-deep K step: decode dword (s & 3) of the half fragments with scale
-// byte (s >> 1), then FN x JV MFMAs
-#define NVFP4_STEP(s, WA, TB, WSC, TSC)                                                         \
+// decode of one 16-deep K step: dword (s & 3) of the half fragments with
+// scale byte (s >> 1); and the FN x JV MFMAs of a decoded step
+#define NVFP4_DECODE(s, WA, TB, WSC, TSC, AV, BV)                                               \
   do {                                                                                          \
-    half8v av[FN], bv[FM];                                                                      \
     _Pragma("unroll") for (int i = 0; i < FN; ++i)                                              \
-      av[i] = decode8(pick(WA[i], (s) & 3), WSC[i].get((s) >> 1));                              \
+      AV[i] = decode8(pick(WA[i], (s) & 3), WSC[i].get((s) >> 1));                              \
     _Pragma("unroll") for (int j = 0; j < JV; ++j)                                              \
-      bv[j] = decode8(pick(TB[j], (s) & 3), TSC[j].get((s) >> 1));                              \
+      BV[j] = decode8(pick(TB[j], (s) & 3), TSC[j].get((s) >> 1));                              \
+  } while (0)
+#define NVFP4_MFMAS(AV, BV)                                                                     \
+  do {                                                                                          \
     _Pragma("unroll") for (int i = 0; i < FN; ++i)                                              \
       _Pragma("unroll") for (int j = 0; j < JV; ++j)                                            \
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);   \
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(AV[i], BV[j], acc[i][j], 0, 0, 0);   \
+  } while (0)
+// interleave: one MFMA of this step, then VPM VALU of the next step's decode
+#define NVFP4_INTERLEAVE()                                                                      \
+  do {                                                                                          \
+    _Pragma("unroll") for (int q = 0; q < FN * JV; ++q) {                                       \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                        \
+      __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);                                      \
+    }                                                                                           \
   } while (0)
 
   float16v acc[FN][FM];
@@ -257,15 +274,20 @@ __device__ __forceinline__ void run_tile(const Params& p, uint8_t* smem, int e, 
     for (int j = 0; j < FM; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  // VALU of one step's decode per MFMA of a step
+  constexpr int VPM = ((FN + JV) * 8 + FN * JV - 1) / (FN * JV);
 
   // Pipeline (three LDS buffers, stage ks in buffer ks % 3):
-  //   stage ks, steps 0-3: half A fragments (already in registers); the loads
-  //     of stage ks+2 are issued, a quarter per step; half B fragments of
-  //     stage ks are read from LDS;
-  //   steps 4-5: half B;  then wait until stage ks+1 has landed (the loads
-  //     of ks+2 may stay in flight) and synchronise the block;
-  //   the half A fragments and scales of stage ks+1 are read from LDS;
-  //   steps 6-7: half B.
+  //   steps 0-3: half A fragments (in registers); half B fragments of stage
+  //     ks are read from LDS;
+  //   after step 3: wait until stage ks+1 has landed (the loads of ks+2
+  //     issued so far may stay in flight), synchronise the block, read the
+  //     half A fragments and scales of stage ks+1;
+  //   steps 4-7: half B;
+  //   the loads of stage ks+2 are spread over steps 0-6.
+  // Every step runs its MFMAs on operands decoded during the previous step
+  // while it decodes the next step's operands, so decode and MFMA overlap;
+  // step 7 decodes step 0 of the next stage.
   // Buffer (ks+2) % 3 was last read before the mid-stage barrier of ks-1.
   const int nks = (int)(K / BK);
   NVFP4_ISSUE(0, 0, -1);
@@ -280,42 +302,61 @@ __device__ __forceinline__ void run_tile(const Params& p, uint8_t* smem, int e, 
 
   uint4 fa[FN], ta[FM], fb[FN], tb[FM];
   uint32_t wsr[FN], tsr[FM];
+  Scales4 wsc[FN], tsc[FM];
+  half8v av0[FN], bv0[FM], av1[FN], bv1[FM];
   NVFP4_READ_HALF(0, 0, fa, ta);
   NVFP4_READ_SF(0, wsr, tsr);
+#pragma unroll
+  for (int i = 0; i < FN; ++i) wsc[i] = scales4(wsr[i]);
+#pragma unroll
+  for (int j = 0; j < JV; ++j) tsc[j] = scales4(tsr[j]);
+  NVFP4_DECODE(0, fa, ta, wsc, tsc, av0, bv0);
 
   int buf = 0;
   for (int ks = 0; ks < nks; ++ks) {
-    Scales4 wsc[FN], tsc[FM];
-#pragma unroll
-    for (int i = 0; i < FN; ++i) wsc[i] = scales4(wsr[i]);
-#pragma unroll
-    for (int j = 0; j < JV; ++j) tsc[j] = scales4(tsr[j]);
     NVFP4_READ_HALF(buf, 1, fb, tb);
-    const bool more2 = ks + 2 < nks;
+    const bool more2 = ks + 2 < nks, more1 = ks + 1 < nks;
     const int buf2 = buf == 0 ? 2 : buf - 1;           // (ks + 2) % 3
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      if (more2) NVFP4_ISSUE(ks + 2, buf2, s);
-      NVFP4_STEP(s, fa, ta, wsc, tsc);
-    }
-    NVFP4_STEP(4, fb, tb, wsc, tsc);
-    NVFP4_STEP(5, fb, tb, wsc, tsc);
-    if (more2) asm volatile("s_waitcnt vmcnt(15)" ::: "memory");
+    const int buf1 = buf == 2 ? 0 : buf + 1;           // (ks + 1) % 3
+    // operands of even steps live in av0/bv0, of odd steps in av1/bv1
+    if (more2) NVFP4_ISSUE(ks + 2, buf2, 0);
+    NVFP4_DECODE(1, fa, ta, wsc, tsc, av1, bv1); NVFP4_MFMAS(av0, bv0); NVFP4_INTERLEAVE();
+    if (more2) NVFP4_ISSUE(ks + 2, buf2, 1);
+    NVFP4_DECODE(2, fa, ta, wsc, tsc, av0, bv0); NVFP4_MFMAS(av1, bv1); NVFP4_INTERLEAVE();
+    if (more2) NVFP4_ISSUE(ks + 2, buf2, 2);
+    NVFP4_DECODE(3, fa, ta, wsc, tsc, av1, bv1); NVFP4_MFMAS(av0, bv0); NVFP4_INTERLEAVE();
+    if (more2) NVFP4_ISSUE(ks + 2, buf2, 3);
+    NVFP4_DECODE(4, fb, tb, wsc, tsc, av0, bv0); NVFP4_MFMAS(av1, bv1); NVFP4_INTERLEAVE();
+    // stage ks+1 must have landed; the loads of ks+2 issued so far may not have
+    if (more2) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");  // kLoadsBeforeBarrier
     else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    const int buf1 = buf == 2 ? 0 : buf + 1;           // (ks + 1) % 3
-    if (ks + 1 < nks) {
+    if (more1) {
       NVFP4_READ_HALF(buf1, 0, fa, ta);
       NVFP4_READ_SF(buf1, wsr, tsr);
     }
-    NVFP4_STEP(6, fb, tb, wsc, tsc);
-    NVFP4_STEP(7, fb, tb, wsc, tsc);
+    if (more2) NVFP4_ISSUE(ks + 2, buf2, 4);
+    NVFP4_DECODE(5, fb, tb, wsc, tsc, av1, bv1); NVFP4_MFMAS(av0, bv0); NVFP4_INTERLEAVE();
+    if (more2) NVFP4_ISSUE(ks + 2, buf2, 5);
+    NVFP4_DECODE(6, fb, tb, wsc, tsc, av0, bv0); NVFP4_MFMAS(av1, bv1); NVFP4_INTERLEAVE();
+    if (more2) NVFP4_ISSUE(ks + 2, buf2, 6);
+    NVFP4_DECODE(7, fb, tb, wsc, tsc, av1, bv1); NVFP4_MFMAS(av0, bv0); NVFP4_INTERLEAVE();
+    if (more1) {
+#pragma unroll
+      for (int i = 0; i < FN; ++i) wsc[i] = scales4(wsr[i]);
+#pragma unroll
+      for (int j = 0; j < JV; ++j) tsc[j] = scales4(tsr[j]);
+      NVFP4_DECODE(0, fa, ta, wsc, tsc, av0, bv0);
+    }
+    NVFP4_MFMAS(av1, bv1); NVFP4_INTERLEAVE();
     buf = buf1;
   }
 #undef NVFP4_ISSUE
 #undef NVFP4_READ_HALF
 #undef NVFP4_READ_SF
-#undef NVFP4_STEP
+#undef NVFP4_DECODE
+#undef NVFP4_MFMAS
+#undef NVFP4_INTERLEAVE
   __syncthreads();   // every wave is done with the stage buffers (the epilogue reuses LDS)
 
   // ---- epilogue
