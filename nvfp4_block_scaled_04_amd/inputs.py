@@ -54,7 +54,7 @@ class Workload:
 # which runs the CPU oracle on a row sample of each workload.
 WORKLOADS = {
     "tiny": Workload("tiny", 1, T=64, H=256, I=128, E=4, k=2, routing="router",
-                     special="tiny", weight_seed=0x5EED0001, gs_h=2048.0),
+                     special="tiny", weight_seed=0x5EED0001, gs_h=1024.0),
     "dense": Workload("dense", 2, dense_mkn=(4096, 7168, 2048), weight_seed=0x5EED0002),
     "decode": Workload("decode", 3, T=256, H=7168, I=2048, E=256, k=8,
                        weight_seed=0x5EED0003, gs_h=32.0),
