@@ -258,11 +258,17 @@ __device__ __forceinline__ void run_tile(const Params& p, uint8_t* smem, int e, 
       _Pragma("unroll") for (int j = 0; j < JV; ++j)                                            \
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(AV[i], BV[j], acc[i][j], 0, 0, 0);   \
   } while (0)
-// interleave: one MFMA of this step, then VPM VALU of the next step's decode
-#define NVFP4_INTERLEAVE()                                                                      \
+// interleave: one MFMA of this step, then VPM VALU of the next step's decode;
+// the step's NL stage loads go right after MFMAs spread over the step, so a
+// load that waits to issue leaves the matrix pipe busy
+#define NVFP4_INTERLEAVE(NL)                                                                    \
   do {                                                                                          \
+    constexpr int nl_ = (NL);                                                                   \
+    constexpr int every_ = nl_ > 0 ? (FN * JV + nl_ - 1) / nl_ : 1;                             \
     _Pragma("unroll") for (int q = 0; q < FN * JV; ++q) {                                       \
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                        \
+      if (nl_ > 0 && q % every_ == 0 && q / every_ < nl_)                                       \
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                                      \
       __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);                                      \
     }                                                                                           \
   } while (0)
@@ -312,45 +318,52 @@ __device__ __forceinline__ void run_tile(const Params& p, uint8_t* smem, int e, 
   for (int j = 0; j < JV; ++j) tsc[j] = scales4(tsr[j]);
   NVFP4_DECODE(0, fa, ta, wsc, tsc, av0, bv0);
 
+// One stage.  LOADS (a literal 1 or 0): whether stage ks+2 exists and is
+// loaded here; with LOADS the body has no branches, so the loads and the
+// MFMAs share one scheduling region.
+#define NVFP4_STAGE(LOADS)                                                                      \
+  do {                                                                                          \
+    NVFP4_READ_HALF(buf, 1, fb, tb);                                                            \
+    const bool more1 = (LOADS) || ks + 1 < nks;                                                 \
+    const int buf2 = buf == 0 ? 2 : buf - 1;           /* (ks + 2) % 3 */                       \
+    const int buf1 = buf == 2 ? 0 : buf + 1;           /* (ks + 1) % 3 */                       \
+    /* operands of even steps live in av0/bv0, of odd steps in av1/bv1 */                       \
+    if (LOADS) NVFP4_ISSUE(ks + 2, buf2, 0);                                                    \
+    NVFP4_DECODE(1, fa, ta, wsc, tsc, av1, bv1); NVFP4_MFMAS(av0, bv0); NVFP4_INTERLEAVE((LOADS) ? 3 : 0); \
+    if (LOADS) NVFP4_ISSUE(ks + 2, buf2, 1);                                                    \
+    NVFP4_DECODE(2, fa, ta, wsc, tsc, av0, bv0); NVFP4_MFMAS(av1, bv1); NVFP4_INTERLEAVE((LOADS) ? 2 : 0); \
+    if (LOADS) NVFP4_ISSUE(ks + 2, buf2, 2);                                                    \
+    NVFP4_DECODE(3, fa, ta, wsc, tsc, av1, bv1); NVFP4_MFMAS(av0, bv0); NVFP4_INTERLEAVE((LOADS) ? 2 : 0); \
+    if (LOADS) NVFP4_ISSUE(ks + 2, buf2, 3);                                                    \
+    NVFP4_DECODE(4, fb, tb, wsc, tsc, av0, bv0); NVFP4_MFMAS(av1, bv1); NVFP4_INTERLEAVE((LOADS) ? 2 : 0); \
+    /* stage ks+1 must have landed; the loads of ks+2 issued so far may not have */             \
+    if (LOADS) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");  /* kLoadsBeforeBarrier */     \
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");                                       \
+    __syncthreads();                                                                            \
+    if (more1) {                                                                                \
+      NVFP4_READ_HALF(buf1, 0, fa, ta);                                                         \
+      NVFP4_READ_SF(buf1, wsr, tsr);                                                            \
+    }                                                                                           \
+    if (LOADS) NVFP4_ISSUE(ks + 2, buf2, 4);                                                    \
+    NVFP4_DECODE(5, fb, tb, wsc, tsc, av1, bv1); NVFP4_MFMAS(av0, bv0); NVFP4_INTERLEAVE((LOADS) ? 2 : 0); \
+    if (LOADS) NVFP4_ISSUE(ks + 2, buf2, 5);                                                    \
+    NVFP4_DECODE(6, fb, tb, wsc, tsc, av0, bv0); NVFP4_MFMAS(av1, bv1); NVFP4_INTERLEAVE((LOADS) ? 2 : 0); \
+    if (LOADS) NVFP4_ISSUE(ks + 2, buf2, 6);                                                    \
+    NVFP4_DECODE(7, fb, tb, wsc, tsc, av1, bv1); NVFP4_MFMAS(av0, bv0); NVFP4_INTERLEAVE((LOADS) ? 2 : 0); \
+    if (more1) {                                                                                \
+      _Pragma("unroll") for (int i = 0; i < FN; ++i) wsc[i] = scales4(wsr[i]);                  \
+      _Pragma("unroll") for (int j = 0; j < JV; ++j) tsc[j] = scales4(tsr[j]);                  \
+      NVFP4_DECODE(0, fa, ta, wsc, tsc, av0, bv0);                                              \
+    }                                                                                           \
+    NVFP4_MFMAS(av1, bv1); NVFP4_INTERLEAVE(0);                                                 \
+    buf = buf1;                                                                                 \
+  } while (0)
+
   int buf = 0;
-  for (int ks = 0; ks < nks; ++ks) {
-    NVFP4_READ_HALF(buf, 1, fb, tb);
-    const bool more2 = ks + 2 < nks, more1 = ks + 1 < nks;
-    const int buf2 = buf == 0 ? 2 : buf - 1;           // (ks + 2) % 3
-    const int buf1 = buf == 2 ? 0 : buf + 1;           // (ks + 1) % 3
-    // operands of even steps live in av0/bv0, of odd steps in av1/bv1
-    if (more2) NVFP4_ISSUE(ks + 2, buf2, 0);
-    NVFP4_DECODE(1, fa, ta, wsc, tsc, av1, bv1); NVFP4_MFMAS(av0, bv0); NVFP4_INTERLEAVE();
-    if (more2) NVFP4_ISSUE(ks + 2, buf2, 1);
-    NVFP4_DECODE(2, fa, ta, wsc, tsc, av0, bv0); NVFP4_MFMAS(av1, bv1); NVFP4_INTERLEAVE();
-    if (more2) NVFP4_ISSUE(ks + 2, buf2, 2);
-    NVFP4_DECODE(3, fa, ta, wsc, tsc, av1, bv1); NVFP4_MFMAS(av0, bv0); NVFP4_INTERLEAVE();
-    if (more2) NVFP4_ISSUE(ks + 2, buf2, 3);
-    NVFP4_DECODE(4, fb, tb, wsc, tsc, av0, bv0); NVFP4_MFMAS(av1, bv1); NVFP4_INTERLEAVE();
-    // stage ks+1 must have landed; the loads of ks+2 issued so far may not have
-    if (more2) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");  // kLoadsBeforeBarrier
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (more1) {
-      NVFP4_READ_HALF(buf1, 0, fa, ta);
-      NVFP4_READ_SF(buf1, wsr, tsr);
-    }
-    if (more2) NVFP4_ISSUE(ks + 2, buf2, 4);
-    NVFP4_DECODE(5, fb, tb, wsc, tsc, av1, bv1); NVFP4_MFMAS(av0, bv0); NVFP4_INTERLEAVE();
-    if (more2) NVFP4_ISSUE(ks + 2, buf2, 5);
-    NVFP4_DECODE(6, fb, tb, wsc, tsc, av0, bv0); NVFP4_MFMAS(av1, bv1); NVFP4_INTERLEAVE();
-    if (more2) NVFP4_ISSUE(ks + 2, buf2, 6);
-    NVFP4_DECODE(7, fb, tb, wsc, tsc, av1, bv1); NVFP4_MFMAS(av0, bv0); NVFP4_INTERLEAVE();
-    if (more1) {
-#pragma unroll
-      for (int i = 0; i < FN; ++i) wsc[i] = scales4(wsr[i]);
-#pragma unroll
-      for (int j = 0; j < JV; ++j) tsc[j] = scales4(tsr[j]);
-      NVFP4_DECODE(0, fa, ta, wsc, tsc, av0, bv0);
-    }
-    NVFP4_MFMAS(av1, bv1); NVFP4_INTERLEAVE();
-    buf = buf1;
-  }
+  int ks = 0;
+  for (; ks + 2 < nks; ++ks) NVFP4_STAGE(1);
+  for (; ks < nks; ++ks) NVFP4_STAGE(0);
+#undef NVFP4_STAGE
 #undef NVFP4_ISSUE
 #undef NVFP4_READ_HALF
 #undef NVFP4_READ_SF
