@@ -54,7 +54,8 @@ int nvfp4_version(void);
  * Weight layout (untimed preparation).
  * README "What We Have", bridge layer: gate/up interleave of the L1 weight
  * at granularity 8 and conversion of B to K-major; "Fused SwiGLU — How It
- * Works": interleaved output columns read [gate0-7, up0-7, gate8-15, ...].
+ * Works": the interleaved output alternates eight gate columns with the eight
+ * matching up columns.
  *
  * For each of `groups` matrices src[g] (rows x cols, BF16, row-major),
  * writes dst[g] = transpose (cols x rows).  With interleave_gate_up != 0 the

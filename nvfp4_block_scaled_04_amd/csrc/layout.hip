@@ -3,8 +3,9 @@
 //
 // README "NVFP4 MegaMoE Kernel", "What We Have" (bridge layer): the L1 weight
 // is interleaved gate/up at granularity 8 along N and B is made K-major;
-// "Fused SwiGLU — How It Works": interleaved columns read
-// [gate0-7, up0-7, gate8-15, up8-15, ...]; "The //2 Bug": granularity 8.
+// "Fused SwiGLU — How It Works": the interleaved output alternates eight gate
+// columns with the eight matching up columns; "The //2 Bug": the granularity
+// is 8, not 4.
 //
 // dst[g][n][r] = src[g][r][col(n)], col(n) = n without interleave, else
 //   8*(n/16) + n%8 (gate, n%16 < 8) or I + 8*(n/16) + n%8 - 8 (up), I = cols/2.

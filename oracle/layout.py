@@ -2,8 +2,8 @@
 
 README ("NVFP4 MegaMoE Kernel"):
   * "Fused SwiGLU — How It Works", "The Solution": the L1 weight's gate and up
-    columns are interleaved at granularity 8 along N, so the GEMM output reads
-    [gate 0-7, up 0-7, gate 8-15, up 8-15, ...];
+    columns are interleaved at granularity 8 along N, so the GEMM output holds
+    eight gate columns, then the eight matching up columns, and so on;
   * same section, "The //2 Bug": the granularity is 8 (a leftover //2 once
     gave 4), because the interleave runs along N, not along the packed K axis;
   * "What We Have" (bridge layer): weights are quantised along K and the B

@@ -9,7 +9,8 @@ Follows the README ("NVFP4 MegaMoE Kernel"):
     FP8 scale 0 (no clamp to a tiny positive value);
   * same table, bug 4: an underflow block (amax < 6 * 2**-9) is zeroed
     instead of dividing by a tiny scale;
-  * same table, bug 2: dequantise -> requantise is byte-identical;
+  * same table, bug 2: requantising the dequantised values reproduces every
+    byte;
   * CURRENT_BUG.md, "What Works": the activation global scale is recomputed
     on every call.
 

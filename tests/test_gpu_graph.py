@@ -1,8 +1,8 @@
 """The forward is graph-capturable and deterministic.
 
-README "NVFP4 MegaMoE Kernel", "What We Have" (grouped GEMM): CUDAGraph-safe,
-workspace pre-allocated, no runtime allocations; "File Structure" lists a
-CUDAGraph test.  Here: capture moe_expert_forward in a hipGraph (through
+README "NVFP4 MegaMoE Kernel", "What We Have" (grouped GEMM): the kernel is
+safe under graph capture because its workspace is allocated up front and it
+allocates nothing at run time; "File Structure" lists a graph-capture test.  Here: capture moe_expert_forward in a hipGraph (through
 torch.cuda.graph), replay it several times with eager work and
 synchronisation in between, and require every replay to equal the eager
 result bit for bit; and two eager runs must be bitwise identical."""

@@ -197,8 +197,8 @@ def test_fp32_sequence_matches_exact_rational_away_from_ties():
 
 
 def test_dequant_requant_byte_identical():
-    # README "Correctness Bugs Fixed", bug 2: dequantise -> requantise is
-    # byte-identical.  Weight-like data; requantise from the BF16 rounding of
+    # README "Correctness Bugs Fixed", bug 2: requantising the dequantised
+    # values gives back every byte.  Weight-like data; requantise from the BF16 rounding of
     # the dequantised values with a freshly computed global scale.
     x = _randn_bf16((2 * 128, 512), 9, std=0.02)
     q, sf, gs = Q.quantize_nvfp4(x, groups=2)

@@ -63,7 +63,7 @@ def test_route_zero_tokens():
 
 
 def test_interleave_pattern():
-    # README "Fused SwiGLU": output columns read [gate0-7, up0-7, gate8-15, ...]
+    # README "Fused SwiGLU": eight gate columns, then their eight up columns, ...
     src = L.interleave_src(64)
     half = 32
     assert src[:8].tolist() == list(range(8))
