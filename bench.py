@@ -35,9 +35,22 @@ from nvfp4_block_scaled_04_amd import inputs as I  # noqa: E402
 
 FP16_MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense FP16 MFMA
 HBM_PEAK_GBS = 8000.0
-# traffic scale: rocprofv3 FETCH_SIZE/WRITE_SIZE of the same command, divided by
-# what they read for a plain copy of known size (see profiles/)
+# HBM traffic of the L1 grouped GEMM per launch (bytes), from two rocprofv3
+# --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch),
+# each scaled by the ratio of known bytes to the counter's reading for a plain
+# 1 GiB device copy (--copy-calibration).  Reported only while the GEMM
+# sources hash to the value the counters were taken with; otherwise null.
 TRAFFIC = {}
+TRAFFIC_SRC_SHA = None
+
+
+def gemm_src_sha():
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "device.hpp"):
+        with open(os.path.join(ROOT, "nvfp4_block_scaled_04_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def log(msg):
@@ -57,7 +70,7 @@ def build_weights(w, dev, chunk=32):
         w1s.append(torch.stack([p[0] for p in pairs]))
         w2s.append(torch.stack([p[1] for p in pairs]))
         del pairs
-    ew = nv.prepare_expert_weights(w1s, w2s, dev)
+    ew = nv.prepare_expert_weights(w1s, w2s, dev, keep_rowmajor=False)
     del w1s, w2s
     torch.cuda.empty_cache()
     return ew
@@ -125,10 +138,10 @@ def bench_moe(w, steps, warmup, dev):
     h_sf = torch.empty((M, Iw // 16), dtype=torch.uint8, device=dev)
     y = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
     qbuf = (a_q, a_sf, gs_a)
-    l1 = lambda: nv.grouped_gemm(nv.EPI_SWIGLU_NVFP4, a_q, a_sf, gs_a, off, ew.w1_q, ew.w1_sf,
+    l1 = lambda: nv.grouped_gemm(nv.EPI_SWIGLU_NVFP4, a_q, a_sf, gs_a, off, ew.w1,
                                  ew.gs_w1, M, a_row_src=perm, a_row_div=k, gs_out=gs_h,
                                  out=(h_q, h_sf, None))
-    l2 = lambda: nv.grouped_gemm(nv.EPI_BF16, h_q, h_sf, gs_h, off, ew.w2_q, ew.w2_sf, ew.gs_w2,
+    l2 = lambda: nv.grouped_gemm(nv.EPI_BF16, h_q, h_sf, gs_h, off, ew.w2, ew.gs_w2,
                                  M, out=y)
     stages = {
         "quantize": lambda: nv.quantize(x, out=qbuf),
@@ -150,7 +163,7 @@ def bench_moe(w, steps, warmup, dev):
     roof = {"kernel": "grouped_gemm_kernel<SwiGLU+NVFP4 epilogue> (L1)", "bound": "mfma",
             "achieved": round(achieved, 2), "peak": FP16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(achieved / FP16_MFMA_PEAK_TFLOPS, 4),
-            "traffic": TRAFFIC.get((w.name, "l1"))}
+            "traffic": (TRAFFIC.get((w.name, "l1")) if TRAFFIC_SRC_SHA == gemm_src_sha() else None)}
     extra = {
         "tokens_per_s": T / (ms_step * 1e-3),
         "l2_gemm_tflops": l2_flops / (st_ms["l2_gemm"] * 1e-3) / 1e12,
@@ -219,7 +232,17 @@ def main():
     ap.add_argument("--workload", default="prefill", choices=["tiny", "decode", "prefill", "skewed"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only copy 1 GiB device-to-device 3 times (counter calibration)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": src.numel() * 4, "copies": 3}))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the expert-parallel "
               "sharding over several GPUs is a design note, not built.", file=sys.stderr)

@@ -98,6 +98,27 @@ nvfp4_status nvfp4_quantize(const void* x_bf16, int64_t groups, int64_t rows_per
                             float* gs_out, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Weight packing for the grouped GEMM (untimed preparation).
+ * README "What We Have", bridge layer: scale assembly and layout conversion
+ * of the B operand for the block-scaled MMA.  Here the B operand is re-blocked
+ * so that each (n tile, K stage) of the GEMM is one contiguous block.
+ *
+ * Input: row-major NVFP4 weights q uint8 [E][N][K/2], sf uint8 [E][N][K/16]
+ * (K-major, as written by nvfp4_quantize).
+ * Output, with Np = N rounded up to NVFP4_PACK_ROWS and S = K / NVFP4_PACK_K:
+ *   q_packed  uint8 [E][Np/NVFP4_PACK_ROWS][S][NVFP4_PACK_ROWS][NVFP4_PACK_K/2]
+ *   sf_packed uint8 [E][Np/NVFP4_PACK_ROWS][S][NVFP4_PACK_ROWS][NVFP4_PACK_K/16]
+ * i.e. byte c of stage s of row n goes to tile n / ROWS, stage s, row n % ROWS;
+ * rows N..Np-1 are zero.  Sizes from nvfp4_packed_weight_bytes().
+ * Shapes: E >= 1, N >= 1, K % NVFP4_PACK_K == 0.  In and out must not overlap.
+ * ---------------------------------------------------------------------- */
+#define NVFP4_PACK_ROWS 512
+#define NVFP4_PACK_K 128
+size_t nvfp4_packed_weight_bytes(int64_t E, int64_t N, int64_t K, size_t* sf_bytes);
+nvfp4_status nvfp4_pack_weights(const uint8_t* q, const uint8_t* sf, int64_t E, int64_t N,
+                                int64_t K, uint8_t* q_packed, uint8_t* sf_packed, void* stream);
+
+/* ------------------------------------------------------------------------
  * Expert offsets and expert-order permutation.
  * README "Correctness Bugs Fixed", bug 5: a histogram, not an O(n x E) mask;
  * README "Key Lessons" 4: quantise compact rows, then place them.
@@ -133,8 +154,8 @@ nvfp4_status nvfp4_moe_route(const int32_t* topk_ids, int64_t T, int k, int E,
  *   acc[d][n] = sum_k dec(A)[d][k] * dec(B[e])[n][k] / (gs_a[0] * gs_b[e]),
  *   dec = E2M1 * E4M3 (exact), fp32 accumulation.
  * A: a_q uint8 [rows_a][K/2], a_sf uint8 [rows_a][K/16], gs_a float[1].
- * B: b_q uint8 [E][N][K/2], b_sf uint8 [E][N][K/16], gs_b float[E]
- *    (K-major, i.e. the weight's N rows each hold K elements).
+ * B: b_q, b_sf packed by nvfp4_pack_weights from K-major NVFP4 weights
+ *    [E][N][K/2] codes and [E][N][K/16] scales; gs_b float[E].
  * epilogue NVFP4_EPI_BF16: c_bf16 [M][N] = bf16_rne(acc).
  * epilogue NVFP4_EPI_SWIGLU_NVFP4: N = 2I interleaved at 8 (see
  *   nvfp4_weight_layout); h[d][c] = silu(gate) * up in fp32 with
@@ -179,8 +200,10 @@ nvfp4_status nvfp4_moe_combine(const void* y_bf16, const int32_t* inv_perm,
  * are one fused kernel.
  *
  * x BF16 [T][H]; topk_ids int32 [T][k]; topk_w float [T][k];
- * w1_q [E][2I][H/2], w1_sf [E][2I][H/16], gs_w1 [E]  (interleaved, K-major);
- * w2_q [E][H][I/2],  w2_sf [E][H][I/16],  gs_w2 [E]  (K-major);
+ * w1_q, w1_sf: nvfp4_pack_weights of the interleaved, K-major L1 weight
+ *   ([E][2I][H/2] codes, [E][2I][H/16] scales); gs_w1 [E];
+ * w2_q, w2_sf: nvfp4_pack_weights of the K-major L2 weight ([E][H][I/2],
+ *   [E][H][I/16]); gs_w2 [E];
  * gs_h float[1]: global scale of the requantised L2 input (pre-computed);
  * out BF16 [T][H].
  * Steps on `stream`: nvfp4_quantize(x, per-call gs) -> nvfp4_moe_route ->

@@ -7,9 +7,9 @@ seeded synthetic workloads.
 """
 
 from .binding import (  # noqa: F401
-    EPI_BF16, EPI_SWIGLU_NVFP4, ExpertWeights, Nvfp4Error, Taps, forward_workspace, grouped_gemm,
-    lib, moe_combine, moe_expert_forward, moe_route, prepare_expert_weights, quantize,
-    weight_layout,
+    EPI_BF16, EPI_SWIGLU_NVFP4, ExpertWeights, Nvfp4Error, PackedWeight, Taps, forward_workspace,
+    grouped_gemm, lib, moe_combine, moe_expert_forward, moe_route, pack_weights,
+    prepare_expert_weights, quantize, weight_layout,
 )
 
 __version__ = "0.1.0"

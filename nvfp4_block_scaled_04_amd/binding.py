@@ -30,6 +30,9 @@ SIGNATURES = {
     "nvfp4_last_error": (ctypes.c_char_p, []),
     "nvfp4_version": (c_int, []),
     "nvfp4_weight_layout": (c_int, [c_void_p, c_int64, c_int64, c_int64, c_int, c_void_p, c_void_p]),
+    "nvfp4_packed_weight_bytes": (c_size_t, [c_int64, c_int64, c_int64, ctypes.POINTER(c_size_t)]),
+    "nvfp4_pack_weights": (c_int, [c_void_p, c_void_p, c_int64, c_int64, c_int64, c_void_p, c_void_p,
+                                   c_void_p]),
     "nvfp4_quantize_workspace_size": (c_size_t, [c_int64, c_int64, c_int64]),
     "nvfp4_quantize": (c_int, [c_void_p, c_int64, c_int64, c_int64, c_void_p, c_void_p, c_void_p,
                                c_void_p, c_void_p, c_size_t, c_void_p]),
@@ -123,6 +126,30 @@ def weight_layout(w, interleave_gate_up):
     return out
 
 
+class PackedWeight:
+    """NVFP4 weights of E experts, N rows of K elements, in the GEMM's packed
+    layout (nvfp4_pack_weights): flat uint8 codes `q` and scales `sf`."""
+
+    def __init__(self, q, sf, E, N, K):
+        self.q, self.sf, self.E, self.N, self.K = q, sf, E, N, K
+
+
+def pack_weights(q, sf):
+    """Row-major NVFP4 weights q (E, N, K/2), sf (E, N, K/16) -> PackedWeight."""
+    _dev(q, torch.uint8, "q")
+    E, N, Kh = q.shape
+    K = Kh * 2
+    _dev(sf, torch.uint8, "sf", (E, N, K // 16))
+    L = lib()
+    sfb = c_size_t(0)
+    qb = L.nvfp4_packed_weight_bytes(E, N, K, ctypes.byref(sfb))
+    qp = torch.empty(max(qb, 1), dtype=torch.uint8, device=q.device)
+    sfp = torch.empty(max(sfb.value, 1), dtype=torch.uint8, device=q.device)
+    _check(L.nvfp4_pack_weights(_ptr(q), _ptr(sf), E, N, K, _ptr(qp), _ptr(sfp), _stream(q.device)),
+           "nvfp4_pack_weights")
+    return PackedWeight(qp, sfp, E, N, K)
+
+
 def quantize(x, groups=1, gs_in=None, out=None):
     """x (R, C) bf16 -> (q (R, C/2) u8, sf (R, C/16) u8, gs (groups,) f32)."""
     _dev(x, torch.bfloat16, "x")
@@ -163,16 +190,17 @@ def moe_route(topk_ids, E):
     return off, perm, inv, bad
 
 
-def grouped_gemm(epilogue, a_q, a_sf, gs_a, offsets, b_q, b_sf, gs_b, M, a_row_src=None,
+def grouped_gemm(epilogue, a_q, a_sf, gs_a, offsets, b: PackedWeight, gs_b, M, a_row_src=None,
                  a_row_div=1, gs_out=None, debug=False, out=None):
-    """Expert-grouped NVFP4 GEMM.  BF16 epilogue returns c (M, N) bf16; the
-    SwiGLU epilogue returns (c_q (M, N/4), c_sf (M, N/32), h f32 (M, N/2) or None)."""
-    E, N, Kh = b_q.shape
-    K = Kh * 2
-    dev = b_q.device
+    """Expert-grouped NVFP4 GEMM with packed B.  BF16 epilogue returns c (M, N)
+    bf16; the SwiGLU epilogue returns (c_q (M, N/4), c_sf (M, N/32), h f32
+    (M, N/2) or None)."""
+    E, N, K = b.E, b.N, b.K
+    dev = b.q.device
     _dev(a_q, torch.uint8, "a_q")
     _dev(a_sf, torch.uint8, "a_sf")
-    _dev(b_sf, torch.uint8, "b_sf", (E, N, K // 16))
+    _dev(b.q, torch.uint8, "b.q")
+    _dev(b.sf, torch.uint8, "b.sf")
     _dev(gs_a, torch.float32, "gs_a")
     _dev(gs_b, torch.float32, "gs_b", (E,))
     _dev(offsets, torch.int32, "offsets", (E + 1,))
@@ -192,7 +220,7 @@ def grouped_gemm(epilogue, a_q, a_sf, gs_a, offsets, b_q, b_sf, gs_b, M, a_row_s
             dbg = torch.empty((M, I), dtype=torch.float32, device=dev) if debug else None
         _dev(gs_out, torch.float32, "gs_out")
     _check(lib().nvfp4_grouped_gemm(epilogue, _ptr(a_q), _ptr(a_sf), _ptr(gs_a), _ptr(a_row_src),
-                                    a_row_div, _ptr(offsets), E, M, N, K, _ptr(b_q), _ptr(b_sf),
+                                    a_row_div, _ptr(offsets), E, M, N, K, _ptr(b.q), _ptr(b.sf),
                                     _ptr(gs_b), _ptr(gs_out), _ptr(c), _ptr(c_q), _ptr(c_sf),
                                     _ptr(dbg), None, 0, _stream(dev)), "nvfp4_grouped_gemm")
     return c if epilogue == EPI_BF16 else (c_q, c_sf, dbg)
@@ -214,23 +242,25 @@ def moe_combine(y, inv_perm, topk_w, offsets, out=None):
 
 
 class ExpertWeights:
-    """NVFP4 expert weights as the forward reads them (device tensors)."""
+    """NVFP4 expert weights as the forward reads them: packed L1 (`w1`, rows
+    interleaved gate/up) and L2 (`w2`) weights with per-expert global scales;
+    optionally the row-major NVFP4 arrays they were packed from."""
 
-    def __init__(self, w1_q, w1_sf, gs_w1, w2_q, w2_sf, gs_w2):
-        self.w1_q, self.w1_sf, self.gs_w1 = w1_q, w1_sf, gs_w1
-        self.w2_q, self.w2_sf, self.gs_w2 = w2_q, w2_sf, gs_w2
+    def __init__(self, w1: PackedWeight, gs_w1, w2: PackedWeight, gs_w2, rowmajor=None):
+        self.w1, self.gs_w1, self.w2, self.gs_w2 = w1, gs_w1, w2, gs_w2
+        self.rowmajor = rowmajor or {}
 
     @property
     def E(self):
-        return self.w1_q.shape[0]
+        return self.w1.E
 
     @property
     def I(self):
-        return self.w1_q.shape[1] // 2
+        return self.w1.N // 2
 
     @property
     def H(self):
-        return self.w1_q.shape[2] * 2
+        return self.w1.K
 
 
 def forward_workspace(T, H, I, E, k, device):
@@ -248,11 +278,9 @@ def moe_expert_forward(x, topk_ids, topk_w, w: ExpertWeights, gs_h, out=None, ta
     dev = x.device
     _dev(topk_ids, torch.int32, "topk_ids", (T, k))
     _dev(topk_w, torch.float32, "topk_w", (T, k))
-    _dev(w.w1_q, torch.uint8, "w1_q", (E, 2 * I, H // 2))
-    _dev(w.w1_sf, torch.uint8, "w1_sf", (E, 2 * I, H // 16))
+    if w.H != H or w.w2.N != H or w.w2.K != I or w.w2.E != E:
+        raise ValueError("weight shapes do not match x")
     _dev(w.gs_w1, torch.float32, "gs_w1", (E,))
-    _dev(w.w2_q, torch.uint8, "w2_q", (E, H, I // 2))
-    _dev(w.w2_sf, torch.uint8, "w2_sf", (E, H, I // 16))
     _dev(w.gs_w2, torch.float32, "gs_w2", (E,))
     _dev(gs_h, torch.float32, "gs_h", (1,))
     o = out if out is not None else torch.empty((T, H), dtype=torch.bfloat16, device=dev)
@@ -262,20 +290,22 @@ def moe_expert_forward(x, topk_ids, topk_w, w: ExpertWeights, gs_h, out=None, ta
     tp = None
     if taps:
         tp = Taps(**{name: t.data_ptr() for name, t in taps.items()})
-    _check(L.moe_expert_forward(_ptr(x), T, H, I, E, k, _ptr(topk_ids), _ptr(topk_w), _ptr(w.w1_q),
-                                _ptr(w.w1_sf), _ptr(w.gs_w1), _ptr(w.w2_q), _ptr(w.w2_sf),
+    _check(L.moe_expert_forward(_ptr(x), T, H, I, E, k, _ptr(topk_ids), _ptr(topk_w), _ptr(w.w1.q),
+                                _ptr(w.w1.sf), _ptr(w.gs_w1), _ptr(w.w2.q), _ptr(w.w2.sf),
                                 _ptr(w.gs_w2), _ptr(gs_h), _ptr(o),
                                 ctypes.byref(tp) if tp is not None else None, _ptr(ws), ws.numel(),
                                 _stream(dev)), "moe_expert_forward")
     return o
 
 
-def prepare_expert_weights(w1_list, w2_list, device):
+def prepare_expert_weights(w1_list, w2_list, device, keep_rowmajor=True):
     """Logical bf16 weights -> ExpertWeights on the device.
 
     w1_list: iterable of chunks (Ec, H, 2I) bf16 ([gate | up]); w2_list of
     (Ec, I, H).  Each chunk goes through nvfp4_weight_layout (interleave +
-    K-major) and nvfp4_quantize (one global scale per expert)."""
+    K-major) and nvfp4_quantize (one global scale per expert); the stacked
+    result is packed with nvfp4_pack_weights.  keep_rowmajor keeps the
+    row-major NVFP4 arrays (for bit-exact checks) in `.rowmajor`."""
     w1q, w1s, g1, w2q, w2s, g2 = [], [], [], [], [], []
     for w1c, w2c in zip(w1_list, w2_list):
         Ec = w1c.shape[0]
@@ -288,4 +318,7 @@ def prepare_expert_weights(w1_list, w2_list, device):
         w2q.append(q.view(Ec, l2.shape[1], -1)); w2s.append(s.view(Ec, l2.shape[1], -1)); g2.append(g)
         del l2
     cat = lambda xs: xs[0] if len(xs) == 1 else torch.cat(xs)
-    return ExpertWeights(cat(w1q), cat(w1s), cat(g1), cat(w2q), cat(w2s), cat(g2))
+    w1q, w1s, w2q, w2s = cat(w1q), cat(w1s), cat(w2q), cat(w2s)
+    p1, p2 = pack_weights(w1q, w1s), pack_weights(w2q, w2s)
+    rm = dict(w1_q=w1q, w1_sf=w1s, w2_q=w2q, w2_sf=w2s) if keep_rowmajor else None
+    return ExpertWeights(p1, cat(g1), p2, cat(g2), rm)

@@ -185,6 +185,32 @@ nvfp4_status nvfp4_weight_layout(const void* src, int64_t groups, int64_t rows, 
                 "nvfp4_weight_layout launch");
 }
 
+size_t nvfp4_packed_weight_bytes(int64_t E, int64_t N, int64_t K, size_t* sf_bytes) {
+  if (E < 1 || N < 1 || K < NVFP4_PACK_K || K % NVFP4_PACK_K) {
+    if (sf_bytes) *sf_bytes = 0;
+    return 0;
+  }
+  const int64_t Np = nvfp4::packed_rows(N);
+  if (sf_bytes) *sf_bytes = (size_t)(E * Np * (K / 16));
+  return (size_t)(E * Np * (K / 2));
+}
+
+nvfp4_status nvfp4_pack_weights(const uint8_t* q, const uint8_t* sf, int64_t E, int64_t N,
+                                int64_t K, uint8_t* q_packed, uint8_t* sf_packed, void* stream) {
+  if (E < 1 || E > 65535 || N < 1) return fail(NVFP4_ERR_SHAPE, "E must be in [1, 65535] and N >= 1");
+  if (K < NVFP4_PACK_K || K % NVFP4_PACK_K)
+    return fail(NVFP4_ERR_SHAPE, "K must be a positive multiple of %d (got %lld)", NVFP4_PACK_K, (long long)K);
+  if (!q || !sf || !q_packed || !sf_packed) return fail(NVFP4_ERR_INVALID_ARG, "all pointers must be non-NULL");
+  if (!aligned(q, 16) || !aligned(q_packed, 16) || !aligned(sf, 8) || !aligned(sf_packed, 8))
+    return fail(NVFP4_ERR_INVALID_ARG, "codes must be 16-byte and scales 8-byte aligned");
+  if (q == q_packed || sf == sf_packed) return fail(NVFP4_ERR_INVALID_ARG, "in and out must not overlap");
+  nvfp4_status st = check_arch();
+  if (st != NVFP4_OK) return st;
+  return finish(nvfp4::launch_pack_weights(q, sf, E, N, K, q_packed, sf_packed,
+                                           static_cast<hipStream_t>(stream)),
+                "nvfp4_pack_weights launch");
+}
+
 size_t nvfp4_quantize_workspace_size(int64_t groups, int64_t rows_per_group, int64_t cols) {
   if (groups <= 0 || rows_per_group <= 0 || cols <= 0) return 0;
   return sizeof(float) * (size_t)groups * (size_t)nvfp4::quantize_parts(groups, rows_per_group, cols);

@@ -134,24 +134,27 @@ struct Cfg {
   static constexpr int STAGE_BYTES = CODE_BYTES + ROWS * SF_BYTES;
   static constexpr int NBUF = 3;                       // LDS stage buffers
   static constexpr int LDS_BYTES = NBUF * STAGE_BYTES;
-  // direct-to-LDS loads: a code load fills 16 rows, a scale load 32 rows
-  static constexpr int CODE_LOADS = ROWS / 16 / NW;    // per wave per stage
+  // direct-to-LDS loads per wave and stage: a code load fills 16 rows; a
+  // weight scale load (16 bytes per lane) 128 rows, a token scale load 32 rows
+  static constexpr int CODE_LOADS = ROWS / 16 / NW;
   static constexpr int CODE_LOADS_W = BN / 16 / NW;    // ... of which weight rows
-  static constexpr int SF_LOADS = ROWS / 32 / NW;
-  static constexpr int SF_LOADS_W = BN / 32 / NW;
+  static constexpr int SF_LOADS_W = BN / 128 / NW;
+  static constexpr int SF_LOADS_T = BM / 32 / NW;
+  static constexpr int SF_LOADS = SF_LOADS_W + SF_LOADS_T;
+  static constexpr int LOADS = CODE_LOADS + SF_LOADS;
   static_assert(TN % 32 == 0 && TM % 32 == 0, "wave tile must be a multiple of 32");
   static_assert(ROWS % (16 * NW) == 0 && BN % (16 * NW) == 0, "code loads must divide evenly");
-  static_assert(ROWS % (32 * NW) == 0 && BN % (32 * NW) == 0, "scale loads must divide evenly");
+  static_assert(BN % (128 * NW) == 0 && BM % (32 * NW) == 0, "scale loads must divide evenly");
+  static_assert(BN == NVFP4_PACK_ROWS && BK == NVFP4_PACK_K, "tiles follow the packed weight layout");
   static_assert(WM == 1, "column-block skipping assumes one wave row");
 };
 
 __device__ __forceinline__ int chunk_pos(int row, int q) { return q ^ ((row >> 2) & 3); }
 
-// step (0..6) of the K loop that issues stage load L (0..14): 3, then 2 per step
-__host__ __device__ constexpr int load_step(int L) { return L < 3 ? 0 : (L - 1) / 2; }
+// step (0..5) of the K loop that issues stage load L (0..11): two per step
+__host__ __device__ constexpr int load_step(int L) { return L / 2; }
 // loads issued in steps 0..3, still in flight at the mid-stage wait
-constexpr int kLoadsBeforeBarrier = 9;
-static_assert(load_step(8) == 3 && load_step(9) == 4 && load_step(14) == 6, "load schedule");
+constexpr int kLoadsBeforeBarrier = 8;
 
 // One tile: the K loop and the epilogue.  JV = number of 32-token column
 // blocks that hold rows (1..FM); the rest are skipped.
@@ -166,18 +169,18 @@ __device__ __forceinline__ void run_tile(const Params& p, uint8_t* smem, int e, 
   const int hf = lane >> 5, l32 = lane & 31;
   const int64_t N = p.N, K = p.K;
   const uint32_t kb = (uint32_t)(K / 2), ksf = (uint32_t)(K / 16);
-  const uint8_t* wbase = p.b_q + (int64_t)e * N * kb;
-  const uint8_t* wsbase = p.b_sf + (int64_t)e * N * ksf;
+  // packed weights: tile (e, n0 / BN) is S stages of BN rows (64 code bytes
+  // and 8 scale bytes per row), rows zero-padded to a multiple of BN
+  const int64_t Np = (N + BN - 1) / BN * BN;
+  const uint8_t* wbase = p.b_q + ((int64_t)e * Np + n0) * kb;
+  const uint8_t* wsbase = p.b_sf + ((int64_t)e * Np + n0) * ksf;
 
-  // global source row of LDS row r (weights: clamped to N-1, SwiGLU order;
-  // tokens: clamped to the tile's last row, gathered through a_row_src)
-  auto src_row = [&](int r) -> uint32_t {
-    if (r < BN) {
-      const int q = (EPI == NVFP4_EPI_SWIGLU_NVFP4) ? ((r & ~31) | swiglu_phys_row(r & 31)) : r;
-      const int64_t n = n0 + q;
-      return (uint32_t)(n < N ? n : N - 1);
-    }
-    const int i = r - BN;
+  // physical weight row (within the tile) held by LDS row r
+  auto wrow = [&](int r) -> int {
+    return (EPI == NVFP4_EPI_SWIGLU_NVFP4) ? ((r & ~31) | swiglu_phys_row(r & 31)) : r;
+  };
+  // token row of LDS row BN + i: clamped to the tile's last row, gathered
+  auto trow = [&](int i) -> uint32_t {
     const int d = row0 + (i < nrows ? i : nrows - 1);
     return (uint32_t)(p.a_row_src ? p.a_row_src[d] / p.a_row_div : d);
   };
@@ -188,33 +191,42 @@ __device__ __forceinline__ void run_tile(const Params& p, uint8_t* smem, int e, 
     const int g = c * C::NW + wave;                // 16-row group
     const int r = 16 * g + (lane >> 2);
     const int q = chunk_pos(r, lane & 3);          // logical chunk stored at this lane's position
-    coff[c] = src_row(r) * kb + 16 * q;
+    coff[c] = (c < C::CODE_LOADS_W) ? (uint32_t)(wrow(r) * ROW_BYTES + 16 * q)
+                                    : trow(r - BN) * kb + 16 * q;
   }
 #pragma unroll
-  for (int c = 0; c < C::SF_LOADS; ++c) {
-    const int g = c * C::NW + wave;                // 32-row group
-    const int r = 32 * g + (lane >> 1);
-    soff[c] = src_row(r) * ksf + 4 * (lane & 1);
+  for (int c = 0; c < C::SF_LOADS_W; ++c) {      // 2 consecutive rows per lane
+    const int r = 128 * (c * C::NW + wave) + 2 * lane;
+    soff[c] = (uint32_t)(wrow(r) * SF_BYTES);      // wrow(r + 1) == wrow(r) + 1 (r even)
+  }
+#pragma unroll
+  for (int c = 0; c < C::SF_LOADS_T; ++c) {      // one 4-byte half row per lane
+    const int i = 32 * (c * C::NW + wave) + (lane >> 1);
+    soff[C::SF_LOADS_W + c] = trow(i) * ksf + 4 * (lane & 1);
   }
 
-// loads of stage `ks` into LDS buffer `buf`.  Load L (codes 0..CODE_LOADS-1,
-// then scales) is issued in step load_step(L) of the loop (part = step), or
-// all at once (part = -1).
 #define NVFP4_ISSUE(ks, buf, part)                                                              \
   do {                                                                                          \
     uint8_t* sbw = smem + (buf) * C::STAGE_BYTES;                                               \
     _Pragma("unroll") for (int c = 0; c < C::CODE_LOADS; ++c) {                                 \
       if ((part) < 0 || load_step(c) == (part)) {                                               \
-        const uint8_t* b = (c < C::CODE_LOADS_W) ? wbase : p.a_q;                               \
-        __builtin_amdgcn_global_load_lds(b + coff[c] + (uint32_t)(ks) * ROW_BYTES,              \
-                                         sbw + (c * C::NW + wave) * 1024, 16, 0, 0);            \
+        if (c < C::CODE_LOADS_W)                                                                \
+          __builtin_amdgcn_global_load_lds(wbase + coff[c] + (uint32_t)(ks) * (BN * ROW_BYTES), \
+                                           sbw + (c * C::NW + wave) * 1024, 16, 0, 0);          \
+        else                                                                                    \
+          __builtin_amdgcn_global_load_lds(p.a_q + coff[c] + (uint32_t)(ks) * ROW_BYTES,        \
+                                           sbw + (c * C::NW + wave) * 1024, 16, 0, 0);          \
       }                                                                                         \
     }                                                                                           \
     _Pragma("unroll") for (int c = 0; c < C::SF_LOADS; ++c) {                                   \
       if ((part) < 0 || load_step(C::CODE_LOADS + c) == (part)) {                               \
-        const uint8_t* b = (c < C::SF_LOADS_W) ? wsbase : p.a_sf;                               \
-        __builtin_amdgcn_global_load_lds(b + soff[c] + (uint32_t)(ks) * SF_BYTES,               \
-                                         sbw + C::CODE_BYTES + (c * C::NW + wave) * 256, 4, 0, 0); \
+        if (c < C::SF_LOADS_W)                                                                  \
+          __builtin_amdgcn_global_load_lds(wsbase + soff[c] + (uint32_t)(ks) * (BN * SF_BYTES), \
+                                           sbw + C::CODE_BYTES + (c * C::NW + wave) * 1024, 16, 0, 0); \
+        else                                                                                    \
+          __builtin_amdgcn_global_load_lds(p.a_sf + soff[c] + (uint32_t)(ks) * SF_BYTES,        \
+                                           sbw + C::CODE_BYTES + BN * SF_BYTES +                \
+                                               ((c - C::SF_LOADS_W) * C::NW + wave) * 256, 4, 0, 0); \
       }                                                                                         \
     }                                                                                           \
   } while (0)
@@ -290,7 +302,7 @@ __device__ __forceinline__ void run_tile(const Params& p, uint8_t* smem, int e, 
   //     issued so far may stay in flight), synchronise the block, read the
   //     half A fragments and scales of stage ks+1;
   //   steps 4-7: half B;
-  //   the loads of stage ks+2 are spread over steps 0-6.
+  //   the loads of stage ks+2 are spread over steps 0-5, two per step.
   // Every step runs its MFMAs on operands decoded during the previous step
   // while it decodes the next step's operands, so decode and MFMA overlap;
   // step 7 decodes step 0 of the next stage.
@@ -299,12 +311,12 @@ __device__ __forceinline__ void run_tile(const Params& p, uint8_t* smem, int e, 
   NVFP4_ISSUE(0, 0, -1);
   if (nks > 1) {
     NVFP4_ISSUE(1, 1, -1);
-    asm volatile("s_waitcnt vmcnt(15)" ::: "memory");
+    asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
   } else {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
   __syncthreads();
-  static_assert(C::CODE_LOADS + C::SF_LOADS == 15, "vmcnt immediates assume 15 loads per stage");
+  static_assert(C::LOADS == 12 && kLoadsBeforeBarrier == 8, "vmcnt immediates assume 12 loads per stage");
 
   uint4 fa[FN], ta[FM], fb[FN], tb[FM];
   uint32_t wsr[FN], tsr[FM];
@@ -329,7 +341,7 @@ __device__ __forceinline__ void run_tile(const Params& p, uint8_t* smem, int e, 
     const int buf1 = buf == 2 ? 0 : buf + 1;           /* (ks + 1) % 3 */                       \
     /* operands of even steps live in av0/bv0, of odd steps in av1/bv1 */                       \
     if (LOADS) NVFP4_ISSUE(ks + 2, buf2, 0);                                                    \
-    NVFP4_DECODE(1, fa, ta, wsc, tsc, av1, bv1); NVFP4_MFMAS(av0, bv0); NVFP4_INTERLEAVE((LOADS) ? 3 : 0); \
+    NVFP4_DECODE(1, fa, ta, wsc, tsc, av1, bv1); NVFP4_MFMAS(av0, bv0); NVFP4_INTERLEAVE((LOADS) ? 2 : 0); \
     if (LOADS) NVFP4_ISSUE(ks + 2, buf2, 1);                                                    \
     NVFP4_DECODE(2, fa, ta, wsc, tsc, av0, bv0); NVFP4_MFMAS(av1, bv1); NVFP4_INTERLEAVE((LOADS) ? 2 : 0); \
     if (LOADS) NVFP4_ISSUE(ks + 2, buf2, 2);                                                    \
@@ -337,7 +349,7 @@ __device__ __forceinline__ void run_tile(const Params& p, uint8_t* smem, int e, 
     if (LOADS) NVFP4_ISSUE(ks + 2, buf2, 3);                                                    \
     NVFP4_DECODE(4, fb, tb, wsc, tsc, av0, bv0); NVFP4_MFMAS(av1, bv1); NVFP4_INTERLEAVE((LOADS) ? 2 : 0); \
     /* stage ks+1 must have landed; the loads of ks+2 issued so far may not have */             \
-    if (LOADS) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");  /* kLoadsBeforeBarrier */     \
+    if (LOADS) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");  /* kLoadsBeforeBarrier */     \
     else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");                                       \
     __syncthreads();                                                                            \
     if (more1) {                                                                                \
@@ -348,8 +360,7 @@ __device__ __forceinline__ void run_tile(const Params& p, uint8_t* smem, int e, 
     NVFP4_DECODE(5, fb, tb, wsc, tsc, av1, bv1); NVFP4_MFMAS(av0, bv0); NVFP4_INTERLEAVE((LOADS) ? 2 : 0); \
     if (LOADS) NVFP4_ISSUE(ks + 2, buf2, 5);                                                    \
     NVFP4_DECODE(6, fb, tb, wsc, tsc, av0, bv0); NVFP4_MFMAS(av1, bv1); NVFP4_INTERLEAVE((LOADS) ? 2 : 0); \
-    if (LOADS) NVFP4_ISSUE(ks + 2, buf2, 6);                                                    \
-    NVFP4_DECODE(7, fb, tb, wsc, tsc, av1, bv1); NVFP4_MFMAS(av0, bv0); NVFP4_INTERLEAVE((LOADS) ? 2 : 0); \
+    NVFP4_DECODE(7, fb, tb, wsc, tsc, av1, bv1); NVFP4_MFMAS(av0, bv0); NVFP4_INTERLEAVE(0); \
     if (more1) {                                                                                \
       _Pragma("unroll") for (int i = 0; i < FN; ++i) wsc[i] = scales4(wsr[i]);                  \
       _Pragma("unroll") for (int j = 0; j < JV; ++j) tsc[j] = scales4(tsr[j]);                  \

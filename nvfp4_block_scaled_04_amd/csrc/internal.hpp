@@ -29,6 +29,9 @@ hipError_t launch_route(const int32_t* topk_ids, int64_t T, int k, int E, int32_
                         hipStream_t stream);
 
 // layout.hip
+int64_t packed_rows(int64_t N);
+hipError_t launch_pack_weights(const uint8_t* q, const uint8_t* sf, int64_t E, int64_t N, int64_t K,
+                               uint8_t* qp, uint8_t* sfp, hipStream_t stream);
 hipError_t launch_weight_layout(const void* src, int64_t groups, int64_t rows, int64_t cols,
                                 int interleave, void* dst, hipStream_t stream);
 

@@ -58,7 +58,48 @@ __global__ void fill_i32_kernel(int32_t* p, int32_t v, int64_t n) {
   if (i < n) p[i] = v;
 }
 
+// One thread per (expert, padded row, K stage): 64 code bytes and 8 scale
+// bytes from the row-major weight to the stage-tiled layout (zeros for rows
+// past N).
+__global__ __launch_bounds__(256) void pack_weights_kernel(
+    const uint4* __restrict__ q, const uint2* __restrict__ sf, int64_t N, int64_t Np, int64_t S,
+    int64_t total, uint4* __restrict__ qp, uint2* __restrict__ sfp) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= total) return;
+  // i enumerates the destination: ((e * T + t) * S + s) * ROWS + r
+  const int64_t r = i % NVFP4_PACK_ROWS;
+  const int64_t rest = i / NVFP4_PACK_ROWS;
+  const int64_t s = rest % S;
+  const int64_t et = rest / S;
+  const int64_t tiles = Np / NVFP4_PACK_ROWS;
+  const int64_t t = et % tiles, e = et / tiles;
+  const int64_t n = t * NVFP4_PACK_ROWS + r;
+  uint4 c0 = make_uint4(0, 0, 0, 0), c1 = c0, c2 = c0, c3 = c0;
+  uint2 sc = make_uint2(0, 0);
+  if (n < N) {
+    const uint4* src = q + ((e * N + n) * S + s) * 4;       // 64 bytes = 4 x 16
+    c0 = src[0]; c1 = src[1]; c2 = src[2]; c3 = src[3];
+    sc = sf[(e * N + n) * S + s];
+  }
+  uint4* dst = qp + i * 4;
+  dst[0] = c0; dst[1] = c1; dst[2] = c2; dst[3] = c3;
+  sfp[i] = sc;
+}
+
 }  // namespace
+
+int64_t packed_rows(int64_t N) { return (N + NVFP4_PACK_ROWS - 1) / NVFP4_PACK_ROWS * NVFP4_PACK_ROWS; }
+
+hipError_t launch_pack_weights(const uint8_t* q, const uint8_t* sf, int64_t E, int64_t N, int64_t K,
+                               uint8_t* qp, uint8_t* sfp, hipStream_t stream) {
+  const int64_t Np = packed_rows(N), S = K / NVFP4_PACK_K;
+  const int64_t total = E * Np * S;
+  if (total == 0) return hipSuccess;
+  pack_weights_kernel<<<(unsigned)((total + 255) / 256), 256, 0, stream>>>(
+      reinterpret_cast<const uint4*>(q), reinterpret_cast<const uint2*>(sf), N, Np, S, total,
+      reinterpret_cast<uint4*>(qp), reinterpret_cast<uint2*>(sfp));
+  return hipGetLastError();
+}
 
 hipError_t launch_weight_layout(const void* src, int64_t groups, int64_t rows, int64_t cols,
                                 int interleave, void* dst, hipStream_t stream) {

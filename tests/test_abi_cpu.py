@@ -30,7 +30,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported(L):
     names = _declared()
-    assert len(names) >= 12
+    assert len(names) >= 14
     for n in names:
         assert hasattr(L, n), n
 
@@ -118,3 +118,13 @@ def test_combine_and_forward_reject(L):
     assert f(ws=FAKE + 16) == -3
     assert L.nvfp4_weight_layout(FAKE, 2, 4, 24, 1, FAKE, None) == -2
     assert L.nvfp4_weight_layout(FAKE, 2, 4, 32, 1, None, None) == -1
+
+
+def test_packed_weight_sizes_and_rejects(L):
+    sf = ctypes.c_size_t(0)
+    assert L.nvfp4_packed_weight_bytes(2, 1000, 384, ctypes.byref(sf)) == 2 * 1024 * 192
+    assert sf.value == 2 * 1024 * 24
+    assert L.nvfp4_packed_weight_bytes(2, 1000, 100, ctypes.byref(sf)) == 0
+    assert L.nvfp4_pack_weights(FAKE, FAKE, 2, 100, 200, FAKE, FAKE, None) == -2
+    assert L.nvfp4_pack_weights(None, FAKE, 2, 100, 256, FAKE, FAKE, None) == -1
+    assert L.nvfp4_pack_weights(FAKE, FAKE, 2, 100, 256, FAKE, FAKE + 8, None) == -1

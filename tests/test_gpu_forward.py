@@ -61,8 +61,9 @@ def _check_full(w, ids=None):
     w1 = np.stack([host(I.make_expert_weights(w, e, DEV)[0]) for e in range(w.E)])
     w2 = np.stack([host(I.make_expert_weights(w, e, DEV)[1]) for e in range(w.E)])
     wts = O.prepare_weights(w1, w2)
-    for n in ("w1_q", "w1_sf", "gs_w1", "w2_q", "w2_sf", "gs_w2"):
-        assert np.array_equal(host(getattr(ew, n)), wts[n]), n
+    for n in ("w1_q", "w1_sf", "w2_q", "w2_sf"):
+        assert np.array_equal(host(ew.rowmajor[n]), wts[n]), n
+    assert np.array_equal(host(ew.gs_w1), wts["gs_w1"]) and np.array_equal(host(ew.gs_w2), wts["gs_w2"])
     ref = O.moe_forward(host(x), ids, tw, wts, np.float32(w.gs_h), w.E)
     # bit-exact steps
     assert np.array_equal(tp["a_q"], ref["a_q"]) and np.array_equal(tp["a_sf"], ref["a_sf"])
@@ -169,7 +170,7 @@ def test_forward_full_size_sampled_tokens(name):
         res = [f.result() for f in futs]
     for (t, j, e, _, _), r in zip(jobs, res):
         for n in ("w1_q", "w1_sf", "w2_q", "w2_sf"):
-            assert np.array_equal(host(getattr(ew, n)[e]), r[n]), (n, e)
+            assert np.array_equal(host(ew.rowmajor[n][e]), r[n]), (n, e)
         assert host(ew.gs_w1)[e] == r["gs_w1"] and host(ew.gs_w2)[e] == r["gs_w2"]
     for t in toks:
         rows = [(j, r) for (tt, j, _, _, _), r in zip(jobs, res) if tt == t]

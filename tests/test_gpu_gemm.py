@@ -46,9 +46,9 @@ def _grouped_case(counts, N, K, seed, epi, gather_k=None, T=0):
         a_rows = np.arange(M)
     w = _randn((E * N, K), seed + 1, 0.02)
     b_q, b_sf, gs_b = nv.quantize(w, groups=E)
-    b_q, b_sf = b_q.view(E, N, K // 2), b_sf.view(E, N, K // 16)
+    b = nv.pack_weights(b_q.view(E, N, K // 2), b_sf.view(E, N, K // 16))
     gs_out = torch.tensor([64.0], device=DEV)
-    res = nv.grouped_gemm(epi, a_q, a_sf, gs_a, off, b_q, b_sf, gs_b, M, a_row_src=src,
+    res = nv.grouped_gemm(epi, a_q, a_sf, gs_a, off, b, gs_b, M, a_row_src=src,
                           a_row_div=gather_k or 1, gs_out=gs_out, debug=True)
     torch.cuda.synchronize()
     # oracle from the same bf16 inputs
@@ -105,8 +105,8 @@ def test_dense_linear_config2_sampled_rows():
     bk = nv.weight_layout(b.view(1, K, N), False)[0]              # (N, K)
     b_q, b_sf, gs_b = nv.quantize(bk)
     off = torch.tensor([0, M], dtype=torch.int32, device=DEV)
-    c = nv.grouped_gemm(nv.EPI_BF16, a_q, a_sf, gs_a, off, b_q.view(1, N, K // 2),
-                        b_sf.view(1, N, K // 16), gs_b, M)
+    c = nv.grouped_gemm(nv.EPI_BF16, a_q, a_sf, gs_a, off,
+                        nv.pack_weights(b_q.view(1, N, K // 2), b_sf.view(1, N, K // 16)), gs_b, M)
     torch.cuda.synchronize()
     ab, bb = host(a), host(b)
     gsa = Q.global_scale(ab)

@@ -172,5 +172,30 @@ def test_expert_weight_prep_bit_exact_tiny():
     ew = nv.prepare_expert_weights([w1], [w2], DEV)
     torch.cuda.synchronize()
     ref = O.prepare_weights(host(w1), host(w2))
-    for name in ("w1_q", "w1_sf", "gs_w1", "w2_q", "w2_sf", "gs_w2"):
-        assert np.array_equal(host(getattr(ew, name)), ref[name]), name
+    for name in ("w1_q", "w1_sf", "w2_q", "w2_sf"):
+        assert np.array_equal(host(ew.rowmajor[name]), ref[name]), name
+    assert np.array_equal(host(ew.gs_w1), ref["gs_w1"]) and np.array_equal(host(ew.gs_w2), ref["gs_w2"])
+
+
+def _pack_reference(q, sf, rows=512, kstage=128):
+    """The packed layout written out with NumPy reshapes (a pure re-blocking)."""
+    E, N, Kh = q.shape
+    S = Kh * 2 // kstage
+    Np = -(-N // rows) * rows
+    qp = np.zeros((E, Np, Kh), np.uint8); qp[:, :N] = q
+    sp = np.zeros((E, Np, sf.shape[2]), np.uint8); sp[:, :N] = sf
+    qp = qp.reshape(E, Np // rows, rows, S, kstage // 2).transpose(0, 1, 3, 2, 4)
+    sp = sp.reshape(E, Np // rows, rows, S, kstage // 16).transpose(0, 1, 3, 2, 4)
+    return qp.ravel(), sp.ravel()
+
+
+@pytest.mark.parametrize("E,N,K", [(1, 512, 128), (3, 96, 256), (2, 1000, 384), (4, 4096, 7168)])
+def test_pack_weights_layout(E, N, K):
+    g = torch.Generator(device=DEV).manual_seed(E * N + K)
+    q = torch.randint(0, 256, (E, N, K // 2), generator=g, device=DEV, dtype=torch.int32).to(torch.uint8)
+    sf = torch.randint(0, 256, (E, N, K // 16), generator=g, device=DEV, dtype=torch.int32).to(torch.uint8)
+    print(f"[case] pack E={E} N={N} K={K}", flush=True)
+    pw = nv.pack_weights(q, sf)
+    torch.cuda.synchronize()
+    rq, rs = _pack_reference(host(q), host(sf))
+    assert np.array_equal(host(pw.q), rq) and np.array_equal(host(pw.sf), rs)
