@@ -42,6 +42,9 @@ def _compile(src):
 
 def build(verbose=True):
     os.makedirs(BUILD, exist_ok=True)
+    # a failed build must not leave an older library behind to be loaded
+    if os.path.exists(LIB):
+        os.remove(LIB)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
         objs = list(ex.map(_compile, srcs))

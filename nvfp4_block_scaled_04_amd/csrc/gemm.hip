@@ -96,10 +96,10 @@ __device__ __forceinline__ half8v decode8(uint32_t w, _Float16 s) {
 // four E4M3 scale bytes -> four FP16 values (exact: E4M3 is a subset of FP16)
 struct Scales4 {
   half2v lo, hi;
-  __device__ __forceinline__ _Float16 get(int i) const {
-    return i == 0 ? lo[0] : i == 1 ? lo[1] : i == 2 ? hi[0] : hi[1];
-  }
 };
+__device__ __forceinline__ _Float16 sget(const Scales4& s, int i) {
+  return i == 0 ? s.lo[0] : i == 1 ? s.lo[1] : i == 2 ? s.hi[0] : s.hi[1];
+}
 __device__ __forceinline__ Scales4 scales4(uint32_t b) {
   Scales4 s;
   s.lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b, 1.0f, false);
@@ -156,6 +156,222 @@ __host__ __device__ constexpr int load_step(int L) { return L / 2; }
 // loads issued in steps 0..3, still in flight at the mid-stage wait
 constexpr int kLoadsBeforeBarrier = 8;
 
+// Per-lane state of a tile's K loop; every member lives in registers once the
+// stage functions below are inlined.
+template <int BN, int BM, int WN, int WM, int JV>
+struct KState {
+  using C = Cfg<BN, BM, WN, WM>;
+  int wn, wm, hf, l32;
+  float16v acc[C::FN][C::FM];
+  uint4 fa[C::FN], ta[C::FM], fb[C::FN], tb[C::FM];  // half-stage code fragments
+  uint32_t wsr[C::FN], tsr[C::FM];                   // scale bytes of the next stage
+  Scales4 wsc[C::FN], tsc[C::FM];                    // scales of the current stage
+  half8v av0[C::FN], bv0[C::FM], av1[C::FN], bv1[C::FM];   // decoded operands: even, odd steps
+};
+
+// Workgroup barrier without a memory fence.  The waits a stage needs are its
+// own s_waitcnt; the empty asm statements stop the compiler from moving
+// memory accesses across the barrier.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Direct-to-LDS loads of stage ks into `dst`: all of them (part < 0) or those
+// of K step `part`.  wq/wsf: this tile's packed weight codes/scales; aq/asf:
+// token codes/scales; coff/soff: per-lane byte offsets of the wave's loads.
+// The load counts and sizes come from plain constexpr ints (NVFP4_LOAD_CONSTS):
+// the host pass rejects the load builtin when its arguments involve members
+// of the dependent tile configuration.
+#define NVFP4_LOAD_CONSTS                                                                       \
+  constexpr int kNW = C::NW, kCodeLoads = C::CODE_LOADS, kCodeLoadsW = C::CODE_LOADS_W;         \
+  constexpr int kSfLoads = C::SF_LOADS, kSfLoadsW = C::SF_LOADS_W, kCodeBytes = C::CODE_BYTES
+#define NVFP4_ISSUE(ks, dst, part)                                                              \
+  do {                                                                                          \
+    uint8_t* sbw = (dst);                                                                       \
+    _Pragma("unroll") for (int c = 0; c < kCodeLoads; ++c) {                                    \
+      if ((part) < 0 || load_step(c) == (part)) {                                               \
+        if (c < kCodeLoadsW)                                                                    \
+          __builtin_amdgcn_global_load_lds(wq + coff[c] + (uint32_t)(ks) * (BN * ROW_BYTES),    \
+                                           sbw + (c * kNW + wave) * 1024, 16, 0, 0);            \
+        else                                                                                    \
+          __builtin_amdgcn_global_load_lds(aq + coff[c] + (uint32_t)(ks) * ROW_BYTES,           \
+                                           sbw + (c * kNW + wave) * 1024, 16, 0, 0);            \
+      }                                                                                         \
+    }                                                                                           \
+    _Pragma("unroll") for (int c = 0; c < kSfLoads; ++c) {                                      \
+      if ((part) < 0 || load_step(kCodeLoads + c) == (part)) {                                  \
+        if (c < kSfLoadsW)                                                                      \
+          __builtin_amdgcn_global_load_lds(wsf + soff[c] + (uint32_t)(ks) * (BN * SF_BYTES),    \
+                                           sbw + kCodeBytes + (c * kNW + wave) * 1024, 16, 0, 0); \
+        else                                                                                    \
+          __builtin_amdgcn_global_load_lds(asf + soff[c] + (uint32_t)(ks) * SF_BYTES,           \
+                                           sbw + kCodeBytes + BN * SF_BYTES +                   \
+                                               ((c - kSfLoadsW) * kNW + wave) * 256, 4, 0, 0);  \
+      }                                                                                         \
+    }                                                                                           \
+  } while (0)
+
+// fragment reads: half h (0 or 1) of every A and B block of the stage held
+// in `src`: 16 contiguous code bytes per lane and block
+#define NVFP4_READ_HALF(src, h, WA, TB)                                                         \
+  do {                                                                                          \
+    const uint8_t* sbr = (src);                                                                 \
+    _Pragma("unroll") for (int i = 0; i < FN; ++i) {                                            \
+      const int r = st.wn * TN + i * 32 + st.l32;                                               \
+      WA[i] = *reinterpret_cast<const uint4*>(sbr + r * ROW_BYTES + 16 * chunk_pos(r, 2 * st.hf + (h))); \
+    }                                                                                           \
+    _Pragma("unroll") for (int j = 0; j < JV; ++j) {                                            \
+      const int r = BN + st.wm * TM + j * 32 + st.l32;                                          \
+      TB[j] = *reinterpret_cast<const uint4*>(sbr + r * ROW_BYTES + 16 * chunk_pos(r, 2 * st.hf + (h))); \
+    }                                                                                           \
+  } while (0)
+
+#define NVFP4_READ_SF(src, WS, TS)                                                              \
+  do {                                                                                          \
+    const uint8_t* sbr = (src) + C::CODE_BYTES;                                                 \
+    _Pragma("unroll") for (int i = 0; i < FN; ++i)                                              \
+      WS[i] = *reinterpret_cast<const uint32_t*>(sbr + (st.wn * TN + i * 32 + st.l32) * SF_BYTES + st.hf * 4); \
+    _Pragma("unroll") for (int j = 0; j < JV; ++j)                                              \
+      TS[j] = *reinterpret_cast<const uint32_t*>(sbr + (BN + st.wm * TM + j * 32 + st.l32) * SF_BYTES + st.hf * 4); \
+  } while (0)
+
+// decode of one 16-deep K step: dword (s & 3) of the half fragments with
+// scale byte (s >> 1); and the FN x JV MFMAs of a decoded step
+#define NVFP4_DECODE(s, WA, TB, WSC, TSC, AV, BV)                                               \
+  do {                                                                                          \
+    _Pragma("unroll") for (int i = 0; i < FN; ++i)                                              \
+      AV[i] = decode8(pick(WA[i], (s) & 3), sget(WSC[i], (s) >> 1));                            \
+    _Pragma("unroll") for (int j = 0; j < JV; ++j)                                              \
+      BV[j] = decode8(pick(TB[j], (s) & 3), sget(TSC[j], (s) >> 1));                            \
+  } while (0)
+#define NVFP4_MFMAS(AV, BV)                                                                     \
+  do {                                                                                          \
+    _Pragma("unroll") for (int i = 0; i < FN; ++i)                                              \
+      _Pragma("unroll") for (int j = 0; j < JV; ++j)                                            \
+        st.acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(AV[i], BV[j], st.acc[i][j], 0, 0, 0); \
+  } while (0)
+// interleave: one MFMA of this step, then VPM VALU of the next step's decode;
+// the step's NL stage loads go right after MFMAs spread over the step, so a
+// load that waits to issue leaves the matrix pipe busy
+#define NVFP4_INTERLEAVE(NL)                                                                    \
+  do {                                                                                          \
+    constexpr int nl_ = (NL);                                                                   \
+    constexpr int every_ = nl_ > 0 ? (FN * JV + nl_ - 1) / (nl_ > 0 ? nl_ : 1) : 1;             \
+    _Pragma("unroll") for (int q = 0; q < FN * JV; ++q) {                                       \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                        \
+      if (nl_ > 0 && q % every_ == 0 && q / every_ < nl_)                                       \
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                                      \
+      __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);                                      \
+    }                                                                                           \
+  } while (0)
+
+// Loads stages 0 and 1 (buffers b0, b1), waits for stage 0 and decodes its
+// step 0.  The pointer parameters are __restrict__ here and in k_stage: LDS
+// reads of one buffer are then known not to alias direct loads into
+// another, so the compiler adds no wait on the loads in flight; every wait
+// those reads need is an explicit s_waitcnt + barrier.
+template <int BN, int BM, int WN, int WM, int JV>
+__device__ __forceinline__ void k_prologue(KState<BN, BM, WN, WM, JV>& st, int nks, int wave,
+                                           const uint32_t* coff, const uint32_t* soff,
+                                           const uint8_t* __restrict__ wq,
+                                           const uint8_t* __restrict__ wsf,
+                                           const uint8_t* __restrict__ aq,
+                                           const uint8_t* __restrict__ asf,
+                                           uint8_t* __restrict__ b0, uint8_t* __restrict__ b1) {
+  using C = Cfg<BN, BM, WN, WM>;
+  constexpr int FN = C::FN, TN = C::TN, TM = C::TM;
+  NVFP4_LOAD_CONSTS;
+  static_assert(C::LOADS == 12 && kLoadsBeforeBarrier == 8, "vmcnt immediates assume 12 loads per stage");
+  NVFP4_ISSUE(0, b0, -1);
+  if (nks > 1) {
+    NVFP4_ISSUE(1, b1, -1);
+    asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+  } else {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+  stage_barrier();
+  NVFP4_READ_HALF(b0, 0, st.fa, st.ta);
+  NVFP4_READ_SF(b0, st.wsr, st.tsr);
+#pragma unroll
+  for (int i = 0; i < FN; ++i) st.wsc[i] = scales4(st.wsr[i]);
+#pragma unroll
+  for (int j = 0; j < JV; ++j) st.tsc[j] = scales4(st.tsr[j]);
+  NVFP4_DECODE(0, st.fa, st.ta, st.wsc, st.tsc, st.av0, st.bv0);
+}
+
+// One stage ks, held in br; stage ks+1 is in bm; with LOADS (a literal 1 or
+// 0: whether stage ks+2 exists) its loads go into bw.  LOADS stages have no
+// branches, so the loads and the MFMAs share one scheduling region.
+//   steps 0-3: half A fragments (in registers); half B fragments of stage ks
+//     are read from LDS;
+//   after step 3: wait until stage ks+1 has landed (the loads of ks+2 issued
+//     so far may stay in flight), synchronise the block, read the half A
+//     fragments and scales of stage ks+1;
+//   steps 4-7: half B;
+//   the loads of stage ks+2 are spread over steps 0-5, two per step.
+// Every step runs its MFMAs on operands decoded during the previous step
+// while it decodes the next step's operands, so decode and MFMA overlap;
+// step 7 decodes step 0 of the next stage.  bw held stage ks-1, last read
+// before the mid-stage barrier of ks-1.
+template <int BN, int BM, int WN, int WM, int JV, int LOADS>
+__device__ __forceinline__ void k_stage(KState<BN, BM, WN, WM, JV>& st, int ks, int nks, int wave,
+                                        const uint32_t* coff, const uint32_t* soff,
+                                        const uint8_t* __restrict__ wq,
+                                        const uint8_t* __restrict__ wsf,
+                                        const uint8_t* __restrict__ aq,
+                                        const uint8_t* __restrict__ asf,
+                                        const uint8_t* __restrict__ br,
+                                        const uint8_t* __restrict__ bm,
+                                        uint8_t* __restrict__ bw) {
+  using C = Cfg<BN, BM, WN, WM>;
+  constexpr int FN = C::FN, TN = C::TN, TM = C::TM;
+  NVFP4_LOAD_CONSTS;
+  // VALU of one step's decode per MFMA of a step
+  constexpr int VPM = ((FN + JV) * 8 + FN * JV - 1) / (FN * JV);
+  constexpr int NL = LOADS ? 2 : 0;
+  NVFP4_READ_HALF(br, 1, st.fb, st.tb);
+  const bool more1 = LOADS || ks + 1 < nks;
+  // operands of even steps live in av0/bv0, of odd steps in av1/bv1
+  if (LOADS) NVFP4_ISSUE(ks + 2, bw, 0);
+  NVFP4_DECODE(1, st.fa, st.ta, st.wsc, st.tsc, st.av1, st.bv1); NVFP4_MFMAS(st.av0, st.bv0); NVFP4_INTERLEAVE(NL);
+  if (LOADS) NVFP4_ISSUE(ks + 2, bw, 1);
+  NVFP4_DECODE(2, st.fa, st.ta, st.wsc, st.tsc, st.av0, st.bv0); NVFP4_MFMAS(st.av1, st.bv1); NVFP4_INTERLEAVE(NL);
+  if (LOADS) NVFP4_ISSUE(ks + 2, bw, 2);
+  NVFP4_DECODE(3, st.fa, st.ta, st.wsc, st.tsc, st.av1, st.bv1); NVFP4_MFMAS(st.av0, st.bv0); NVFP4_INTERLEAVE(NL);
+  if (LOADS) NVFP4_ISSUE(ks + 2, bw, 3);
+  NVFP4_DECODE(4, st.fb, st.tb, st.wsc, st.tsc, st.av0, st.bv0); NVFP4_MFMAS(st.av1, st.bv1); NVFP4_INTERLEAVE(NL);
+  // stage ks+1 must have landed; the loads of ks+2 issued so far may not have
+  if (LOADS) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");   // kLoadsBeforeBarrier
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  stage_barrier();
+  if (more1) {
+    NVFP4_READ_HALF(bm, 0, st.fa, st.ta);
+    NVFP4_READ_SF(bm, st.wsr, st.tsr);
+  }
+  if (LOADS) NVFP4_ISSUE(ks + 2, bw, 4);
+  NVFP4_DECODE(5, st.fb, st.tb, st.wsc, st.tsc, st.av1, st.bv1); NVFP4_MFMAS(st.av0, st.bv0); NVFP4_INTERLEAVE(NL);
+  if (LOADS) NVFP4_ISSUE(ks + 2, bw, 5);
+  NVFP4_DECODE(6, st.fb, st.tb, st.wsc, st.tsc, st.av0, st.bv0); NVFP4_MFMAS(st.av1, st.bv1); NVFP4_INTERLEAVE(NL);
+  NVFP4_DECODE(7, st.fb, st.tb, st.wsc, st.tsc, st.av1, st.bv1); NVFP4_MFMAS(st.av0, st.bv0); NVFP4_INTERLEAVE(0);
+  if (more1) {
+#pragma unroll
+    for (int i = 0; i < FN; ++i) st.wsc[i] = scales4(st.wsr[i]);
+#pragma unroll
+    for (int j = 0; j < JV; ++j) st.tsc[j] = scales4(st.tsr[j]);
+    NVFP4_DECODE(0, st.fa, st.ta, st.wsc, st.tsc, st.av0, st.bv0);
+  }
+  NVFP4_MFMAS(st.av1, st.bv1); NVFP4_INTERLEAVE(0);
+}
+#undef NVFP4_ISSUE
+#undef NVFP4_LOAD_CONSTS
+#undef NVFP4_READ_HALF
+#undef NVFP4_READ_SF
+#undef NVFP4_DECODE
+#undef NVFP4_MFMAS
+#undef NVFP4_INTERLEAVE
+
 // One tile: the K loop and the epilogue.  JV = number of 32-token column
 // blocks that hold rows (1..FM); the rest are skipped.
 template <int BN, int BM, int WN, int WM, int EPI, int JV>
@@ -175,6 +391,8 @@ __device__ __forceinline__ void run_tile(const Params& p, uint8_t* smem, int e, 
   const uint8_t* wbase = p.b_q + ((int64_t)e * Np + n0) * kb;
   const uint8_t* wsbase = p.b_sf + ((int64_t)e * Np + n0) * ksf;
 
+  KState<BN, BM, WN, WM, JV> st;
+  st.wn = wn; st.wm = wm; st.hf = hf; st.l32 = l32;
   // physical weight row (within the tile) held by LDS row r
   auto wrow = [&](int r) -> int {
     return (EPI == NVFP4_EPI_SWIGLU_NVFP4) ? ((r & ~31) | swiglu_phys_row(r & 31)) : r;
@@ -192,195 +410,45 @@ __device__ __forceinline__ void run_tile(const Params& p, uint8_t* smem, int e, 
     const int r = 16 * g + (lane >> 2);
     const int q = chunk_pos(r, lane & 3);          // logical chunk stored at this lane's position
     coff[c] = (c < C::CODE_LOADS_W) ? (uint32_t)(wrow(r) * ROW_BYTES + 16 * q)
-                                    : trow(r - BN) * kb + 16 * q;
+                                       : trow(r - BN) * kb + 16 * q;
   }
 #pragma unroll
   for (int c = 0; c < C::SF_LOADS_W; ++c) {      // 2 consecutive rows per lane
     const int r = 128 * (c * C::NW + wave) + 2 * lane;
-    soff[c] = (uint32_t)(wrow(r) * SF_BYTES);      // wrow(r + 1) == wrow(r) + 1 (r even)
+    soff[c] = (uint32_t)(wrow(r) * SF_BYTES);   // wrow(r + 1) == wrow(r) + 1 (r even)
   }
 #pragma unroll
   for (int c = 0; c < C::SF_LOADS_T; ++c) {      // one 4-byte half row per lane
     const int i = 32 * (c * C::NW + wave) + (lane >> 1);
     soff[C::SF_LOADS_W + c] = trow(i) * ksf + 4 * (lane & 1);
   }
-
-#define NVFP4_ISSUE(ks, buf, part)                                                              \
-  do {                                                                                          \
-    uint8_t* sbw = smem + (buf) * C::STAGE_BYTES;                                               \
-    _Pragma("unroll") for (int c = 0; c < C::CODE_LOADS; ++c) {                                 \
-      if ((part) < 0 || load_step(c) == (part)) {                                               \
-        if (c < C::CODE_LOADS_W)                                                                \
-          __builtin_amdgcn_global_load_lds(wbase + coff[c] + (uint32_t)(ks) * (BN * ROW_BYTES), \
-                                           sbw + (c * C::NW + wave) * 1024, 16, 0, 0);          \
-        else                                                                                    \
-          __builtin_amdgcn_global_load_lds(p.a_q + coff[c] + (uint32_t)(ks) * ROW_BYTES,        \
-                                           sbw + (c * C::NW + wave) * 1024, 16, 0, 0);          \
-      }                                                                                         \
-    }                                                                                           \
-    _Pragma("unroll") for (int c = 0; c < C::SF_LOADS; ++c) {                                   \
-      if ((part) < 0 || load_step(C::CODE_LOADS + c) == (part)) {                               \
-        if (c < C::SF_LOADS_W)                                                                  \
-          __builtin_amdgcn_global_load_lds(wsbase + soff[c] + (uint32_t)(ks) * (BN * SF_BYTES), \
-                                           sbw + C::CODE_BYTES + (c * C::NW + wave) * 1024, 16, 0, 0); \
-        else                                                                                    \
-          __builtin_amdgcn_global_load_lds(p.a_sf + soff[c] + (uint32_t)(ks) * SF_BYTES,        \
-                                           sbw + C::CODE_BYTES + BN * SF_BYTES +                \
-                                               ((c - C::SF_LOADS_W) * C::NW + wave) * 256, 4, 0, 0); \
-      }                                                                                         \
-    }                                                                                           \
-  } while (0)
-
-// fragment reads: half h (0 or 1) of every A and B block of the stage in
-// buffer `buf`: 16 contiguous code bytes per lane and block
-#define NVFP4_READ_HALF(buf, h, WA, TB)                                                         \
-  do {                                                                                          \
-    const uint8_t* sbr = smem + (buf) * C::STAGE_BYTES;                                         \
-    _Pragma("unroll") for (int i = 0; i < FN; ++i) {                                            \
-      const int r = wn * TN + i * 32 + l32;                                                     \
-      WA[i] = *reinterpret_cast<const uint4*>(sbr + r * ROW_BYTES + 16 * chunk_pos(r, 2 * hf + (h))); \
-    }                                                                                           \
-    _Pragma("unroll") for (int j = 0; j < JV; ++j) {                                            \
-      const int r = BN + wm * TM + j * 32 + l32;                                                \
-      TB[j] = *reinterpret_cast<const uint4*>(sbr + r * ROW_BYTES + 16 * chunk_pos(r, 2 * hf + (h))); \
-    }                                                                                           \
-  } while (0)
-
-#define NVFP4_READ_SF(buf, WS, TS)                                                              \
-  do {                                                                                          \
-    const uint8_t* sbr = smem + (buf) * C::STAGE_BYTES + C::CODE_BYTES;                         \
-    _Pragma("unroll") for (int i = 0; i < FN; ++i)                                              \
-      WS[i] = *reinterpret_cast<const uint32_t*>(sbr + (wn * TN + i * 32 + l32) * SF_BYTES + hf * 4); \
-    _Pragma("unroll") for (int j = 0; j < JV; ++j)                                              \
-      TS[j] = *reinterpret_cast<const uint32_t*>(sbr + (BN + wm * TM + j * 32 + l32) * SF_BYTES + hf * 4); \
-  } while (0)
-
-// decode of one 16-deep K step: dword (s & 3) of the half fragments with
-// scale byte (s >> 1); and the FN x JV MFMAs of a decoded step
-#define NVFP4_DECODE(s, WA, TB, WSC, TSC, AV, BV)                                               \
-  do {                                                                                          \
-    _Pragma("unroll") for (int i = 0; i < FN; ++i)                                              \
-      AV[i] = decode8(pick(WA[i], (s) & 3), WSC[i].get((s) >> 1));                              \
-    _Pragma("unroll") for (int j = 0; j < JV; ++j)                                              \
-      BV[j] = decode8(pick(TB[j], (s) & 3), TSC[j].get((s) >> 1));                              \
-  } while (0)
-#define NVFP4_MFMAS(AV, BV)                                                                     \
-  do {                                                                                          \
-    _Pragma("unroll") for (int i = 0; i < FN; ++i)                                              \
-      _Pragma("unroll") for (int j = 0; j < JV; ++j)                                            \
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(AV[i], BV[j], acc[i][j], 0, 0, 0);   \
-  } while (0)
-// interleave: one MFMA of this step, then VPM VALU of the next step's decode;
-// the step's NL stage loads go right after MFMAs spread over the step, so a
-// load that waits to issue leaves the matrix pipe busy
-#define NVFP4_INTERLEAVE(NL)                                                                    \
-  do {                                                                                          \
-    constexpr int nl_ = (NL);                                                                   \
-    constexpr int every_ = nl_ > 0 ? (FN * JV + nl_ - 1) / nl_ : 1;                             \
-    _Pragma("unroll") for (int q = 0; q < FN * JV; ++q) {                                       \
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                        \
-      if (nl_ > 0 && q % every_ == 0 && q / every_ < nl_)                                       \
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                                      \
-      __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);                                      \
-    }                                                                                           \
-  } while (0)
-
-  float16v acc[FN][FM];
 #pragma unroll
   for (int i = 0; i < FN; ++i)
 #pragma unroll
     for (int j = 0; j < FM; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-  // VALU of one step's decode per MFMA of a step
-  constexpr int VPM = ((FN + JV) * 8 + FN * JV - 1) / (FN * JV);
+      for (int r = 0; r < 16; ++r) st.acc[i][j][r] = 0.0f;
 
-  // Pipeline (three LDS buffers, stage ks in buffer ks % 3):
-  //   steps 0-3: half A fragments (in registers); half B fragments of stage
-  //     ks are read from LDS;
-  //   after step 3: wait until stage ks+1 has landed (the loads of ks+2
-  //     issued so far may stay in flight), synchronise the block, read the
-  //     half A fragments and scales of stage ks+1;
-  //   steps 4-7: half B;
-  //   the loads of stage ks+2 are spread over steps 0-5, two per step.
-  // Every step runs its MFMAs on operands decoded during the previous step
-  // while it decodes the next step's operands, so decode and MFMA overlap;
-  // step 7 decodes step 0 of the next stage.
-  // Buffer (ks+2) % 3 was last read before the mid-stage barrier of ks-1.
+  // three LDS stage buffers, stage ks in buffer ks % 3
   const int nks = (int)(K / BK);
-  NVFP4_ISSUE(0, 0, -1);
-  if (nks > 1) {
-    NVFP4_ISSUE(1, 1, -1);
-    asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
-  } else {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  }
-  __syncthreads();
-  static_assert(C::LOADS == 12 && kLoadsBeforeBarrier == 8, "vmcnt immediates assume 12 loads per stage");
-
-  uint4 fa[FN], ta[FM], fb[FN], tb[FM];
-  uint32_t wsr[FN], tsr[FM];
-  Scales4 wsc[FN], tsc[FM];
-  half8v av0[FN], bv0[FM], av1[FN], bv1[FM];
-  NVFP4_READ_HALF(0, 0, fa, ta);
-  NVFP4_READ_SF(0, wsr, tsr);
-#pragma unroll
-  for (int i = 0; i < FN; ++i) wsc[i] = scales4(wsr[i]);
-#pragma unroll
-  for (int j = 0; j < JV; ++j) tsc[j] = scales4(tsr[j]);
-  NVFP4_DECODE(0, fa, ta, wsc, tsc, av0, bv0);
-
-// One stage.  LOADS (a literal 1 or 0): whether stage ks+2 exists and is
-// loaded here; with LOADS the body has no branches, so the loads and the
-// MFMAs share one scheduling region.
-#define NVFP4_STAGE(LOADS)                                                                      \
-  do {                                                                                          \
-    NVFP4_READ_HALF(buf, 1, fb, tb);                                                            \
-    const bool more1 = (LOADS) || ks + 1 < nks;                                                 \
-    const int buf2 = buf == 0 ? 2 : buf - 1;           /* (ks + 2) % 3 */                       \
-    const int buf1 = buf == 2 ? 0 : buf + 1;           /* (ks + 1) % 3 */                       \
-    /* operands of even steps live in av0/bv0, of odd steps in av1/bv1 */                       \
-    if (LOADS) NVFP4_ISSUE(ks + 2, buf2, 0);                                                    \
-    NVFP4_DECODE(1, fa, ta, wsc, tsc, av1, bv1); NVFP4_MFMAS(av0, bv0); NVFP4_INTERLEAVE((LOADS) ? 2 : 0); \
-    if (LOADS) NVFP4_ISSUE(ks + 2, buf2, 1);                                                    \
-    NVFP4_DECODE(2, fa, ta, wsc, tsc, av0, bv0); NVFP4_MFMAS(av1, bv1); NVFP4_INTERLEAVE((LOADS) ? 2 : 0); \
-    if (LOADS) NVFP4_ISSUE(ks + 2, buf2, 2);                                                    \
-    NVFP4_DECODE(3, fa, ta, wsc, tsc, av1, bv1); NVFP4_MFMAS(av0, bv0); NVFP4_INTERLEAVE((LOADS) ? 2 : 0); \
-    if (LOADS) NVFP4_ISSUE(ks + 2, buf2, 3);                                                    \
-    NVFP4_DECODE(4, fb, tb, wsc, tsc, av0, bv0); NVFP4_MFMAS(av1, bv1); NVFP4_INTERLEAVE((LOADS) ? 2 : 0); \
-    /* stage ks+1 must have landed; the loads of ks+2 issued so far may not have */             \
-    if (LOADS) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");  /* kLoadsBeforeBarrier */     \
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");                                       \
-    __syncthreads();                                                                            \
-    if (more1) {                                                                                \
-      NVFP4_READ_HALF(buf1, 0, fa, ta);                                                         \
-      NVFP4_READ_SF(buf1, wsr, tsr);                                                            \
-    }                                                                                           \
-    if (LOADS) NVFP4_ISSUE(ks + 2, buf2, 4);                                                    \
-    NVFP4_DECODE(5, fb, tb, wsc, tsc, av1, bv1); NVFP4_MFMAS(av0, bv0); NVFP4_INTERLEAVE((LOADS) ? 2 : 0); \
-    if (LOADS) NVFP4_ISSUE(ks + 2, buf2, 5);                                                    \
-    NVFP4_DECODE(6, fb, tb, wsc, tsc, av0, bv0); NVFP4_MFMAS(av1, bv1); NVFP4_INTERLEAVE((LOADS) ? 2 : 0); \
-    NVFP4_DECODE(7, fb, tb, wsc, tsc, av1, bv1); NVFP4_MFMAS(av0, bv0); NVFP4_INTERLEAVE(0); \
-    if (more1) {                                                                                \
-      _Pragma("unroll") for (int i = 0; i < FN; ++i) wsc[i] = scales4(wsr[i]);                  \
-      _Pragma("unroll") for (int j = 0; j < JV; ++j) tsc[j] = scales4(tsr[j]);                  \
-      NVFP4_DECODE(0, fa, ta, wsc, tsc, av0, bv0);                                              \
-    }                                                                                           \
-    NVFP4_MFMAS(av1, bv1); NVFP4_INTERLEAVE(0);                                                 \
-    buf = buf1;                                                                                 \
-  } while (0)
-
+  k_prologue(st, nks, wave, coff, soff, wbase, wsbase, p.a_q, p.a_sf, smem, smem + C::STAGE_BYTES);
   int buf = 0;
   int ks = 0;
-  for (; ks + 2 < nks; ++ks) NVFP4_STAGE(1);
-  for (; ks < nks; ++ks) NVFP4_STAGE(0);
-#undef NVFP4_STAGE
-#undef NVFP4_ISSUE
-#undef NVFP4_READ_HALF
-#undef NVFP4_READ_SF
-#undef NVFP4_DECODE
-#undef NVFP4_MFMAS
-#undef NVFP4_INTERLEAVE
+  for (; ks + 2 < nks; ++ks) {
+    const int buf1 = buf == 2 ? 0 : buf + 1, buf2 = buf == 0 ? 2 : buf - 1;
+    k_stage<BN, BM, WN, WM, JV, 1>(st, ks, nks, wave, coff, soff, wbase, wsbase, p.a_q, p.a_sf,
+                                   smem + buf * C::STAGE_BYTES, smem + buf1 * C::STAGE_BYTES,
+                                   smem + buf2 * C::STAGE_BYTES);
+    buf = buf1;
+  }
+  for (; ks < nks; ++ks) {
+    const int buf1 = buf == 2 ? 0 : buf + 1, buf2 = buf == 0 ? 2 : buf - 1;
+    k_stage<BN, BM, WN, WM, JV, 0>(st, ks, nks, wave, coff, soff, wbase, wsbase, p.a_q, p.a_sf,
+                                   smem + buf * C::STAGE_BYTES, smem + buf1 * C::STAGE_BYTES,
+                                   smem + buf2 * C::STAGE_BYTES);
+    buf = buf1;
+  }
+  float16v (&acc)[FN][FM] = st.acc;
   __syncthreads();   // every wave is done with the stage buffers (the epilogue reuses LDS)
 
   // ---- epilogue
