@@ -267,30 +267,36 @@ __device__ __forceinline__ void stage_barrier() {
     }                                                                                           \
   } while (0)
 
-// Loads stages 0 and 1 (buffers b0, b1), waits for stage 0 and decodes its
-// step 0.  The pointer parameters are __restrict__ here and in k_stage: LDS
-// reads of one buffer are then known not to alias direct loads into
-// another, so the compiler adds no wait on the loads in flight; every wait
-// those reads need is an explicit s_waitcnt + barrier.
+// Direct loads of a tile's stages 0 and 1 into buffers b0 and b1.  The
+// pointer parameters are __restrict__ here and in k_stage: LDS reads of one
+// buffer are then known not to alias direct loads into another, so the
+// compiler adds no wait on loads in flight; every wait those reads need is
+// an explicit s_waitcnt + barrier.
+template <int BN, int BM, int WN, int WM>
+__device__ __forceinline__ void k_issue_first(int nks, int wave, const uint32_t* coff,
+                                              const uint32_t* soff,
+                                              const uint8_t* __restrict__ wq,
+                                              const uint8_t* __restrict__ wsf,
+                                              const uint8_t* __restrict__ aq,
+                                              const uint8_t* __restrict__ asf,
+                                              uint8_t* __restrict__ b0, uint8_t* __restrict__ b1) {
+  using C = Cfg<BN, BM, WN, WM>;
+  NVFP4_LOAD_CONSTS;
+  NVFP4_ISSUE(0, b0, -1);
+  if (nks > 1) NVFP4_ISSUE(1, b1, -1);
+}
+
+// Waits for stage 0 (in b0; stages 0 and 1 are the last loads issued, later
+// vector memory operations are stores), synchronises the block and decodes
+// step 0.
 template <int BN, int BM, int WN, int WM, int JV>
-__device__ __forceinline__ void k_prologue(KState<BN, BM, WN, WM, JV>& st, int nks, int wave,
-                                           const uint32_t* coff, const uint32_t* soff,
-                                           const uint8_t* __restrict__ wq,
-                                           const uint8_t* __restrict__ wsf,
-                                           const uint8_t* __restrict__ aq,
-                                           const uint8_t* __restrict__ asf,
-                                           uint8_t* __restrict__ b0, uint8_t* __restrict__ b1) {
+__device__ __forceinline__ void k_begin(KState<BN, BM, WN, WM, JV>& st, int nks,
+                                        const uint8_t* __restrict__ b0) {
   using C = Cfg<BN, BM, WN, WM>;
   constexpr int FN = C::FN, TN = C::TN, TM = C::TM;
-  NVFP4_LOAD_CONSTS;
   static_assert(C::LOADS == 12 && kLoadsBeforeBarrier == 8, "vmcnt immediates assume 12 loads per stage");
-  NVFP4_ISSUE(0, b0, -1);
-  if (nks > 1) {
-    NVFP4_ISSUE(1, b1, -1);
-    asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
-  } else {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  }
+  if (nks > 1) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   stage_barrier();
   NVFP4_READ_HALF(b0, 0, st.fa, st.ta);
   NVFP4_READ_SF(b0, st.wsr, st.tsr);
@@ -372,56 +378,107 @@ __device__ __forceinline__ void k_stage(KState<BN, BM, WN, WM, JV>& st, int ks, 
 #undef NVFP4_MFMAS
 #undef NVFP4_INTERLEAVE
 
-// One tile: the K loop and the epilogue.  JV = number of 32-token column
-// blocks that hold rows (1..FM); the rest are skipped.
-template <int BN, int BM, int WN, int WM, int EPI, int JV>
-__device__ __forceinline__ void run_tile(const Params& p, uint8_t* smem, int e, int row0,
-                                         int nrows, int64_t n0) {
-  using C = Cfg<BN, BM, WN, WM>;
-  constexpr int FN = C::FN, FM = C::FM, TN = C::TN, TM = C::TM;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wn = wave % WN, wm = wave / WN;
-  const int hf = lane >> 5, l32 = lane & 31;
-  const int64_t N = p.N, K = p.K;
-  const uint32_t kb = (uint32_t)(K / 2), ksf = (uint32_t)(K / 16);
-  // packed weights: tile (e, n0 / BN) is S stages of BN rows (64 code bytes
-  // and 8 scale bytes per row), rows zero-padded to a multiple of BN
-  const int64_t Np = (N + BN - 1) / BN * BN;
-  const uint8_t* wbase = p.b_q + ((int64_t)e * Np + n0) * kb;
-  const uint8_t* wsbase = p.b_sf + ((int64_t)e * Np + n0) * ksf;
+// A tile: expert e, rows [row0, row0 + nrows) of the expert-ordered M
+// dimension, weight rows [n0, n0 + BN), jv occupied 32-token column blocks.
+struct Tile {
+  int e, row0, nrows, jv;
+  int64_t n0;
+};
 
-  KState<BN, BM, WN, WM, JV> st;
-  st.wn = wn; st.wm = wm; st.hf = hf; st.l32 = l32;
+// Tile number `logical` of the expert-ordered tile list (m tiles of BM rows,
+// n tiles innermost); false past the end.  tprefix: per-expert m-tile prefix.
+template <int BN, int BM>
+__device__ __forceinline__ bool tile_at(const Params& p, const int* tprefix, int logical,
+                                        Tile& t) {
+  const int mt = logical / p.n_tiles;
+  if (mt >= tprefix[p.E]) return false;
+  const int nt = logical - mt * p.n_tiles;
+  // expert owning m tile mt: the largest e with tprefix[e] <= mt
+  int lo = 0, hi = p.E - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (tprefix[mid] <= mt) lo = mid; else hi = mid - 1;
+  }
+  // the fields are wave-uniform: readfirstlane keeps them in scalar registers
+  t.e = __builtin_amdgcn_readfirstlane(lo);
+  t.row0 = __builtin_amdgcn_readfirstlane(p.offsets[t.e] + (mt - tprefix[t.e]) * BM);
+  t.nrows = __builtin_amdgcn_readfirstlane(min(BM, p.offsets[t.e + 1] - t.row0));
+  t.n0 = (int64_t)__builtin_amdgcn_readfirstlane(nt) * BN;
+  t.jv = (t.nrows + 31) / 32;
+  return true;
+}
+
+// packed weights: tile (e, n0 / BN) is K/BK stages of BN rows (64 code bytes
+// and 8 scale bytes per row), rows zero-padded to a multiple of BN
+template <int BN>
+__device__ __forceinline__ const uint8_t* tile_wq(const Params& p, const Tile& t) {
+  const int64_t Np = (p.N + BN - 1) / BN * BN;
+  return p.b_q + ((int64_t)t.e * Np + t.n0) * (p.K / 2);
+}
+template <int BN>
+__device__ __forceinline__ const uint8_t* tile_wsf(const Params& p, const Tile& t) {
+  const int64_t Np = (p.N + BN - 1) / BN * BN;
+  return p.b_sf + ((int64_t)t.e * Np + t.n0) * (p.K / 16);
+}
+
+// Per-lane byte offsets (stage 0) of this wave's direct loads for tile t.
+template <int BN, int BM, int WN, int WM, int EPI>
+__device__ __forceinline__ void tile_offsets(const Params& p, const Tile& t, int wave, int lane,
+                                             uint32_t* coff, uint32_t* soff) {
+  using C = Cfg<BN, BM, WN, WM>;
+  const uint32_t kb = (uint32_t)(p.K / 2), ksf = (uint32_t)(p.K / 16);
   // physical weight row (within the tile) held by LDS row r
   auto wrow = [&](int r) -> int {
     return (EPI == NVFP4_EPI_SWIGLU_NVFP4) ? ((r & ~31) | swiglu_phys_row(r & 31)) : r;
   };
   // token row of LDS row BN + i: clamped to the tile's last row, gathered
   auto trow = [&](int i) -> uint32_t {
-    const int d = row0 + (i < nrows ? i : nrows - 1);
+    const int d = t.row0 + (i < t.nrows ? i : t.nrows - 1);
     return (uint32_t)(p.a_row_src ? p.a_row_src[d] / p.a_row_div : d);
   };
-  // per-lane byte offsets of this wave's direct loads (stage 0)
-  uint32_t coff[C::CODE_LOADS], soff[C::SF_LOADS];
 #pragma unroll
   for (int c = 0; c < C::CODE_LOADS; ++c) {
     const int g = c * C::NW + wave;                // 16-row group
     const int r = 16 * g + (lane >> 2);
     const int q = chunk_pos(r, lane & 3);          // logical chunk stored at this lane's position
     coff[c] = (c < C::CODE_LOADS_W) ? (uint32_t)(wrow(r) * ROW_BYTES + 16 * q)
-                                       : trow(r - BN) * kb + 16 * q;
+                                    : trow(r - BN) * kb + 16 * q;
   }
 #pragma unroll
   for (int c = 0; c < C::SF_LOADS_W; ++c) {      // 2 consecutive rows per lane
     const int r = 128 * (c * C::NW + wave) + 2 * lane;
-    soff[c] = (uint32_t)(wrow(r) * SF_BYTES);   // wrow(r + 1) == wrow(r) + 1 (r even)
+    soff[c] = (uint32_t)(wrow(r) * SF_BYTES);      // wrow(r + 1) == wrow(r) + 1 (r even)
   }
 #pragma unroll
   for (int c = 0; c < C::SF_LOADS_T; ++c) {      // one 4-byte half row per lane
     const int i = 32 * (c * C::NW + wave) + (lane >> 1);
     soff[C::SF_LOADS_W + c] = trow(i) * ksf + 4 * (lane & 1);
   }
+}
+
+// One tile: the K loop and the epilogue.  JV = number of 32-token column
+// blocks that hold rows (1..FM); the rest are skipped.  Stages 0 and 1 of
+// the tile were issued by the caller with the load offsets coff/soff; after
+// the K loop the stages 0 and 1 of the next tile (if any) are issued, with
+// coff/soff rewritten for it, so that their latency overlaps the epilogue.
+template <int BN, int BM, int WN, int WM, int EPI, int JV>
+__device__ __forceinline__ void run_tile(const Params& p, uint8_t* smem, const Tile& cur,
+                                         uint32_t* coff, uint32_t* soff, const Tile& nxt,
+                                         bool has_next) {
+  using C = Cfg<BN, BM, WN, WM>;
+  constexpr int FN = C::FN, FM = C::FM, TN = C::TN, TM = C::TM;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wn = wave % WN, wm = wave / WN;
+  const int hf = lane >> 5, l32 = lane & 31;
+  const int64_t N = p.N, K = p.K;
+  const int e = cur.e, row0 = cur.row0, nrows = cur.nrows;
+  const int64_t n0 = cur.n0;
+  const uint8_t* wbase = tile_wq<BN>(p, cur);
+  const uint8_t* wsbase = tile_wsf<BN>(p, cur);
+
+  KState<BN, BM, WN, WM, JV> st;
+  st.wn = wn; st.wm = wm; st.hf = hf; st.l32 = l32;
 #pragma unroll
   for (int i = 0; i < FN; ++i)
 #pragma unroll
@@ -431,7 +488,7 @@ __device__ __forceinline__ void run_tile(const Params& p, uint8_t* smem, int e, 
 
   // three LDS stage buffers, stage ks in buffer ks % 3
   const int nks = (int)(K / BK);
-  k_prologue(st, nks, wave, coff, soff, wbase, wsbase, p.a_q, p.a_sf, smem, smem + C::STAGE_BYTES);
+  k_begin(st, nks, smem);
   int buf = 0;
   int ks = 0;
   for (; ks + 2 < nks; ++ks) {
@@ -449,45 +506,47 @@ __device__ __forceinline__ void run_tile(const Params& p, uint8_t* smem, int e, 
     buf = buf1;
   }
   float16v (&acc)[FN][FM] = st.acc;
-  __syncthreads();   // every wave is done with the stage buffers (the epilogue reuses LDS)
+  __syncthreads();   // every wave is done with the stage buffers
+  // Lane index values for the code after the K loop, from an opaque copy:
+  // the compiler cannot compute them (and their addresses) before the loop
+  // and keep them live across it, which would spill.
+  int lane_x = lane;
+  asm volatile("" : "+v"(lane_x));
+  {
+  const int lane = lane_x, hf = lane_x >> 5, l32 = lane_x & 31;
+  if (has_next) {
+    tile_offsets<BN, BM, WN, WM, EPI>(p, nxt, wave, lane, coff, soff);
+    k_issue_first<BN, BM, WN, WM>(nks, wave, coff, soff, tile_wq<BN>(p, nxt), tile_wsf<BN>(p, nxt),
+                                  p.a_q, p.a_sf, smem, smem + C::STAGE_BYTES);
+  }
 
   // ---- epilogue
   const float alpha = 1.0f / (p.gs_a[0] * p.gs_b[e]);
   if constexpr (EPI == NVFP4_EPI_BF16) {
-    // stage the wave's TN x TM tile in LDS as token rows of TN bf16 (a
-    // 256-byte pitch, 16-byte chunk q of row t stored at q ^ (t & 15)), then
-    // write each token row with 16-byte stores
-    constexpr int PITCH = TN * 2;
-    static_assert(PITCH == 256, "the chunk swizzle assumes 16 chunks per row");
-    static_assert(C::NW * TM * PITCH <= C::LDS_BYTES, "epilogue tile must fit the stage buffers");
-    uint8_t* tile = smem + wave * TM * PITCH;
+    // Each lane holds, for token j*32 + l32, output columns 32i + 8g + 4hf
+    // .. +3 of the wave's TN: 8 contiguous bytes per (i, g).  The two lane
+    // halves write 16 contiguous bytes of a token row per store and the four
+    // g stores its 64 bytes of block i, which L2 merges before write-back.
+    // No LDS: buffers 0 and 1 may be receiving the next tile.
+    const int64_t nw0 = n0 + wn * TN;
 #pragma unroll
     for (int j = 0; j < JV; ++j) {
       const int tok = j * 32 + l32;
+      uint16_t* crow = p.c_bf16 + (int64_t)(row0 + tok) * N + nw0 + 4 * hf;
 #pragma unroll
       for (int i = 0; i < FN; ++i) {
+        // one 32 x 32 block at a time: the scheduler would otherwise copy
+        // all accumulators out of the AGPRs at once and spill
+        __builtin_amdgcn_sched_barrier(0);
+        if (tok >= nrows || nw0 + i * 32 >= N) continue;   // N % 32 == 0
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           uint2 o;
-          o.x = f32_to_bf16_rne(acc[i][j][4 * g + 0] * alpha) |
-                (f32_to_bf16_rne(acc[i][j][4 * g + 1] * alpha) << 16);
-          o.y = f32_to_bf16_rne(acc[i][j][4 * g + 2] * alpha) |
-                (f32_to_bf16_rne(acc[i][j][4 * g + 3] * alpha) << 16);
-          const int cb = (i * 32 + 8 * g + 4 * hf) * 2;          // byte column
-          *reinterpret_cast<uint2*>(tile + tok * PITCH + (((cb >> 4) ^ (tok & 15)) << 4) + (cb & 15)) = o;
+          o.x = pack_bf16x2(acc[i][j][4 * g + 0] * alpha, acc[i][j][4 * g + 1] * alpha);
+          o.y = pack_bf16x2(acc[i][j][4 * g + 2] * alpha, acc[i][j][4 * g + 3] * alpha);
+          *reinterpret_cast<uint2*>(crow + i * 32 + 8 * g) = o;
         }
       }
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    __builtin_amdgcn_wave_barrier();
-    // 16 lanes cover one token row (TN bf16 = 256 bytes); 4 rows per instruction
-    const int64_t nw0 = n0 + wn * TN;
-    const int col = (lane & 15) * 8;           // bf16 column within the wave's TN
-    const bool col_ok = nw0 + col < N;         // N % 32 == 0: a 16-byte piece is all in or out
-    for (int t = lane >> 4; t < JV * 32; t += 4) {
-      if (t >= nrows || !col_ok) continue;
-      const uint4 v = *reinterpret_cast<const uint4*>(tile + t * PITCH + (((lane & 15) ^ (t & 15)) << 4));
-      *reinterpret_cast<uint4*>(p.c_bf16 + (int64_t)(row0 + t) * N + nw0 + col) = v;
     }
   } else {
     const float gs_h = p.gs_out[0];
@@ -499,6 +558,8 @@ __device__ __forceinline__ void run_tile(const Params& p, uint8_t* smem, int e, 
       const int64_t hb = nb / 32;
 #pragma unroll
       for (int j = 0; j < JV; ++j) {
+        // one 32 x 32 block at a time (see the BF16 epilogue)
+        __builtin_amdgcn_sched_barrier(0);
         const int tok = wm * TM + j * 32 + l32;
         float h[8];
 #pragma unroll
@@ -506,7 +567,8 @@ __device__ __forceinline__ void run_tile(const Params& p, uint8_t* smem, int e, 
           const int gi = (q < 4) ? q : 8 + (q - 4);      // gate register; up is gi + 4
           const float g = acc[i][j][gi] * alpha;
           const float u = acc[i][j][gi + 4] * alpha;
-          h[q] = (g / (1.0f + __expf(-g))) * u;
+          // silu(g) * u; v_rcp_f32 (1 ulp) in place of an IEEE division
+          h[q] = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
         }
         // block amax over 16 h columns: 8 in this lane, 8 in lane l^32
         float m = 0.0f;
@@ -542,6 +604,7 @@ __device__ __forceinline__ void run_tile(const Params& p, uint8_t* smem, int e, 
       }
     }
   }
+  }
 }
 
 template <int BN, int BM, int WN, int WM, int EPI>
@@ -575,35 +638,33 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_gemm_kernel(Params p)
     if (tid == C::NT - 1) tprefix[E] = s_scan[C::NT - 1];
     __syncthreads();
   }
-  const int total_m = tprefix[p.E];
   const int G = gridDim.x;                 // a multiple of 8
   const int slice = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
-  for (int base = 0;; base += G) {
-    const int logical = base + slice;
-    const int mt = logical / p.n_tiles;
-    if (mt >= total_m) break;
-    const int nt = logical - mt * p.n_tiles;
-    // expert owning m tile mt: the largest e with tprefix[e] <= mt
-    int lo = 0, hi = p.E - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (tprefix[mid] <= mt) lo = mid; else hi = mid - 1;
-    }
-    const int e = lo;
-    const int row0 = p.offsets[e] + (mt - tprefix[e]) * BM;
-    const int nrows = min(BM, p.offsets[e + 1] - row0);
-    const int64_t n0 = (int64_t)nt * BN;
-    const int jv = (nrows + 31) / 32;      // occupied 32-token column blocks
-    if (jv >= C::FM) {
-      run_tile<BN, BM, WN, WM, EPI, C::FM>(p, smem, e, row0, nrows, n0);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int nks = (int)(p.K / BK);
+  Tile cur;
+  bool have = tile_at<BN, BM>(p, tprefix, slice, cur);
+  uint32_t coff[C::CODE_LOADS], soff[C::SF_LOADS];
+  if (have) {
+    tile_offsets<BN, BM, WN, WM, EPI>(p, cur, wave, lane, coff, soff);
+    k_issue_first<BN, BM, WN, WM>(nks, wave, coff, soff, tile_wq<BN>(p, cur), tile_wsf<BN>(p, cur),
+                                  p.a_q, p.a_sf, smem, smem + C::STAGE_BYTES);
+  }
+  for (int logical = slice; have; logical += G) {
+    // the next tile is found before this one runs (its fields are scalars)
+    Tile nxt;
+    const bool more = tile_at<BN, BM>(p, tprefix, logical + G, nxt);
+    if (cur.jv >= C::FM) {
+      run_tile<BN, BM, WN, WM, EPI, C::FM>(p, smem, cur, coff, soff, nxt, more);
     } else if constexpr (C::FM > 1) {
-      if (jv == 1) run_tile<BN, BM, WN, WM, EPI, 1>(p, smem, e, row0, nrows, n0);
+      if (cur.jv == 1) run_tile<BN, BM, WN, WM, EPI, 1>(p, smem, cur, coff, soff, nxt, more);
       else if constexpr (C::FM > 2) {
-        if (jv == 2) run_tile<BN, BM, WN, WM, EPI, 2>(p, smem, e, row0, nrows, n0);
-        else if constexpr (C::FM > 3) run_tile<BN, BM, WN, WM, EPI, 3>(p, smem, e, row0, nrows, n0);
+        if (cur.jv == 2) run_tile<BN, BM, WN, WM, EPI, 2>(p, smem, cur, coff, soff, nxt, more);
+        else if constexpr (C::FM > 3) run_tile<BN, BM, WN, WM, EPI, 3>(p, smem, cur, coff, soff, nxt, more);
       }
     }
-    __syncthreads();
+    cur = nxt;
+    have = more;
   }
 }
 

@@ -199,3 +199,35 @@ def test_pack_weights_layout(E, N, K):
     torch.cuda.synchronize()
     rq, rs = _pack_reference(host(q), host(sf))
     assert np.array_equal(host(pw.q), rq) and np.array_equal(host(pw.sf), rs)
+
+
+def test_combine_rounding_exact_ties():
+    # Every product and two-term sum below is exact in fp32 (powers-of-two
+    # weights, addends within 2^-13 of each other's exponent), so the GPU's
+    # fp32 accumulation and the oracle's fp64 one agree before rounding; the
+    # second addend is a multiple of a quarter bf16 ulp of the first, so many
+    # sums fall exactly halfway between two bf16 values and the output bits
+    # pin round-to-nearest-even.
+    rng = np.random.default_rng(11)
+    T, H, k = 512, 64, 2
+    sign = rng.choice([-1.0, 1.0], size=(T * k, H))
+    mant = 1.0 + rng.integers(0, 128, size=(T * k, H)) / 128.0     # bf16 mantissas
+    expo = rng.integers(-20, 20, size=(T * k, H))
+    y = (sign * mant * np.exp2(expo)).astype(np.float32)
+    # slot 1 rows: a quarter-ulp multiple of the slot 0 row of the same token
+    base = y.reshape(T, k, H)[:, 0, :]
+    ulp4 = np.exp2(np.floor(np.log2(np.abs(base))) - 9)
+    y.reshape(T, k, H)[:, 1, :] = (rng.integers(-8, 9, size=(T, H)) * ulp4).astype(np.float32)
+    y_bits = (y.view(np.uint32) >> 16).astype(np.uint16)
+    assert np.array_equal((y_bits.astype(np.uint32) << 16).view(np.float32), y)   # exact bf16
+    w = np.ones((T, k), np.float32)
+    inv_perm = np.arange(T * k, dtype=np.int32)
+    out = nv.moe_combine(_bits_to_dev(y_bits), torch.from_numpy(inv_perm).to(DEV),
+                         torch.from_numpy(w).to(DEV),
+                         torch.tensor([0, T * k], dtype=torch.int32, device=DEV))
+    from oracle import moe as O
+    ref = O.combine(y_bits, inv_perm, w, T * k)
+    exact = base.astype(np.float64) + y.reshape(T, k, H)[:, 1, :].astype(np.float64)
+    r16 = (exact.astype(np.float32).view(np.uint32) & 0xFFFF)
+    assert (r16 == 0x8000).sum() > 100                # many exact ties exercised
+    assert np.array_equal(host(out).view(np.uint16), ref)
