@@ -167,10 +167,15 @@ nvfp4_status nvfp4_moe_route(const int32_t* topk_ids, int64_t T, int k, int E,
  * Shapes: E >= 1, M >= 0, K % 128 == 0, K >= 128, N % 32 == 0, N >= 32;
  *   SwiGLU: N % 32 == 0 (I % 16 == 0).
  * Unused output pointers of the other epilogue may be NULL.
- * Workspace: none (ws may be NULL; ws_bytes ignored).
+ * Workspace: nvfp4_grouped_gemm_workspace_size() bytes, 4-byte aligned,
+ *   caller-owned: the tile scheduler's counters.  Each call first zeroes
+ *   them (a small kernel on `stream`), so the contents need no set-up;
+ *   calls that share a workspace must be ordered on one stream.  May be
+ *   NULL only when M == 0.
  * ---------------------------------------------------------------------- */
 #define NVFP4_EPI_BF16 0
 #define NVFP4_EPI_SWIGLU_NVFP4 1
+size_t nvfp4_grouped_gemm_workspace_size(void);
 nvfp4_status nvfp4_grouped_gemm(int epilogue, const uint8_t* a_q, const uint8_t* a_sf,
                                 const float* gs_a, const int32_t* a_row_src, int a_row_div,
                                 const int32_t* expert_offsets, int E, int64_t M, int64_t N,

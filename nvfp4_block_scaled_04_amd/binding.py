@@ -39,6 +39,7 @@ SIGNATURES = {
     "nvfp4_moe_route_workspace_size": (c_size_t, [c_int64, c_int, c_int]),
     "nvfp4_moe_route": (c_int, [c_void_p, c_int64, c_int, c_int, c_void_p, c_void_p, c_void_p,
                                 c_void_p, c_void_p, c_size_t, c_void_p]),
+    "nvfp4_grouped_gemm_workspace_size": (c_size_t, []),
     "nvfp4_grouped_gemm": (c_int, [c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_void_p,
                                    c_int, c_int64, c_int64, c_int64, c_void_p, c_void_p, c_void_p,
                                    c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
@@ -190,11 +191,17 @@ def moe_route(topk_ids, E):
     return off, perm, inv, bad
 
 
+def gemm_workspace_bytes():
+    """Workspace bytes nvfp4_grouped_gemm needs (the tile scheduler's counters)."""
+    return int(lib().nvfp4_grouped_gemm_workspace_size())
+
+
 def grouped_gemm(epilogue, a_q, a_sf, gs_a, offsets, b: PackedWeight, gs_b, M, a_row_src=None,
-                 a_row_div=1, gs_out=None, debug=False, out=None):
+                 a_row_div=1, gs_out=None, debug=False, out=None, workspace=None):
     """Expert-grouped NVFP4 GEMM with packed B.  BF16 epilogue returns c (M, N)
     bf16; the SwiGLU epilogue returns (c_q (M, N/4), c_sf (M, N/32), h f32
-    (M, N/2) or None)."""
+    (M, N/2) or None).  workspace: uint8 tensor of at least
+    gemm_workspace_bytes() (allocated here when None)."""
     E, N, K = b.E, b.N, b.K
     dev = b.q.device
     _dev(a_q, torch.uint8, "a_q")
@@ -219,10 +226,13 @@ def grouped_gemm(epilogue, a_q, a_sf, gs_a, offsets, b: PackedWeight, gs_b, M, a
             c_sf = torch.empty((M, I // 16), dtype=torch.uint8, device=dev)
             dbg = torch.empty((M, I), dtype=torch.float32, device=dev) if debug else None
         _dev(gs_out, torch.float32, "gs_out")
+    ws = workspace if workspace is not None else torch.empty(gemm_workspace_bytes(), dtype=torch.uint8,
+                                                             device=dev)
+    _dev(ws, torch.uint8, "workspace")
     _check(lib().nvfp4_grouped_gemm(epilogue, _ptr(a_q), _ptr(a_sf), _ptr(gs_a), _ptr(a_row_src),
                                     a_row_div, _ptr(offsets), E, M, N, K, _ptr(b.q), _ptr(b.sf),
                                     _ptr(gs_b), _ptr(gs_out), _ptr(c), _ptr(c_q), _ptr(c_sf),
-                                    _ptr(dbg), None, 0, _stream(dev)), "nvfp4_grouped_gemm")
+                                    _ptr(dbg), _ptr(ws), ws.numel(), _stream(dev)), "nvfp4_grouped_gemm")
     return c if epilogue == EPI_BF16 else (c_q, c_sf, dbg)
 
 

@@ -98,6 +98,9 @@ nvfp4_status check_gemm(const nvfp4::GemmArgs& a) {
   if (a.N < 32 || a.N % 32) return fail(NVFP4_ERR_SHAPE, "N must be a positive multiple of 32 (got %lld)", (long long)a.N);
   if (a.N >= (int64_t(1) << 30) || a.K >= (int64_t(1) << 30)) return fail(NVFP4_ERR_SHAPE, "N and K must be < 2^30");
   if (a.a_row_src && a.a_row_div < 1) return fail(NVFP4_ERR_SHAPE, "a_row_div must be >= 1");
+  // tile indices are 32-bit: (M/128 + E) m tiles times N/512 n tiles
+  if (((a.M + 127) / 128 + a.E) * ((a.N + 511) / 512) >= (int64_t(1) << 31))
+    return fail(NVFP4_ERR_SHAPE, "too many GEMM tiles (M, N too large)");
   if (!a.offsets) return fail(NVFP4_ERR_INVALID_ARG, "expert_offsets is NULL");
   if (a.M == 0) return NVFP4_OK;
   if (!a.a_q || !a.a_sf || !a.gs_a || !a.b_q || !a.b_sf || !a.gs_b)
@@ -127,7 +130,7 @@ nvfp4_status check_combine(const void* y, const int32_t* inv, const float* w, co
 }
 
 struct FwdLayout {
-  size_t a_q, a_sf, gs_a, qws, off, perm, inv, bad, rws, h_q, h_sf, y, total;
+  size_t a_q, a_sf, gs_a, qws, off, perm, inv, bad, rws, gws, h_q, h_sf, y, total;
 };
 
 FwdLayout fwd_layout(int64_t T, int64_t H, int64_t I, int E, int k) {
@@ -144,6 +147,7 @@ FwdLayout fwd_layout(int64_t T, int64_t H, int64_t I, int E, int k) {
   L.inv = take(sizeof(int32_t) * (size_t)M);
   L.bad = take(sizeof(int32_t));
   L.rws = take(nvfp4::route_ws_bytes(T, k, E));
+  L.gws = take(nvfp4::kGemmWorkspaceBytes);
   L.h_q = take((size_t)(M * I / 2));
   L.h_sf = take((size_t)(M * I / 16));
   L.y = take((size_t)(M * H * 2));
@@ -256,6 +260,8 @@ nvfp4_status nvfp4_moe_route(const int32_t* topk_ids, int64_t T, int k, int E,
                 "nvfp4_moe_route launch");
 }
 
+size_t nvfp4_grouped_gemm_workspace_size(void) { return nvfp4::kGemmWorkspaceBytes; }
+
 nvfp4_status nvfp4_grouped_gemm(int epilogue, const uint8_t* a_q, const uint8_t* a_sf,
                                 const float* gs_a, const int32_t* a_row_src, int a_row_div,
                                 const int32_t* expert_offsets, int E, int64_t M, int64_t N,
@@ -263,13 +269,15 @@ nvfp4_status nvfp4_grouped_gemm(int epilogue, const uint8_t* a_q, const uint8_t*
                                 const float* gs_b, const float* gs_out, void* c_bf16,
                                 uint8_t* c_q, uint8_t* c_sf, float* c_debug_f32, void* ws,
                                 size_t ws_bytes, void* stream) {
-  (void)ws;
-  (void)ws_bytes;
   nvfp4::GemmArgs a{epilogue, a_q, a_sf, gs_a, a_row_src, a_row_div, expert_offsets, E, M, N, K,
-                    b_q, b_sf, gs_b, gs_out, c_bf16, c_q, c_sf, c_debug_f32};
+                    b_q, b_sf, gs_b, gs_out, c_bf16, c_q, c_sf, c_debug_f32, ws};
   nvfp4_status st = check_gemm(a);
   if (st != NVFP4_OK) return st;
   if (M == 0) return NVFP4_OK;
+  if (ws == nullptr || ws_bytes < nvfp4::kGemmWorkspaceBytes)
+    return fail(NVFP4_ERR_WORKSPACE, "grouped GEMM needs %zu workspace bytes (got %zu)",
+                nvfp4::kGemmWorkspaceBytes, ws_bytes);
+  if (!aligned(ws, 4)) return fail(NVFP4_ERR_WORKSPACE, "workspace must be 4-byte aligned");
   st = check_arch();
   if (st != NVFP4_OK) return st;
   return finish(nvfp4::launch_grouped_gemm(a, static_cast<hipStream_t>(stream)),
@@ -350,11 +358,11 @@ nvfp4_status moe_expert_forward(const void* x_bf16, int64_t T, int64_t H, int64_
   if (err != hipSuccess) return hip_fail(err, "moe_expert_forward route");
   if (M > 0) {
     nvfp4::GemmArgs l1{NVFP4_EPI_SWIGLU_NVFP4, a_q, a_sf, gs_a, perm, k, off, E, M, 2 * I, H,
-                       w1_q, w1_sf, gs_w1, gs_h, nullptr, h_q, h_sf, tp.h_f32};
+                       w1_q, w1_sf, gs_w1, gs_h, nullptr, h_q, h_sf, tp.h_f32, base + L.gws};
     err = nvfp4::launch_grouped_gemm(l1, s);
     if (err != hipSuccess) return hip_fail(err, "moe_expert_forward L1");
     nvfp4::GemmArgs l2{NVFP4_EPI_BF16, h_q, h_sf, gs_h, nullptr, 1, off, E, M, H, I,
-                       w2_q, w2_sf, gs_w2, nullptr, y, nullptr, nullptr, nullptr};
+                       w2_q, w2_sf, gs_w2, nullptr, y, nullptr, nullptr, nullptr, base + L.gws};
     err = nvfp4::launch_grouped_gemm(l2, s);
     if (err != hipSuccess) return hip_fail(err, "moe_expert_forward L2");
   }

@@ -75,6 +75,7 @@ struct Params {
   uint8_t* c_q;
   uint8_t* c_sf;
   float* c_debug;
+  int* sched;       // per-XCD tile counters (8), zero at launch
   int n_tiles;
 };
 
@@ -385,28 +386,38 @@ struct Tile {
   int64_t n0;
 };
 
-// Tile number `logical` of the expert-ordered tile list (m tiles of BM rows,
-// n tiles innermost); false past the end.  tprefix: per-expert m-tile prefix.
+// Tile number `logical` (< number of tiles) of the expert-ordered tile list
+// (m tiles of BM rows, n tiles innermost).  tprefix: per-expert m-tile
+// prefix (E <= 4096).  The fields are wave-uniform: readfirstlane keeps them
+// in scalar registers.
 template <int BN, int BM>
-__device__ __forceinline__ bool tile_at(const Params& p, const int* tprefix, int logical,
-                                        Tile& t) {
+__device__ __forceinline__ void tile_at(const Params& p, const int* tprefix, int logical, Tile& t) {
   const int mt = logical / p.n_tiles;
-  if (mt >= tprefix[p.E]) return false;
   const int nt = logical - mt * p.n_tiles;
-  // expert owning m tile mt: the largest e with tprefix[e] <= mt
-  int lo = 0, hi = p.E - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (tprefix[mid] <= mt) lo = mid; else hi = mid - 1;
-  }
-  // the fields are wave-uniform: readfirstlane keeps them in scalar registers
-  t.e = __builtin_amdgcn_readfirstlane(lo);
+  // expert owning m tile mt: the largest e with tprefix[e] <= mt (fixed
+  // steps, no loop: tprefix is non-decreasing and tprefix[0] = 0)
+  int e = 0;
+#pragma unroll
+  for (int step = 2048; step > 0; step >>= 1)
+    if (e + step < p.E && tprefix[e + step] <= mt) e += step;
+  t.e = __builtin_amdgcn_readfirstlane(e);
   t.row0 = __builtin_amdgcn_readfirstlane(p.offsets[t.e] + (mt - tprefix[t.e]) * BM);
   t.nrows = __builtin_amdgcn_readfirstlane(min(BM, p.offsets[t.e + 1] - t.row0));
   t.n0 = (int64_t)__builtin_amdgcn_readfirstlane(nt) * BN;
   t.jv = (t.nrows + 31) / 32;
-  return true;
 }
+
+// Tile scheduling.  XCD x (blocks b with b % 8 == x) owns tiles [lo, hi),
+// an eighth of the list, contiguous so that an expert's tiles share one L2;
+// its blocks claim tiles dynamically from counter sched[x].  Thread 0 of a
+// block claims the tile after its next one right before it issues the next
+// tile's loads; the claim is published through LDS at the following
+// post-K-loop barrier, when every earlier load has completed.
+struct Sched {
+  int lo, hi;       // this XCD's tile range
+  int* counter;
+  int* s_claim;     // LDS slot for the pending claim
+};
 
 // packed weights: tile (e, n0 / BN) is K/BK stages of BN rows (64 code bytes
 // and 8 scale bytes per row), rows zero-padded to a multiple of BN
@@ -462,9 +473,9 @@ __device__ __forceinline__ void tile_offsets(const Params& p, const Tile& t, int
 // the K loop the stages 0 and 1 of the next tile (if any) are issued, with
 // coff/soff rewritten for it, so that their latency overlaps the epilogue.
 template <int BN, int BM, int WN, int WM, int EPI, int JV>
-__device__ __forceinline__ void run_tile(const Params& p, uint8_t* smem, const Tile& cur,
-                                         uint32_t* coff, uint32_t* soff, const Tile& nxt,
-                                         bool has_next) {
+__device__ __forceinline__ bool run_tile(const Params& p, uint8_t* smem, const int* tprefix,
+                                         const Sched& sc, const Tile& cur, uint32_t* coff,
+                                         uint32_t* soff, int& claim, Tile& nxt) {
   using C = Cfg<BN, BM, WN, WM>;
   constexpr int FN = C::FN, FM = C::FM, TN = C::TN, TM = C::TM;
   const int tid = threadIdx.x;
@@ -506,15 +517,21 @@ __device__ __forceinline__ void run_tile(const Params& p, uint8_t* smem, const T
     buf = buf1;
   }
   float16v (&acc)[FN][FM] = st.acc;
+  // the last stage waited for every load, the pending claim included
+  if (tid == 0) *sc.s_claim = claim;
   __syncthreads();   // every wave is done with the stage buffers
   // Lane index values for the code after the K loop, from an opaque copy:
   // the compiler cannot compute them (and their addresses) before the loop
   // and keep them live across it, which would spill.
   int lane_x = lane;
   asm volatile("" : "+v"(lane_x));
+  const int t_next = sc.lo + __builtin_amdgcn_readfirstlane(*sc.s_claim);
+  const bool has_next = t_next < sc.hi;
+  if (has_next) tile_at<BN, BM>(p, tprefix, t_next, nxt);
   {
   const int lane = lane_x, hf = lane_x >> 5, l32 = lane_x & 31;
   if (has_next) {
+    if (tid == 0) claim = atomicAdd(sc.counter, 1);
     tile_offsets<BN, BM, WN, WM, EPI>(p, nxt, wave, lane, coff, soff);
     k_issue_first<BN, BM, WN, WM>(nks, wave, coff, soff, tile_wq<BN>(p, nxt), tile_wsf<BN>(p, nxt),
                                   p.a_q, p.a_sf, smem, smem + C::STAGE_BYTES);
@@ -605,6 +622,7 @@ __device__ __forceinline__ void run_tile(const Params& p, uint8_t* smem, const T
     }
   }
   }
+  return has_next;
 }
 
 template <int BN, int BM, int WN, int WM, int EPI>
@@ -638,34 +656,51 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_gemm_kernel(Params p)
     if (tid == C::NT - 1) tprefix[E] = s_scan[C::NT - 1];
     __syncthreads();
   }
-  const int G = gridDim.x;                 // a multiple of 8
-  const int slice = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+  __shared__ int s_claim[2];
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int nks = (int)(p.K / BK);
+  const int x = blockIdx.x & 7;                  // XCD (blocks are dispatched round-robin)
+  const int64_t total = (int64_t)tprefix[p.E] * p.n_tiles;
+  Sched sc;
+  sc.lo = (int)((total * x) >> 3);
+  sc.hi = (int)((total * (x + 1)) >> 3);
+  sc.counter = p.sched + x;
+  sc.s_claim = s_claim;
+  if (tid == 0) {
+    s_claim[0] = atomicAdd(sc.counter, 1);
+    s_claim[1] = atomicAdd(sc.counter, 1);
+  }
+  __syncthreads();
+  int claim = s_claim[1];                  // meaningful in thread 0 only
+  const int t0 = sc.lo + __builtin_amdgcn_readfirstlane(s_claim[0]);
+  bool have = t0 < sc.hi;
   Tile cur;
-  bool have = tile_at<BN, BM>(p, tprefix, slice, cur);
   uint32_t coff[C::CODE_LOADS], soff[C::SF_LOADS];
   if (have) {
+    tile_at<BN, BM>(p, tprefix, t0, cur);
     tile_offsets<BN, BM, WN, WM, EPI>(p, cur, wave, lane, coff, soff);
     k_issue_first<BN, BM, WN, WM>(nks, wave, coff, soff, tile_wq<BN>(p, cur), tile_wsf<BN>(p, cur),
                                   p.a_q, p.a_sf, smem, smem + C::STAGE_BYTES);
   }
-  for (int logical = slice; have; logical += G) {
-    // the next tile is found before this one runs (its fields are scalars)
+  while (have) {
     Tile nxt;
-    const bool more = tile_at<BN, BM>(p, tprefix, logical + G, nxt);
+    bool more = false;
     if (cur.jv >= C::FM) {
-      run_tile<BN, BM, WN, WM, EPI, C::FM>(p, smem, cur, coff, soff, nxt, more);
+      more = run_tile<BN, BM, WN, WM, EPI, C::FM>(p, smem, tprefix, sc, cur, coff, soff, claim, nxt);
     } else if constexpr (C::FM > 1) {
-      if (cur.jv == 1) run_tile<BN, BM, WN, WM, EPI, 1>(p, smem, cur, coff, soff, nxt, more);
+      if (cur.jv == 1) more = run_tile<BN, BM, WN, WM, EPI, 1>(p, smem, tprefix, sc, cur, coff, soff, claim, nxt);
       else if constexpr (C::FM > 2) {
-        if (cur.jv == 2) run_tile<BN, BM, WN, WM, EPI, 2>(p, smem, cur, coff, soff, nxt, more);
-        else if constexpr (C::FM > 3) run_tile<BN, BM, WN, WM, EPI, 3>(p, smem, cur, coff, soff, nxt, more);
+        if (cur.jv == 2) more = run_tile<BN, BM, WN, WM, EPI, 2>(p, smem, tprefix, sc, cur, coff, soff, claim, nxt);
+        else if constexpr (C::FM > 3) more = run_tile<BN, BM, WN, WM, EPI, 3>(p, smem, tprefix, sc, cur, coff, soff, claim, nxt);
       }
     }
     cur = nxt;
     have = more;
   }
+}
+
+__global__ void zero_ints_kernel(int* p, int n) {
+  if ((int)threadIdx.x < n) p[threadIdx.x] = 0;
 }
 
 int g_cu_count = 0;
@@ -678,6 +713,7 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
   p.a_row_div = a.a_row_div; p.offsets = a.offsets; p.E = a.E; p.M = a.M; p.N = a.N; p.K = a.K;
   p.b_q = a.b_q; p.b_sf = a.b_sf; p.gs_b = a.gs_b; p.gs_out = a.gs_out;
   p.c_bf16 = static_cast<uint16_t*>(a.c_bf16); p.c_q = a.c_q; p.c_sf = a.c_sf; p.c_debug = a.c_debug;
+  p.sched = static_cast<int*>(a.ws);
   p.n_tiles = (int)((a.N + BN - 1) / BN);
   if (a.M == 0) return hipSuccess;
   if (g_cu_count == 0) {
@@ -702,6 +738,7 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
     if (err != hipSuccess) return err;
     attr_set = true;
   }
+  zero_ints_kernel<<<1, 64, 0, stream>>>(p.sched, 8);   // a kernel, not a memset: graph-safe
   kern<<<(unsigned)grid, C::NT, lds, stream>>>(p);
   return hipGetLastError();
 }

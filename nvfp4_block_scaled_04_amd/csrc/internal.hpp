@@ -54,7 +54,9 @@ struct GemmArgs {
   uint8_t* c_q;
   uint8_t* c_sf;
   float* c_debug;
+  void* ws;         // kGemmWorkspaceBytes: the tile scheduler's counters
 };
+constexpr size_t kGemmWorkspaceBytes = 256;
 hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t stream);
 
 // combine.hip

@@ -83,12 +83,12 @@ def test_route_rejects(L):
 def _gemm(L, **kw):
     a = dict(epi=0, a_q=FAKE, a_sf=FAKE, gs_a=FAKE, src=None, div=1, off=FAKE, E=4, M=64, N=256,
              K=256, b_q=FAKE, b_sf=FAKE, gs_b=FAKE, gs_out=FAKE, c=FAKE, cq=FAKE, csf=FAKE,
-             dbg=None)
+             dbg=None, ws=FAKE, wsb=256)
     a.update(kw)
     return L.nvfp4_grouped_gemm(a["epi"], a["a_q"], a["a_sf"], a["gs_a"], a["src"], a["div"],
                                 a["off"], a["E"], a["M"], a["N"], a["K"], a["b_q"], a["b_sf"],
-                                a["gs_b"], a["gs_out"], a["c"], a["cq"], a["csf"], a["dbg"], None,
-                                0, None)
+                                a["gs_b"], a["gs_out"], a["c"], a["cq"], a["csf"], a["dbg"],
+                                a["ws"], a["wsb"], None)
 
 
 def test_gemm_rejects(L):
@@ -101,6 +101,16 @@ def test_gemm_rejects(L):
     assert _gemm(L, epi=1, cq=None) == -1
     assert _gemm(L, src=FAKE, div=0) == -2
     assert _gemm(L, off=None) == -1
+    assert _gemm(L, M=1 << 30, N=1 << 29) == -2          # tile indices would overflow 32 bits
+
+
+def test_gemm_workspace(L):
+    need = L.nvfp4_grouped_gemm_workspace_size()
+    assert need >= 32                                     # eight 32-bit counters
+    assert _gemm(L, ws=None, wsb=0) == -3
+    assert _gemm(L, wsb=need - 1) == -3
+    assert _gemm(L, ws=FAKE + 2) == -3                    # not 4-byte aligned
+    assert _gemm(L, M=0, ws=None, wsb=0) == 0             # nothing to do, nothing launched
 
 
 def test_combine_and_forward_reject(L):
