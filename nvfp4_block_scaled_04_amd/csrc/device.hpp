@@ -50,22 +50,25 @@ __device__ __forceinline__ float e4m3_decode(uint32_t b) {
   return __uint_as_float(((e + 120u) << 23) | (m << 20));
 }
 
-// E2M1 magnitude code of v, 0 <= v <= 6, nearest with ties to the even code.
-// Each comparison counts one grid step passed; at a midpoint the strict (>)
-// or non-strict (>=) form keeps the even neighbour.
-__device__ __forceinline__ uint32_t e2m1_encode(float v) {
-  return (uint32_t)(v > 0.25f) + (uint32_t)(v >= 0.75f) + (uint32_t)(v > 1.25f) +
-         (uint32_t)(v >= 1.75f) + (uint32_t)(v > 2.5f) + (uint32_t)(v >= 3.5f) +
-         (uint32_t)(v > 5.0f);
+// Eight fp32 values -> eight E2M1 codes (value i in bits 4i..4i+3):
+// v_cvt_scalef32_pk_fp4_f32 (scale 1) rounds to nearest with ties to the
+// even code, saturates at 6 and takes the sign bit from the value (so -0
+// gives code 8).
+__device__ __forceinline__ uint32_t e2m1_pack8(float v0, float v1, float v2, float v3, float v4,
+                                               float v5, float v6, float v7) {
+  uint32_t c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v0, v1, 1.0f, 0);
+  c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, v2, v3, 1.0f, 1);
+  c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, v4, v5, 1.0f, 2);
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, v6, v7, 1.0f, 3);
 }
 
 // One 16-element block -> (8 bytes of packed codes, scale byte).
-// x[i] are the fp32 values, sgn the sign bits (bit i = sign of element i).
-// gs is the global scale.  Operation order: a_s = amax*gs; zero/underflow
-// (amax == 0 or a_s < 6*2^-9) -> all zero; t = a_s/6; sf = E4M3(min(t,448));
-// r = gs/dec(sf); code_i = sign_i | E2M1(min(|x_i*r|, 6)).
-__device__ __forceinline__ void quantize_block16(const float (&x)[16], uint32_t sgn, float gs,
-                                                 uint32_t& lo, uint32_t& hi, uint32_t& sf) {
+// x[i] are the fp32 values, gs the global scale.  Operation order:
+// a_s = amax*gs; zero/underflow (amax == 0 or a_s < 6*2^-9) -> all zero;
+// t = a_s/6; sf = E4M3(min(t,448)); r = gs/dec(sf);
+// code_i = sign(x_i) | E2M1(min(|x_i*r|, 6)) (x_i*r has the sign of x_i).
+__device__ __forceinline__ void quantize_block16(const float (&x)[16], float gs, uint32_t& lo,
+                                                 uint32_t& hi, uint32_t& sf) {
 #pragma clang fp contract(off)
   float amax = 0.0f;
 #pragma unroll
@@ -76,13 +79,9 @@ __device__ __forceinline__ void quantize_block16(const float (&x)[16], uint32_t 
   const float t = fminf(a_s / 6.0f, kE4m3Max);
   sf = e4m3_encode(t);
   const float r = gs / e4m3_decode(sf);
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const float v = fminf(fabsf(x[i] * r), 6.0f);
-    const uint32_t c = e2m1_encode(v) | (((sgn >> i) & 1u) << 3);
-    if (i < 8) lo |= c << (4 * i);
-    else       hi |= c << (4 * (i - 8));
-  }
+  lo = e2m1_pack8(x[0] * r, x[1] * r, x[2] * r, x[3] * r, x[4] * r, x[5] * r, x[6] * r, x[7] * r);
+  hi = e2m1_pack8(x[8] * r, x[9] * r, x[10] * r, x[11] * r, x[12] * r, x[13] * r, x[14] * r,
+                  x[15] * r);
 }
 
 }  // namespace nvfp4

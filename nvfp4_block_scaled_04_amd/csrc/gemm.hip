@@ -604,13 +604,9 @@ __device__ __forceinline__ bool run_tile(const Params& p, uint8_t* smem, const i
             const float t = fminf(a_s / 6.0f, kE4m3Max);
             sfb = e4m3_encode(t);
             const float r = gs_h / e4m3_decode(sfb);
-            // E2M1 of h*r: v_cvt_scalef32_pk_fp4_f32 rounds to nearest even,
-            // saturates at 6 and keeps the sign (r > 0), two codes per byte,
-            // the even element in the low nibble
-            codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(codes, h[0] * r, h[1] * r, 1.0f, 0);
-            codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(codes, h[2] * r, h[3] * r, 1.0f, 1);
-            codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(codes, h[4] * r, h[5] * r, 1.0f, 2);
-            codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(codes, h[6] * r, h[7] * r, 1.0f, 3);
+            // sign | E2M1(min(|h*r|, 6)); r > 0, so h*r has the sign of h
+            codes = e2m1_pack8(h[0] * r, h[1] * r, h[2] * r, h[3] * r, h[4] * r, h[5] * r,
+                               h[6] * r, h[7] * r);
           }
         }
         *reinterpret_cast<uint32_t*>(p.c_q + d * (I / 2) + hb * 8 + hf * 4) = codes;

@@ -78,16 +78,13 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
   const uint4 v0 = x[2 * b], v1 = x[2 * b + 1];
   const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
   float xs[16];
-  uint32_t sgn = 0;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     xs[2 * j] = bf16_to_f32(w[j] & 0xFFFFu);
     xs[2 * j + 1] = bf16_to_f32(w[j] >> 16);
-    sgn |= ((w[j] >> 15) & 1u) << (2 * j);
-    sgn |= (w[j] >> 31) << (2 * j + 1);
   }
   uint32_t lo, hi, s;
-  quantize_block16(xs, sgn, g, lo, hi, s);
+  quantize_block16(xs, g, lo, hi, s);
   q[b] = make_uint2(lo, hi);
   sf[b] = (uint8_t)s;
 }
