@@ -34,7 +34,9 @@ import nvfp4_block_scaled_04_amd as nv  # noqa: E402
 from nvfp4_block_scaled_04_amd import inputs as I  # noqa: E402
 
 FP16_MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense FP16 MFMA
+FP4_MFMA_PEAK_TFLOPS = 10100.0      # MI355X dense FP4 MFMA (not the operand dtype used here)
 HBM_PEAK_GBS = 8000.0
+RIDGE = FP16_MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)   # flop per byte
 # HBM traffic of the L1 grouped GEMM per launch (bytes), from two rocprofv3
 # --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch),
 # each scaled by the ratio of known bytes to the counter's reading for a plain
@@ -95,6 +97,43 @@ class Events:
         return self.s.elapsed_time(self.e)
 
 
+def nvfp4_bytes(rows, cols):
+    """Codes + E4M3 scales of an NVFP4 (rows, cols) tensor."""
+    return rows * cols * 0.5625
+
+
+def timed_steps(fn, steps):
+    """Wall-clock mean over `steps` calls bracketed by synchronisations, and
+    per-step HIP-event times (ms) for percentiles."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s, e in evs:
+        s.record(torch.cuda.current_stream())
+        fn()
+        e.record(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    mean = (time.perf_counter() - t0) * 1e3 / steps
+    per = np.array([s.elapsed_time(e) for s, e in evs])
+    pct = {"p10": round(float(np.percentile(per, 10)), 4), "p50": round(float(np.median(per)), 4),
+           "p90": round(float(np.percentile(per, 90)), 4)}
+    return mean, pct
+
+
+def roofline(kernel, flops, nbytes, ms, traffic=None):
+    """Roofline object for one kernel: MFMA-bound (FP16 peak) when its
+    arithmetic intensity is above the ridge, else HBM-bound."""
+    if flops / max(nbytes, 1.0) >= RIDGE:
+        a = flops / (ms * 1e-3) / 1e12
+        return {"kernel": kernel, "bound": "mfma", "achieved": round(a, 2),
+                "peak": FP16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(a / FP16_MFMA_PEAK_TFLOPS, 4), "traffic": traffic}
+    a = nbytes / (ms * 1e-3) / 1e9
+    return {"kernel": kernel, "bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(a / HBM_PEAK_GBS, 4), "traffic": traffic}
+
+
 def time_loop(fn, steps):
     torch.cuda.synchronize()
     ev = Events()
@@ -121,13 +160,8 @@ def bench_moe(w, steps, warmup, dev):
     step = lambda: nv.moe_expert_forward(x, ids, tw, ew, gs_h, out=out, workspace=ws)
     for _ in range(warmup):
         step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        step()
-    torch.cuda.synchronize()
-    ms_step = (time.perf_counter() - t0) * 1e3 / steps
-    log(f"[bench] forward {ms_step:.3f} ms/step")
+    ms_step, pct = timed_steps(step, steps)
+    log(f"[bench] forward {ms_step:.3f} ms/step (p10/p50/p90 {pct['p10']}/{pct['p50']}/{pct['p90']})")
 
     # ---- each step alone, same kernels and arguments, events on the stream
     T, H, Iw, E, k = w.T, w.H, w.I, w.E, w.k
@@ -159,12 +193,21 @@ def bench_moe(w, steps, warmup, dev):
     l1_flops = 2.0 * M * (2 * Iw) * H
     l2_flops = 2.0 * M * H * Iw
     flops = moe_flops(T, H, Iw, k)
-    achieved = l1_flops / (st_ms["l1_gemm_swiglu_requant"] * 1e-3) / 1e12
-    roof = {"kernel": "grouped_gemm_kernel<SwiGLU+NVFP4 epilogue> (L1)", "bound": "mfma",
-            "achieved": round(achieved, 2), "peak": FP16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(achieved / FP16_MFMA_PEAK_TFLOPS, 4),
-            "traffic": (TRAFFIC.get((w.name, "l1")) if TRAFFIC_SRC_SHA == gemm_src_sha() else None)}
+    # algorithmic bytes: weights of the experts that hold rows, each once;
+    # A rows gathered, h written (L1); h read, y written (L2)
+    n_live = int(np.unique(ids_h[(ids_h >= 0) & (ids_h < E)]).size)
+    w1_bytes, w2_bytes = n_live * nvfp4_bytes(2 * Iw, H), n_live * nvfp4_bytes(H, Iw)
+    l1_bytes = w1_bytes + nvfp4_bytes(M, H) + nvfp4_bytes(M, Iw)
+    l2_bytes = w2_bytes + nvfp4_bytes(M, Iw) + 2.0 * M * H
+    roof = roofline("grouped_gemm_kernel<SwiGLU+NVFP4 epilogue> (L1)", l1_flops, l1_bytes,
+                    st_ms["l1_gemm_swiglu_requant"],
+                    TRAFFIC.get((w.name, "l1")) if TRAFFIC_SRC_SHA == gemm_src_sha() else None)
     extra = {
+        "ms_percentiles": pct,
+        "live_experts": n_live,
+        "weight_stream_gbs": (w1_bytes + w2_bytes) / (ms_step * 1e-3) / 1e9,
+        "l2_roofline": roofline("grouped_gemm_kernel<BF16 epilogue> (L2)", l2_flops, l2_bytes,
+                                st_ms["l2_gemm"]),
         "tokens_per_s": T / (ms_step * 1e-3),
         "l2_gemm_tflops": l2_flops / (st_ms["l2_gemm"] * 1e-3) / 1e12,
         "quantize_gbs": (2 * T * H + 0.5625 * T * H) / (st_ms["quantize"] * 1e-3) / 1e9,
@@ -172,6 +215,42 @@ def bench_moe(w, steps, warmup, dev):
         "stages_ms": {n: round(v, 4) for n, v in st_ms.items()},
     }
     return flops / (ms_step * 1e-3) / 1e12, ms_step, roof, extra, (x, ids_h, tw_h, ew)
+
+
+def bench_dense(w, steps, warmup, dev):
+    """The single NVFP4 linear (one expert): quantise A, then the GEMM with a
+    BF16 epilogue; each timed alone, and both together as the step."""
+    M, K, N = w.dense_mkn
+    log(f"[bench] dense M={M} K={K} N={N}")
+    a, b = I.make_dense(w, dev)
+    bk = nv.weight_layout(b.view(1, K, N), False)[0]                     # (N, K)
+    b_q, b_sf, gs_b = nv.quantize(bk)
+    bp = nv.pack_weights(b_q.view(1, N, K // 2), b_sf.view(1, N, K // 16))
+    a_q, a_sf, gs_a = nv.quantize(a)
+    off = torch.tensor([0, M], dtype=torch.int32, device=dev)
+    c = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    gws = torch.empty(nv.gemm_workspace_bytes(), dtype=torch.uint8, device=dev)
+    qbuf = (a_q, a_sf, gs_a)
+    quant = lambda: nv.quantize(a, out=qbuf)
+    gemm = lambda: nv.grouped_gemm(nv.EPI_BF16, a_q, a_sf, gs_a, off, bp, gs_b, M, out=c,
+                                   workspace=gws)
+
+    def step():
+        quant()
+        gemm()
+    for _ in range(warmup):
+        step()
+    ms_step, pct = timed_steps(step, steps)
+    st_ms = {"quantize": time_loop(quant, steps), "gemm": time_loop(gemm, steps)}
+    log(f"[bench] dense step {ms_step:.4f} ms; stages (ms): " +
+        ", ".join(f"{n}={v:.4f}" for n, v in st_ms.items()))
+    flops = 2.0 * M * N * K
+    nbytes = nvfp4_bytes(M, K) + nvfp4_bytes(N, K) + 2.0 * M * N
+    roof = roofline("grouped_gemm_kernel<BF16 epilogue> (dense)", flops, nbytes, st_ms["gemm"])
+    extra = {"ms_percentiles": pct, "stages_ms": {n: round(v, 4) for n, v in st_ms.items()},
+             "gemm_tflops": round(flops / (st_ms["gemm"] * 1e-3) / 1e12, 2),
+             "quantize_gbs": round((2.0 * M * K + nvfp4_bytes(M, K)) / (st_ms["quantize"] * 1e-3) / 1e9, 1)}
+    return flops / (ms_step * 1e-3) / 1e12, ms_step, roof, extra
 
 
 def cpu_baseline(w, x, ids_h, tw_h, dev, budget_s=20.0):
@@ -229,7 +308,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="prefill", choices=["tiny", "decode", "prefill", "skewed"])
+    ap.add_argument("--workload", default="prefill", choices=sorted(I.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -250,6 +329,22 @@ def main():
     dev = "cuda:0"
     torch.cuda.set_device(0)
     w = I.WORKLOADS[args.workload]
+    common = {"n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
+              "scaling": "weak", "vs_baseline": None, "dtype": "fp16",
+              "data": "synthetic (seeded; weights N(0,0.02), activations N(0,1))"}
+    if w.dense_mkn:
+        M, K, N = w.dense_mkn
+        value, ms_step, roof, extra = bench_dense(w, args.steps, args.warmup, dev)
+        line = {"metric": f"NVFP4 dense linear TFLOPS, M={M} K={K} N={N} (quantize A + GEMM)",
+                "value": round(value, 3), "unit": "TFLOPS", "ms_per_step": round(ms_step, 4),
+                **common,
+                "config": {"workload": f"dense M={M} K={K} N={N}", "rows": M, "k_dim": K,
+                           "n_dim": N, "parallelism": "single GPU"},
+                "frac_fp16_mfma_peak": round(value / FP16_MFMA_PEAK_TFLOPS, 4),
+                "frac_fp4_mfma_peak": round(value / FP4_MFMA_PEAK_TFLOPS, 4),
+                "roofline": roof, **extra, "cpu_baseline": None}
+        print(json.dumps(line), flush=True)
+        return
     value, ms_step, roof, extra, keep = bench_moe(w, args.steps, args.warmup, dev)
     cpu = None
     if not args.no_cpu_baseline:
@@ -258,19 +353,21 @@ def main():
         cpu = cpu_baseline(w, x, ids_h, tw_h, dev, args.cpu_budget)
         log(f"[bench] cpu oracle: {cpu}")
     line = {
-        "metric": "NVFP4 MoE fwd TFLOPS + tokens/s, T=8192 E=256 top-8; % of MFMA peak",
-        "value": round(value, 3), "unit": "TFLOPS", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "fp16",
-        "data": "synthetic (seeded; weights N(0,0.02), activations N(0,1))",
+        "metric": f"NVFP4 MoE fwd TFLOPS + tokens/s, T={w.T} E={w.E} top-{w.k}; % of MFMA peak",
+        "value": round(value, 3), "unit": "TFLOPS", "ms_per_step": round(ms_step, 4), **common,
         "config": {"workload": f"{w.name} T={w.T} H={w.H} I={w.I} E={w.E} top-{w.k}",
                    "tokens": w.T, "hidden": w.H, "intermediate": w.I, "experts": w.E,
                    "top_k": w.k, "expert_rows": w.M, "parallelism": "single GPU"},
         "tokens_per_s": round(extra["tokens_per_s"], 1),
         "frac_fp16_mfma_peak": round(value / FP16_MFMA_PEAK_TFLOPS, 4),
+        "frac_fp4_mfma_peak": round(value / FP4_MFMA_PEAK_TFLOPS, 4),
+        "ms_percentiles": extra["ms_percentiles"],
         "roofline": roof,
+        "l2_roofline": extra["l2_roofline"],
         "stages_ms": extra["stages_ms"],
         "l2_gemm_tflops": round(extra["l2_gemm_tflops"], 2),
+        "weight_stream_gbs": round(extra["weight_stream_gbs"], 1),
+        "live_experts": extra["live_experts"],
         "quantize_gbs": round(extra["quantize_gbs"], 1),
         "combine_gbs": round(extra["combine_gbs"], 1),
         "cpu_baseline": cpu,

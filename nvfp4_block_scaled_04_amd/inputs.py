@@ -19,6 +19,8 @@ Workloads (names used by the tests and the benchmark):
            seeded permutation (the other 77 = 30% are never chosen), 8
            distinct experts per token by Gumbel-top-8; 1% of x's 16-blocks
            zeroed and 1% rescaled to amax 1e-6.
+  moe384   the pages' own MoE shape: T=8192 H=7168 I=3072 E=384 k=6 (49152
+           expert rows), routing and distributions as prefill.
 decode/prefill/skewed share one weight seed (identical weights).
 BF16 values are float32 draws rounded to nearest even by torch.
 """
@@ -62,6 +64,8 @@ WORKLOADS = {
                         weight_seed=0x5EED0003, gs_h=32.0),
     "skewed": Workload("skewed", 5, T=16384, H=7168, I=2048, E=256, k=8, routing="zipf",
                        special="blocks", weight_seed=0x5EED0003, gs_h=32.0),
+    "moe384": Workload("moe384", 6, T=8192, H=7168, I=3072, E=384, k=6,
+                       weight_seed=0x5EED0006, gs_h=32.0),
 }
 
 

@@ -59,7 +59,7 @@ def calibrate(w):
 
 def main():
     res = {}
-    for name in ("tiny", "decode", "prefill", "skewed"):
+    for name in ("tiny", "decode", "prefill", "skewed", "moe384"):
         res[name] = calibrate(I.WORKLOADS[name])
         print(name, res[name], flush=True)
     res["_recipe"] = ("gs_h = 2**floor(log2(2688/amax(h over a row sample)))/2; sample = rows of the "

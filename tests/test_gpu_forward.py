@@ -126,10 +126,15 @@ def test_forward_zero_tokens():
 _BIG = {}
 
 
-def _big_weights():
-    if "ew" not in _BIG:
-        _BIG["ew"] = _gpu_weights(I.WORKLOADS["prefill"])
-    return _BIG["ew"]
+def _big_weights(w):
+    """Full-size weights, built once per weight set (decode/prefill/skewed
+    share one)."""
+    key = (w.weight_seed, w.E, w.H, w.I)
+    if key not in _BIG:
+        _BIG.clear()                     # one full-size weight set resident at a time
+        torch.cuda.empty_cache()
+        _BIG[key] = _gpu_weights(w)
+    return _BIG[key]
 
 
 def _sample_tokens(name, ids):
@@ -140,10 +145,10 @@ def _sample_tokens(name, ids):
     return [0, T - 1] if name == "decode" else [T // 3]
 
 
-@pytest.mark.parametrize("name", ["decode", "prefill", "skewed"])
+@pytest.mark.parametrize("name", ["decode", "prefill", "skewed", "moe384"])
 def test_forward_full_size_sampled_tokens(name):
     w = I.WORKLOADS[name]
-    ew = _big_weights()
+    ew = _big_weights(w)
     x, ids, tw, out, tp = _run(w, ew)
     # routing is cheap to check in full
     roff, rperm, rinv, _ = R.route(ids, w.E)

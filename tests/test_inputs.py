@@ -15,7 +15,7 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "gs_h.json")
 
 def test_gs_h_constants_match_calibration_file():
     cal = json.load(open(GOLDEN))
-    for name in ("tiny", "decode", "prefill", "skewed"):
+    for name in ("tiny", "decode", "prefill", "skewed", "moe384"):
         assert I.WORKLOADS[name].gs_h == cal[name]["gs_h"], name
 
 
