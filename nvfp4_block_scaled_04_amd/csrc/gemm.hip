@@ -407,17 +407,44 @@ __device__ __forceinline__ void tile_at(const Params& p, const int* tprefix, int
   t.jv = (t.nrows + 31) / 32;
 }
 
-// Tile scheduling.  XCD x (blocks b with b % 8 == x) owns tiles [lo, hi),
-// an eighth of the list, contiguous so that an expert's tiles share one L2;
-// its blocks claim tiles dynamically from counter sched[x].  Thread 0 of a
-// block claims the tile after its next one right before it issues the next
-// tile's loads; the claim is published through LDS at the following
-// post-K-loop barrier, when every earlier load has completed.
+// Tile scheduling.  XCD x (blocks b with b % 8 == x) owns tiles
+// [total*x/8, total*(x+1)/8), an eighth of the list, contiguous so that an
+// expert's tiles share one L2; its blocks claim tiles dynamically from
+// counter x.  The XCDs do not run at one clock, so a block whose range is
+// exhausted steals from the other XCDs' counters.  Thread 0 of a block
+// claims the tile after its next one right before it issues the next tile's
+// loads; the claim is published through LDS at the following post-K-loop
+// barrier, when every earlier load has completed.
 struct Sched {
-  int lo, hi;       // this XCD's tile range
-  int* counter;
-  int* s_claim;     // LDS slot for the pending claim
+  int64_t total;    // tiles in the list
+  int* counters;    // eight per-XCD claim counters, zero at launch
+  int* s_claim;     // LDS: [0] pending claim, [2] stolen tile, [3] its counter
+  int cx;           // counter this block claims from (its XCD's first)
 };
+
+__device__ __forceinline__ int range_lo(int64_t total, int c) { return (int)((total * c) >> 3); }
+
+// Tile index of claim k made on counter sc.cx, or -1 when every range is
+// exhausted.  Every thread calls it with the same k; when sc.cx's range is
+// exhausted thread 0 claims from the other counters in turn and the result
+// is broadcast through LDS (one extra barrier, only at the end of a range).
+__device__ __forceinline__ int resolve_claim(Sched& sc, int k) {
+  if (range_lo(sc.total, sc.cx) + k < range_lo(sc.total, sc.cx + 1))
+    return range_lo(sc.total, sc.cx) + k;
+  if (threadIdx.x == 0) {
+    int t = -1, c = sc.cx;
+    for (int d = 1; d < 8 && t < 0; ++d) {
+      c = (c + 1) & 7;
+      const int kk = atomicAdd(sc.counters + c, 1);
+      if (range_lo(sc.total, c) + kk < range_lo(sc.total, c + 1)) t = range_lo(sc.total, c) + kk;
+    }
+    sc.s_claim[2] = t;
+    sc.s_claim[3] = c;
+  }
+  __syncthreads();
+  sc.cx = __builtin_amdgcn_readfirstlane(sc.s_claim[3]);
+  return __builtin_amdgcn_readfirstlane(sc.s_claim[2]);
+}
 
 // packed weights: tile (e, n0 / BN) is K/BK stages of BN rows (64 code bytes
 // and 8 scale bytes per row), rows zero-padded to a multiple of BN
@@ -474,7 +501,7 @@ __device__ __forceinline__ void tile_offsets(const Params& p, const Tile& t, int
 // coff/soff rewritten for it, so that their latency overlaps the epilogue.
 template <int BN, int BM, int WN, int WM, int EPI, int JV>
 __device__ __forceinline__ bool run_tile(const Params& p, uint8_t* smem, const int* tprefix,
-                                         const Sched& sc, const Tile& cur, uint32_t* coff,
+                                         Sched& sc, const Tile& cur, uint32_t* coff,
                                          uint32_t* soff, int& claim, Tile& nxt) {
   using C = Cfg<BN, BM, WN, WM>;
   constexpr int FN = C::FN, FM = C::FM, TN = C::TN, TM = C::TM;
@@ -525,13 +552,13 @@ __device__ __forceinline__ bool run_tile(const Params& p, uint8_t* smem, const i
   // and keep them live across it, which would spill.
   int lane_x = lane;
   asm volatile("" : "+v"(lane_x));
-  const int t_next = sc.lo + __builtin_amdgcn_readfirstlane(*sc.s_claim);
-  const bool has_next = t_next < sc.hi;
+  const int t_next = resolve_claim(sc, __builtin_amdgcn_readfirstlane(*sc.s_claim));
+  const bool has_next = t_next >= 0;
   if (has_next) tile_at<BN, BM>(p, tprefix, t_next, nxt);
   {
   const int lane = lane_x, hf = lane_x >> 5, l32 = lane_x & 31;
   if (has_next) {
-    if (tid == 0) claim = atomicAdd(sc.counter, 1);
+    if (tid == 0) claim = atomicAdd(sc.counters + sc.cx, 1);
     tile_offsets<BN, BM, WN, WM, EPI>(p, nxt, wave, lane, coff, soff);
     k_issue_first<BN, BM, WN, WM>(nks, wave, coff, soff, tile_wq<BN>(p, nxt), tile_wsf<BN>(p, nxt),
                                   p.a_q, p.a_sf, smem, smem + C::STAGE_BYTES);
@@ -654,24 +681,20 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_gemm_kernel(Params p)
     if (tid == C::NT - 1) tprefix[E] = s_scan[C::NT - 1];
     __syncthreads();
   }
-  __shared__ int s_claim[2];
+  __shared__ int s_claim[4];
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int nks = (int)(p.K / BK);
-  const int x = blockIdx.x & 7;                  // XCD (blocks are dispatched round-robin)
-  const int64_t total = (int64_t)tprefix[p.E] * p.n_tiles;
   Sched sc;
-  sc.lo = (int)((total * x) >> 3);
-  sc.hi = (int)((total * (x + 1)) >> 3);
-  sc.counter = p.sched + x;
+  sc.total = (int64_t)tprefix[p.E] * p.n_tiles;
+  sc.counters = p.sched;
   sc.s_claim = s_claim;
-  if (tid == 0) {
-    s_claim[0] = atomicAdd(sc.counter, 1);
-    s_claim[1] = atomicAdd(sc.counter, 1);
-  }
+  sc.cx = blockIdx.x & 7;                  // own XCD (blocks are dispatched round-robin)
+  if (tid == 0) s_claim[0] = atomicAdd(sc.counters + sc.cx, 1);
   __syncthreads();
-  int claim = s_claim[1];                  // meaningful in thread 0 only
-  const int t0 = sc.lo + __builtin_amdgcn_readfirstlane(s_claim[0]);
-  bool have = t0 < sc.hi;
+  const int t0 = resolve_claim(sc, __builtin_amdgcn_readfirstlane(s_claim[0]));
+  bool have = t0 >= 0;
+  int claim = 0;                           // pending claim, meaningful in thread 0 only
+  if (have && tid == 0) claim = atomicAdd(sc.counters + sc.cx, 1);
   Tile cur;
   uint32_t coff[C::CODE_LOADS], soff[C::SF_LOADS];
   if (have) {
