@@ -357,11 +357,15 @@ __device__ __forceinline__ void k_stage(KState<BN, BM, WN, WM, JV>& st, int ks, 
     NVFP4_READ_HALF(bm, 0, st.fa, st.ta);
     NVFP4_READ_SF(bm, st.wsr, st.tsr);
   }
+  // the reads go out here; their consumers stay in the last step (below),
+  // so their latency hides behind steps 4-6 instead of stalling issue
+  __builtin_amdgcn_sched_barrier(0);
   if (LOADS) NVFP4_ISSUE(ks + 2, bw, 4);
   NVFP4_DECODE(5, st.fb, st.tb, st.wsc, st.tsc, st.av1, st.bv1); NVFP4_MFMAS(st.av0, st.bv0); NVFP4_INTERLEAVE(NL);
   if (LOADS) NVFP4_ISSUE(ks + 2, bw, 5);
   NVFP4_DECODE(6, st.fb, st.tb, st.wsc, st.tsc, st.av0, st.bv0); NVFP4_MFMAS(st.av1, st.bv1); NVFP4_INTERLEAVE(NL);
   NVFP4_DECODE(7, st.fb, st.tb, st.wsc, st.tsc, st.av1, st.bv1); NVFP4_MFMAS(st.av0, st.bv0); NVFP4_INTERLEAVE(0);
+  __builtin_amdgcn_sched_barrier(0);
   if (more1) {
 #pragma unroll
     for (int i = 0; i < FN; ++i) st.wsc[i] = scales4(st.wsr[i]);
