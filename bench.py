@@ -189,6 +189,14 @@ def bench_moe(w, steps, warmup, dev):
         fn()
         st_ms[name] = time_loop(fn, steps)
     log("[bench] stages (ms): " + ", ".join(f"{n}={v:.4f}" for n, v in st_ms.items()))
+    # the step before the path (not in the timed forward, which takes ids and
+    # weights): router top-k + softmax on N(0,1) logits of this shape
+    logits = torch.from_numpy(I.make_router_logits(w)).to(dev)
+    rbuf = (torch.empty((T, k), dtype=torch.int32, device=dev),
+            torch.empty((T, k), dtype=torch.float32, device=dev))
+    router = lambda: nv.router_topk(logits, k, out=rbuf)
+    router()
+    router_ms = time_loop(router, steps)
 
     l1_flops = 2.0 * M * (2 * Iw) * H
     l2_flops = 2.0 * M * H * Iw
@@ -213,6 +221,7 @@ def bench_moe(w, steps, warmup, dev):
         "quantize_gbs": (2 * T * H + 0.5625 * T * H) / (st_ms["quantize"] * 1e-3) / 1e9,
         "combine_gbs": (2 * M * H + 12 * M + 2 * T * H) / (st_ms["combine"] * 1e-3) / 1e9,
         "stages_ms": {n: round(v, 4) for n, v in st_ms.items()},
+        "router_topk_ms": round(router_ms, 4),
     }
     return flops / (ms_step * 1e-3) / 1e12, ms_step, roof, extra, (x, ids_h, tw_h, ew)
 
@@ -365,6 +374,7 @@ def main():
         "roofline": roof,
         "l2_roofline": extra["l2_roofline"],
         "stages_ms": extra["stages_ms"],
+        "router_topk_ms": extra["router_topk_ms"],
         "l2_gemm_tflops": round(extra["l2_gemm_tflops"], 2),
         "weight_stream_gbs": round(extra["weight_stream_gbs"], 1),
         "live_experts": extra["live_experts"],

@@ -119,6 +119,23 @@ nvfp4_status nvfp4_pack_weights(const uint8_t* q, const uint8_t* sf, int64_t E, 
                                 int64_t K, uint8_t* q_packed, uint8_t* sf_packed, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Router: top-k expert ids and routing weights from router logits.
+ * README "NVFP4 MegaMoE Kernel", "What We Have", MoE runner step 6 scatters
+ * "with routing weights": ids and weights are inputs of the path; this is
+ * the step that makes them.  The pages do not define it; the reading used
+ * (as for the tiny workload) is top-k of the logits, then a softmax over the
+ * k chosen:
+ *   topk_ids[t][0..k) = the k largest logits[t][.] in decreasing order,
+ *                       equal logits in increasing expert id;
+ *   topk_w[t][j] = exp(l_j - l_0) / sum_i exp(l_i - l_0)   (fp32).
+ * logits float [T][E] (finite), topk_ids int32 [T][k], topk_w float [T][k].
+ * Shapes: T >= 0, 1 <= E <= 1024, 1 <= k <= min(E, 64).
+ * No workspace.
+ * ---------------------------------------------------------------------- */
+nvfp4_status nvfp4_router_topk(const float* logits, int64_t T, int E, int k, int32_t* topk_ids,
+                               float* topk_w, void* stream);
+
+/* ------------------------------------------------------------------------
  * Expert offsets and expert-order permutation.
  * README "Correctness Bugs Fixed", bug 5: a histogram, not an O(n x E) mask;
  * README "Key Lessons" 4: quantise compact rows, then place them.

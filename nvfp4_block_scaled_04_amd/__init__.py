@@ -10,7 +10,7 @@ from .binding import (  # noqa: F401
     EPI_BF16, EPI_SWIGLU_NVFP4, ExpertWeights, Nvfp4Error, PackedWeight, Taps, forward_workspace,
     gemm_workspace_bytes,
     grouped_gemm, lib, moe_combine, moe_expert_forward, moe_route, pack_weights,
-    prepare_expert_weights, quantize, weight_layout,
+    prepare_expert_weights, quantize, router_topk, weight_layout,
 )
 
 __version__ = "0.1.0"

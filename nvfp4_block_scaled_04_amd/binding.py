@@ -40,6 +40,7 @@ SIGNATURES = {
     "nvfp4_moe_route": (c_int, [c_void_p, c_int64, c_int, c_int, c_void_p, c_void_p, c_void_p,
                                 c_void_p, c_void_p, c_size_t, c_void_p]),
     "nvfp4_grouped_gemm_workspace_size": (c_size_t, []),
+    "nvfp4_router_topk": (c_int, [c_void_p, c_int64, c_int, c_int, c_void_p, c_void_p, c_void_p]),
     "nvfp4_grouped_gemm": (c_int, [c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_void_p,
                                    c_int, c_int64, c_int64, c_int64, c_void_p, c_void_p, c_void_p,
                                    c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
@@ -189,6 +190,21 @@ def moe_route(topk_ids, E):
     _check(L.nvfp4_moe_route(_ptr(topk_ids), T, k, E, _ptr(off), _ptr(perm), _ptr(inv), _ptr(bad),
                              _ptr(ws), nbytes, _stream(dev)), "nvfp4_moe_route")
     return off, perm, inv, bad
+
+
+def router_topk(logits, k, out=None):
+    """logits (T, E) float32 -> (topk_ids (T, k) int32, topk_w (T, k) float32):
+    the k largest logits (equal ones in increasing id) and a softmax over them."""
+    _dev(logits, torch.float32, "logits")
+    T, E = logits.shape
+    if out is not None:
+        ids, w = out
+    else:
+        ids = torch.empty((T, k), dtype=torch.int32, device=logits.device)
+        w = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+    _check(lib().nvfp4_router_topk(_ptr(logits), T, E, k, _ptr(ids), _ptr(w), _stream(logits.device)),
+           "nvfp4_router_topk")
+    return ids, w
 
 
 def gemm_workspace_bytes():

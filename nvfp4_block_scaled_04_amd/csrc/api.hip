@@ -260,6 +260,24 @@ nvfp4_status nvfp4_moe_route(const int32_t* topk_ids, int64_t T, int k, int E,
                 "nvfp4_moe_route launch");
 }
 
+nvfp4_status nvfp4_router_topk(const float* logits, int64_t T, int E, int k, int32_t* topk_ids,
+                               float* topk_w, void* stream) {
+  if (T < 0) return fail(NVFP4_ERR_SHAPE, "T must be >= 0");
+  if (E < 1 || E > nvfp4::kRouterMaxExperts)
+    return fail(NVFP4_ERR_SHAPE, "E must be in [1, %d] (got %d)", nvfp4::kRouterMaxExperts, E);
+  if (k < 1 || k > 64 || k > E) return fail(NVFP4_ERR_SHAPE, "k must be in [1, min(E, 64)] (got %d)", k);
+  if (T == 0) return NVFP4_OK;
+  if (!logits || !topk_ids || !topk_w)
+    return fail(NVFP4_ERR_INVALID_ARG, "logits, topk_ids and topk_w must be non-NULL");
+  if (!aligned(logits, 4) || !aligned(topk_ids, 4) || !aligned(topk_w, 4))
+    return fail(NVFP4_ERR_INVALID_ARG, "logits, topk_ids and topk_w must be 4-byte aligned");
+  nvfp4_status st = check_arch();
+  if (st != NVFP4_OK) return st;
+  return finish(nvfp4::launch_router_topk(logits, T, E, k, topk_ids, topk_w,
+                                          static_cast<hipStream_t>(stream)),
+                "nvfp4_router_topk launch");
+}
+
 size_t nvfp4_grouped_gemm_workspace_size(void) { return nvfp4::kGemmWorkspaceBytes; }
 
 nvfp4_status nvfp4_grouped_gemm(int epilogue, const uint8_t* a_q, const uint8_t* a_sf,

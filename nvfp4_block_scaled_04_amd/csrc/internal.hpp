@@ -58,6 +58,9 @@ struct GemmArgs {
 };
 constexpr size_t kGemmWorkspaceBytes = 256;
 hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t stream);
+constexpr int kRouterMaxExperts = 1024;
+hipError_t launch_router_topk(const float* logits, int64_t T, int E, int k, int32_t* topk_ids,
+                              float* topk_w, hipStream_t stream);
 
 // combine.hip
 hipError_t launch_combine(const void* y, const int32_t* inv_perm, const float* topk_w,

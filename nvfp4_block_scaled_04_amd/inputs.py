@@ -118,6 +118,13 @@ def make_x(w: Workload, device="cpu"):
     return x.to(torch.bfloat16)
 
 
+def make_router_logits(w: Workload):
+    """Router logits (T, E) float32 N(0,1): the draw the router workloads'
+    routing starts from (same seed and stream as make_routing)."""
+    rng = np.random.default_rng(_seed(0x5EED0000 + w.wid, 3))
+    return rng.standard_normal((w.T, w.E)).astype(np.float32)
+
+
 def make_routing(w: Workload):
     """(topk_ids int32 (T, k), topk_w float32 (T, k)) as numpy arrays."""
     rng = np.random.default_rng(_seed(0x5EED0000 + w.wid, 3))

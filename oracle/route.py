@@ -32,3 +32,29 @@ def route(topk_ids, E):
     inv_perm = np.empty_like(perm)
     inv_perm[perm] = np.arange(perm.size, dtype=np.int32)
     return offsets, perm, inv_perm, int(np.count_nonzero(~valid))
+
+
+def router_topk(logits, k):
+    """Router: logits (T, E) float32 -> (topk_ids (T, k) int32, topk_w (T, k)
+    float64).
+
+    The pages take the expert ids and routing weights as given (the runner
+    scatters "with routing weights"); the tiny workload's description fixes
+    the router as top-k of the logits followed by a softmax over the k chosen
+    ones.  Reading: the k largest logits in decreasing order, equal logits in
+    increasing expert id; w_j = exp(l_j - l_max) / sum_i exp(l_i - l_max) over
+    the chosen logits, in float64.
+    """
+    lg = np.asarray(logits, dtype=np.float32)
+    T, E = lg.shape
+    ids = np.empty((T, k), dtype=np.int32)
+    w = np.empty((T, k), dtype=np.float64)
+    for t in range(T):
+        # descending by value; a stable sort of the negated values keeps
+        # equal logits in increasing id
+        order = np.argsort(-lg[t].astype(np.float64), kind="stable")[:k]
+        sel = lg[t, order].astype(np.float64)
+        ex = np.exp(sel - sel[0])
+        ids[t] = order
+        w[t] = ex / ex.sum()
+    return ids, w

@@ -113,6 +113,16 @@ def test_gemm_workspace(L):
     assert _gemm(L, M=0, ws=None, wsb=0) == 0             # nothing to do, nothing launched
 
 
+def test_router_rejects(L):
+    assert L.nvfp4_router_topk(FAKE, 4, 0, 1, FAKE, FAKE, None) == -2          # E < 1
+    assert L.nvfp4_router_topk(FAKE, 4, 1025, 1, FAKE, FAKE, None) == -2       # E > 1024
+    assert L.nvfp4_router_topk(FAKE, 4, 8, 9, FAKE, FAKE, None) == -2          # k > E
+    assert L.nvfp4_router_topk(FAKE, 4, 256, 65, FAKE, FAKE, None) == -2       # k > 64
+    assert L.nvfp4_router_topk(None, 4, 8, 2, FAKE, FAKE, None) == -1
+    assert L.nvfp4_router_topk(FAKE + 2, 4, 8, 2, FAKE, FAKE, None) == -1      # misaligned
+    assert L.nvfp4_router_topk(None, 0, 8, 2, None, None, None) == 0           # nothing to do
+
+
 def test_combine_and_forward_reject(L):
     assert L.nvfp4_moe_combine(FAKE, FAKE, FAKE, FAKE, 4, 2, 4, 12, FAKE, None) == -2
     assert L.nvfp4_moe_combine(None, FAKE, FAKE, FAKE, 4, 2, 4, 16, FAKE, None) == -1

@@ -74,3 +74,13 @@ def test_skewed_special_blocks():
     assert abs(int((amax == 0).sum()) - n // 100) <= 2
     tiny = (amax > 0) & (amax < 2e-6)
     assert abs(int(tiny.sum()) - n // 100) <= 2
+
+
+def test_router_logits_are_the_router_workloads_draw():
+    # the tiny workload's routing is the oracle router applied to these logits
+    from oracle import route as R
+    w = I.WORKLOADS["tiny"]
+    ids, tw = I.make_routing(w)
+    rid, rtw = R.router_topk(I.make_router_logits(w), w.k)
+    assert np.array_equal(ids, rid)
+    np.testing.assert_allclose(tw, rtw, rtol=1e-6)

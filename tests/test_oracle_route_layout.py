@@ -113,3 +113,44 @@ def test_deinterleave_inverts_interleave():
 def test_k_major():
     w = np.arange(24).reshape(1, 4, 6)
     assert np.array_equal(L.k_major(w)[0], w[0].T)
+
+
+def _brute_topk(row, k):
+    """Selection by repeated scan: the largest remaining value, lowest index
+    among equals."""
+    left = list(range(len(row)))
+    out = []
+    for _ in range(k):
+        best = left[0]
+        for e in left[1:]:
+            if row[e] > row[best]:
+                best = e
+        out.append(best)
+        left.remove(best)
+    return out
+
+
+@pytest.mark.parametrize("T,E,k,seed", [(5, 4, 2, 0), (7, 64, 8, 1), (3, 384, 6, 2), (4, 9, 9, 3)])
+def test_router_topk_matches_brute_force(T, E, k, seed):
+    rng = np.random.default_rng(seed)
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    lg[0, : E // 2] = lg[0, 0]                       # a run of equal logits
+    ids, w = R.router_topk(lg, k)
+    for t in range(T):
+        assert ids[t].tolist() == _brute_topk(lg[t].tolist(), k)
+        sel = lg[t, ids[t]].astype(np.float64)
+        ref = [np.exp(v - sel.max()) for v in sel]
+        np.testing.assert_allclose(w[t], np.array(ref) / sum(ref), rtol=1e-15)
+    assert np.all(np.diff(w, axis=1) <= 0)            # weights follow the logit order
+
+
+def test_router_topk_ties_shift_and_k1():
+    lg = np.array([[1.0, 3.0, 3.0, 2.0, 3.0]], np.float32)
+    ids, w = R.router_topk(lg, 3)
+    assert ids.tolist() == [[1, 2, 4]]                # equal logits: lower id first
+    np.testing.assert_array_equal(w, np.full((1, 3), 1 / 3))
+    ids2, w2 = R.router_topk(lg + np.float32(5.0), 3)   # softmax is shift-invariant
+    assert np.array_equal(ids, ids2)
+    np.testing.assert_allclose(w, w2, rtol=1e-15)
+    ids1, w1 = R.router_topk(lg, 1)
+    assert ids1.tolist() == [[1]] and w1[0, 0] == 1.0
