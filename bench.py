@@ -238,7 +238,9 @@ def bench_dense(w, steps, warmup, dev):
     a_q, a_sf, gs_a = nv.quantize(a)
     off = torch.tensor([0, M], dtype=torch.int32, device=dev)
     c = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-    gws = torch.empty(nv.gemm_workspace_bytes(), dtype=torch.uint8, device=dev)
+    # a workspace large enough for split K (128 tiles cannot fill 256 CUs)
+    gws = torch.empty(nv.gemm_splitk_workspace_bytes(nv.EPI_BF16, M, N, K, 1), dtype=torch.uint8,
+                      device=dev)
     qbuf = (a_q, a_sf, gs_a)
     quant = lambda: nv.quantize(a, out=qbuf)
     gemm = lambda: nv.grouped_gemm(nv.EPI_BF16, a_q, a_sf, gs_a, off, bp, gs_b, M, out=c,
@@ -258,6 +260,7 @@ def bench_dense(w, steps, warmup, dev):
     roof = roofline("grouped_gemm_kernel<BF16 epilogue> (dense)", flops, nbytes, st_ms["gemm"])
     extra = {"ms_percentiles": pct, "stages_ms": {n: round(v, 4) for n, v in st_ms.items()},
              "gemm_tflops": round(flops / (st_ms["gemm"] * 1e-3) / 1e12, 2),
+             "split_k": gws.numel() > nv.gemm_workspace_bytes(),
              "quantize_gbs": round((2.0 * M * K + nvfp4_bytes(M, K)) / (st_ms["quantize"] * 1e-3) / 1e9, 1)}
     return flops / (ms_step * 1e-3) / 1e12, ms_step, roof, extra
 

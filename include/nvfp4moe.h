@@ -184,15 +184,28 @@ nvfp4_status nvfp4_moe_route(const int32_t* topk_ids, int64_t T, int k, int E,
  * Shapes: E >= 1, M >= 0, K % 128 == 0, K >= 128, N % 32 == 0, N >= 32;
  *   SwiGLU: N % 32 == 0 (I % 16 == 0).
  * Unused output pointers of the other epilogue may be NULL.
- * Workspace: nvfp4_grouped_gemm_workspace_size() bytes, 4-byte aligned,
- *   caller-owned: the tile scheduler's counters.  Each call first zeroes
- *   them (a small kernel on `stream`), so the contents need no set-up;
- *   calls that share a workspace must be ordered on one stream.  May be
- *   NULL only when M == 0.
+ * Workspace: at least nvfp4_grouped_gemm_workspace_size() bytes, 4-byte
+ *   aligned, caller-owned: the tile scheduler's counters.  Each call first
+ *   zeroes them (a small kernel on `stream`), so the contents need no
+ *   set-up; calls that share a workspace must be ordered on one stream.  May
+ *   be NULL only when M == 0.
+ * Split K (BF16 epilogue only): when the launch has too few tiles to occupy
+ *   the device (at most half as many as it has CUs, e.g. a dense linear of
+ *   a few thousand rows) and ws_bytes >= nvfp4_grouped_gemm_splitk_workspace_size
+ *   (same epilogue, M, N, K, E; current device), each tile's K range is cut
+ *   into up to 4 parts whose fp32 partial sums (scaled by the global scales)
+ *   go to the workspace; a second kernel on `stream` sums them in part order
+ *   and rounds to BF16.  The result differs from the unsplit one only by
+ *   fp32 summation order.  With a smaller workspace K is never split.
  * ---------------------------------------------------------------------- */
 #define NVFP4_EPI_BF16 0
 #define NVFP4_EPI_SWIGLU_NVFP4 1
 size_t nvfp4_grouped_gemm_workspace_size(void);
+/* Workspace that lets a launch of this shape split K on the current device
+ * (nvfp4_grouped_gemm_workspace_size() when it would not split, or when the
+ * device cannot be queried). */
+size_t nvfp4_grouped_gemm_splitk_workspace_size(int epilogue, int64_t M, int64_t N, int64_t K,
+                                                int E);
 nvfp4_status nvfp4_grouped_gemm(int epilogue, const uint8_t* a_q, const uint8_t* a_sf,
                                 const float* gs_a, const int32_t* a_row_src, int a_row_div,
                                 const int32_t* expert_offsets, int E, int64_t M, int64_t N,

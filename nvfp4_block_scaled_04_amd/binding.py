@@ -40,6 +40,7 @@ SIGNATURES = {
     "nvfp4_moe_route": (c_int, [c_void_p, c_int64, c_int, c_int, c_void_p, c_void_p, c_void_p,
                                 c_void_p, c_void_p, c_size_t, c_void_p]),
     "nvfp4_grouped_gemm_workspace_size": (c_size_t, []),
+    "nvfp4_grouped_gemm_splitk_workspace_size": (c_size_t, [c_int, c_int64, c_int64, c_int64, c_int]),
     "nvfp4_router_topk": (c_int, [c_void_p, c_int64, c_int, c_int, c_void_p, c_void_p, c_void_p]),
     "nvfp4_grouped_gemm": (c_int, [c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_void_p,
                                    c_int, c_int64, c_int64, c_int64, c_void_p, c_void_p, c_void_p,
@@ -210,6 +211,12 @@ def router_topk(logits, k, out=None):
 def gemm_workspace_bytes():
     """Workspace bytes nvfp4_grouped_gemm needs (the tile scheduler's counters)."""
     return int(lib().nvfp4_grouped_gemm_workspace_size())
+
+
+def gemm_splitk_workspace_bytes(epilogue, M, N, K, E):
+    """Workspace bytes with which nvfp4_grouped_gemm may split K for this shape
+    on the current device (gemm_workspace_bytes() when it would not)."""
+    return int(lib().nvfp4_grouped_gemm_splitk_workspace_size(epilogue, M, N, K, E))
 
 
 def grouped_gemm(epilogue, a_q, a_sf, gs_a, offsets, b: PackedWeight, gs_b, M, a_row_src=None,

@@ -280,6 +280,12 @@ nvfp4_status nvfp4_router_topk(const float* logits, int64_t T, int E, int k, int
 
 size_t nvfp4_grouped_gemm_workspace_size(void) { return nvfp4::kGemmWorkspaceBytes; }
 
+size_t nvfp4_grouped_gemm_splitk_workspace_size(int epilogue, int64_t M, int64_t N, int64_t K,
+                                                int E) {
+  if (M < 0 || N < 32 || K < 128 || E < 1) return nvfp4::kGemmWorkspaceBytes;
+  return nvfp4::gemm_splitk_ws_bytes(epilogue, M, N, K, E);
+}
+
 nvfp4_status nvfp4_grouped_gemm(int epilogue, const uint8_t* a_q, const uint8_t* a_sf,
                                 const float* gs_a, const int32_t* a_row_src, int a_row_div,
                                 const int32_t* expert_offsets, int E, int64_t M, int64_t N,
@@ -288,7 +294,7 @@ nvfp4_status nvfp4_grouped_gemm(int epilogue, const uint8_t* a_q, const uint8_t*
                                 uint8_t* c_q, uint8_t* c_sf, float* c_debug_f32, void* ws,
                                 size_t ws_bytes, void* stream) {
   nvfp4::GemmArgs a{epilogue, a_q, a_sf, gs_a, a_row_src, a_row_div, expert_offsets, E, M, N, K,
-                    b_q, b_sf, gs_b, gs_out, c_bf16, c_q, c_sf, c_debug_f32, ws};
+                    b_q, b_sf, gs_b, gs_out, c_bf16, c_q, c_sf, c_debug_f32, ws, ws_bytes};
   nvfp4_status st = check_gemm(a);
   if (st != NVFP4_OK) return st;
   if (M == 0) return NVFP4_OK;
@@ -376,11 +382,13 @@ nvfp4_status moe_expert_forward(const void* x_bf16, int64_t T, int64_t H, int64_
   if (err != hipSuccess) return hip_fail(err, "moe_expert_forward route");
   if (M > 0) {
     nvfp4::GemmArgs l1{NVFP4_EPI_SWIGLU_NVFP4, a_q, a_sf, gs_a, perm, k, off, E, M, 2 * I, H,
-                       w1_q, w1_sf, gs_w1, gs_h, nullptr, h_q, h_sf, tp.h_f32, base + L.gws};
+                       w1_q, w1_sf, gs_w1, gs_h, nullptr, h_q, h_sf, tp.h_f32, base + L.gws,
+                       nvfp4::kGemmWorkspaceBytes};
     err = nvfp4::launch_grouped_gemm(l1, s);
     if (err != hipSuccess) return hip_fail(err, "moe_expert_forward L1");
     nvfp4::GemmArgs l2{NVFP4_EPI_BF16, h_q, h_sf, gs_h, nullptr, 1, off, E, M, H, I,
-                       w2_q, w2_sf, gs_w2, nullptr, y, nullptr, nullptr, nullptr, base + L.gws};
+                       w2_q, w2_sf, gs_w2, nullptr, y, nullptr, nullptr, nullptr, base + L.gws,
+                       nvfp4::kGemmWorkspaceBytes};
     err = nvfp4::launch_grouped_gemm(l2, s);
     if (err != hipSuccess) return hip_fail(err, "moe_expert_forward L2");
   }

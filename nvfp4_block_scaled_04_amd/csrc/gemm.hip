@@ -36,6 +36,12 @@
 // 128 K are double-buffered in LDS through registers.  In an expert's last
 // m tile, 32-token column blocks past the expert's rows are skipped.
 //
+// Split K.  When the tile list is too short to occupy every CU (a dense
+// linear of few rows), each tile's K stages are split into ksplit equal
+// ranges run as separate work items; they write fp32 partials (already
+// scaled by the global scales) to a caller workspace and a reduction kernel
+// sums them in split order and rounds to BF16.
+//
 // Scheduling.  A persistent grid (a multiple of 8 blocks) walks tiles in
 // windows of gridDim.x; within a window the 8 XCDs each take a contiguous
 // slice, so the blocks of one XCD share an expert's weights and tokens in
@@ -77,7 +83,13 @@ struct Params {
   float* c_debug;
   int* sched;       // per-XCD tile counters (8), zero at launch
   int n_tiles;
+  int ksplit;       // K ranges per tile (1: no split)
+  int nks_total;    // K / BK
+  float* partial;   // split K: fp32 [ksplit][M][N]
 };
+
+// epilogue of a split-K work item: fp32 partial sums (internal value)
+constexpr int kEpiPartial = 2;
 
 // 8 codes (one dword) -> 8 FP16 values times the block scale
 __device__ __forceinline__ half8v decode8(uint32_t w, _Float16 s) {
@@ -388,6 +400,7 @@ __device__ __forceinline__ void k_stage(KState<BN, BM, WN, WM, JV>& st, int ks, 
 struct Tile {
   int e, row0, nrows, jv;
   int64_t n0;
+  int split, ks_lo, nks;   // K range [ks_lo, ks_lo + nks) in stages
 };
 
 // Tile number `logical` (< number of tiles) of the expert-ordered tile list
@@ -396,8 +409,10 @@ struct Tile {
 // in scalar registers.
 template <int BN, int BM>
 __device__ __forceinline__ void tile_at(const Params& p, const int* tprefix, int logical, Tile& t) {
-  const int mt = logical / p.n_tiles;
-  const int nt = logical - mt * p.n_tiles;
+  const int tix = logical / p.ksplit;
+  const int split = logical - tix * p.ksplit;
+  const int mt = tix / p.n_tiles;
+  const int nt = tix - mt * p.n_tiles;
   // expert owning m tile mt: the largest e with tprefix[e] <= mt (fixed
   // steps, no loop: tprefix is non-decreasing and tprefix[0] = 0)
   int e = 0;
@@ -409,6 +424,9 @@ __device__ __forceinline__ void tile_at(const Params& p, const int* tprefix, int
   t.nrows = __builtin_amdgcn_readfirstlane(min(BM, p.offsets[t.e + 1] - t.row0));
   t.n0 = (int64_t)__builtin_amdgcn_readfirstlane(nt) * BN;
   t.jv = (t.nrows + 31) / 32;
+  t.split = __builtin_amdgcn_readfirstlane(split);
+  t.ks_lo = __builtin_amdgcn_readfirstlane(split * p.nks_total / p.ksplit);
+  t.nks = __builtin_amdgcn_readfirstlane((split + 1) * p.nks_total / p.ksplit) - t.ks_lo;
 }
 
 // Tile scheduling.  XCD x (blocks b with b % 8 == x) owns tiles
@@ -451,16 +469,25 @@ __device__ __forceinline__ int resolve_claim(Sched& sc, int k) {
 }
 
 // packed weights: tile (e, n0 / BN) is K/BK stages of BN rows (64 code bytes
-// and 8 scale bytes per row), rows zero-padded to a multiple of BN
+// and 8 scale bytes per row), rows zero-padded to a multiple of BN; the
+// pointers returned start at the tile's first K stage
 template <int BN>
 __device__ __forceinline__ const uint8_t* tile_wq(const Params& p, const Tile& t) {
   const int64_t Np = (p.N + BN - 1) / BN * BN;
-  return p.b_q + ((int64_t)t.e * Np + t.n0) * (p.K / 2);
+  return p.b_q + ((int64_t)t.e * Np + t.n0) * (p.K / 2) + (int64_t)t.ks_lo * (BN * ROW_BYTES);
 }
 template <int BN>
 __device__ __forceinline__ const uint8_t* tile_wsf(const Params& p, const Tile& t) {
   const int64_t Np = (p.N + BN - 1) / BN * BN;
-  return p.b_sf + ((int64_t)t.e * Np + t.n0) * (p.K / 16);
+  return p.b_sf + ((int64_t)t.e * Np + t.n0) * (p.K / 16) + (int64_t)t.ks_lo * (BN * SF_BYTES);
+}
+// token codes/scales from the tile's first K stage on (rows are added by the
+// per-lane load offsets)
+__device__ __forceinline__ const uint8_t* tile_aq(const Params& p, const Tile& t) {
+  return p.a_q + (int64_t)t.ks_lo * ROW_BYTES;
+}
+__device__ __forceinline__ const uint8_t* tile_asf(const Params& p, const Tile& t) {
+  return p.a_sf + (int64_t)t.ks_lo * SF_BYTES;
 }
 
 // Per-lane byte offsets (stage 0) of this wave's direct loads for tile t.
@@ -518,6 +545,8 @@ __device__ __forceinline__ bool run_tile(const Params& p, uint8_t* smem, const i
   const int64_t n0 = cur.n0;
   const uint8_t* wbase = tile_wq<BN>(p, cur);
   const uint8_t* wsbase = tile_wsf<BN>(p, cur);
+  const uint8_t* abase = tile_aq(p, cur);
+  const uint8_t* asbase = tile_asf(p, cur);
 
   KState<BN, BM, WN, WM, JV> st;
   st.wn = wn; st.wm = wm; st.hf = hf; st.l32 = l32;
@@ -529,20 +558,20 @@ __device__ __forceinline__ bool run_tile(const Params& p, uint8_t* smem, const i
       for (int r = 0; r < 16; ++r) st.acc[i][j][r] = 0.0f;
 
   // three LDS stage buffers, stage ks in buffer ks % 3
-  const int nks = (int)(K / BK);
+  const int nks = cur.nks;
   k_begin(st, nks, smem);
   int buf = 0;
   int ks = 0;
   for (; ks + 2 < nks; ++ks) {
     const int buf1 = buf == 2 ? 0 : buf + 1, buf2 = buf == 0 ? 2 : buf - 1;
-    k_stage<BN, BM, WN, WM, JV, 1>(st, ks, nks, wave, coff, soff, wbase, wsbase, p.a_q, p.a_sf,
+    k_stage<BN, BM, WN, WM, JV, 1>(st, ks, nks, wave, coff, soff, wbase, wsbase, abase, asbase,
                                    smem + buf * C::STAGE_BYTES, smem + buf1 * C::STAGE_BYTES,
                                    smem + buf2 * C::STAGE_BYTES);
     buf = buf1;
   }
   for (; ks < nks; ++ks) {
     const int buf1 = buf == 2 ? 0 : buf + 1, buf2 = buf == 0 ? 2 : buf - 1;
-    k_stage<BN, BM, WN, WM, JV, 0>(st, ks, nks, wave, coff, soff, wbase, wsbase, p.a_q, p.a_sf,
+    k_stage<BN, BM, WN, WM, JV, 0>(st, ks, nks, wave, coff, soff, wbase, wsbase, abase, asbase,
                                    smem + buf * C::STAGE_BYTES, smem + buf1 * C::STAGE_BYTES,
                                    smem + buf2 * C::STAGE_BYTES);
     buf = buf1;
@@ -564,13 +593,32 @@ __device__ __forceinline__ bool run_tile(const Params& p, uint8_t* smem, const i
   if (has_next) {
     if (tid == 0) claim = atomicAdd(sc.counters + sc.cx, 1);
     tile_offsets<BN, BM, WN, WM, EPI>(p, nxt, wave, lane, coff, soff);
-    k_issue_first<BN, BM, WN, WM>(nks, wave, coff, soff, tile_wq<BN>(p, nxt), tile_wsf<BN>(p, nxt),
-                                  p.a_q, p.a_sf, smem, smem + C::STAGE_BYTES);
+    k_issue_first<BN, BM, WN, WM>(nxt.nks, wave, coff, soff, tile_wq<BN>(p, nxt), tile_wsf<BN>(p, nxt),
+                                  tile_aq(p, nxt), tile_asf(p, nxt), smem, smem + C::STAGE_BYTES);
   }
 
   // ---- epilogue
   const float alpha = 1.0f / (p.gs_a[0] * p.gs_b[e]);
-  if constexpr (EPI == NVFP4_EPI_BF16) {
+  if constexpr (EPI == kEpiPartial) {
+    // fp32 partial sums of this K range: the lane's 4 contiguous columns of
+    // each (i, g) as one 16-byte store; summed by splitk_reduce_kernel
+    const int64_t nw0 = n0 + wn * TN;
+#pragma unroll
+    for (int j = 0; j < JV; ++j) {
+      const int tok = j * 32 + l32;
+      float* prow = p.partial + ((int64_t)cur.split * p.M + row0 + tok) * N + nw0 + 4 * hf;
+#pragma unroll
+      for (int i = 0; i < FN; ++i) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (tok >= nrows || nw0 + i * 32 >= N) continue;
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *reinterpret_cast<float4*>(prow + i * 32 + 8 * g) =
+              make_float4(acc[i][j][4 * g + 0] * alpha, acc[i][j][4 * g + 1] * alpha,
+                          acc[i][j][4 * g + 2] * alpha, acc[i][j][4 * g + 3] * alpha);
+      }
+    }
+  } else if constexpr (EPI == NVFP4_EPI_BF16) {
     // Each lane holds, for token j*32 + l32, output columns 32i + 8g + 4hf
     // .. +3 of the wave's TN: 8 contiguous bytes per (i, g).  The two lane
     // halves write 16 contiguous bytes of a token row per store and the four
@@ -687,9 +735,8 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_gemm_kernel(Params p)
   }
   __shared__ int s_claim[4];
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  const int nks = (int)(p.K / BK);
   Sched sc;
-  sc.total = (int64_t)tprefix[p.E] * p.n_tiles;
+  sc.total = (int64_t)tprefix[p.E] * p.n_tiles * p.ksplit;
   sc.counters = p.sched;
   sc.s_claim = s_claim;
   sc.cx = blockIdx.x & 7;                  // own XCD (blocks are dispatched round-robin)
@@ -704,8 +751,8 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_gemm_kernel(Params p)
   if (have) {
     tile_at<BN, BM>(p, tprefix, t0, cur);
     tile_offsets<BN, BM, WN, WM, EPI>(p, cur, wave, lane, coff, soff);
-    k_issue_first<BN, BM, WN, WM>(nks, wave, coff, soff, tile_wq<BN>(p, cur), tile_wsf<BN>(p, cur),
-                                  p.a_q, p.a_sf, smem, smem + C::STAGE_BYTES);
+    k_issue_first<BN, BM, WN, WM>(cur.nks, wave, coff, soff, tile_wq<BN>(p, cur), tile_wsf<BN>(p, cur),
+                                  tile_aq(p, cur), tile_asf(p, cur), smem, smem + C::STAGE_BYTES);
   }
   while (have) {
     Tile nxt;
@@ -728,7 +775,70 @@ __global__ void zero_ints_kernel(int* p, int n) {
   if ((int)threadIdx.x < n) p[threadIdx.x] = 0;
 }
 
+// c[d][n] = bf16_rne(sum over s in order of partial[s][d][n]) for the rows
+// d < offsets[E] (the rows the GEMM defines); 8 columns per thread
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ partial,
+                                                            int ksplit, int64_t M, int64_t N,
+                                                            const int32_t* __restrict__ offsets,
+                                                            int E, uint16_t* __restrict__ c) {
+  const int64_t rows = offsets[E];
+  const int64_t per_row = N / 8;
+  const int64_t total = rows * per_row;
+  for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < total;
+       v += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t off = v * 8;
+    float4 lo = *reinterpret_cast<const float4*>(partial + off);
+    float4 hi = *reinterpret_cast<const float4*>(partial + off + 4);
+    for (int s = 1; s < ksplit; ++s) {
+      const float4 a = *reinterpret_cast<const float4*>(partial + s * M * N + off);
+      const float4 b = *reinterpret_cast<const float4*>(partial + s * M * N + off + 4);
+      lo.x += a.x; lo.y += a.y; lo.z += a.z; lo.w += a.w;
+      hi.x += b.x; hi.y += b.y; hi.z += b.z; hi.w += b.w;
+    }
+    uint4 o;
+    o.x = pack_bf16x2(lo.x, lo.y);
+    o.y = pack_bf16x2(lo.z, lo.w);
+    o.z = pack_bf16x2(hi.x, hi.y);
+    o.w = pack_bf16x2(hi.z, hi.w);
+    *reinterpret_cast<uint4*>(c + off) = o;
+  }
+}
+
 int g_cu_count = 0;
+
+hipError_t query_cu_count() {
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  return hipDeviceGetAttribute(&g_cu_count, hipDeviceAttributeMultiprocessorCount, dev);
+}
+
+constexpr int kBN = 512, kBM = 128;   // the tile every launch uses
+
+// upper bound on the tile count: sum over experts of ceil(rows_e / BM)
+// <= (M + E * (BM - 1)) / BM m tiles, times the n tiles
+int64_t tile_bound(int64_t M, int64_t N, int E) {
+  return (M + (int64_t)E * (kBM - 1)) / kBM * ((N + kBN - 1) / kBN);
+}
+
+// K ranges per tile: 1, unless a BF16-epilogue launch has at most half as
+// many tiles as the device has CUs; then enough ranges to cover the CUs, at
+// most 4 and at least 4 K stages each
+int splitk_factor(int epilogue, int64_t M, int64_t N, int64_t K, int E, int cus) {
+  if (epilogue != NVFP4_EPI_BF16 || M == 0 || cus <= 0) return 1;
+  const int64_t tiles = tile_bound(M, N, E);
+  if (2 * tiles > cus) return 1;
+  int64_t f = cus / tiles;
+  if (f > 4) f = 4;
+  while (f > 1 && K / BK / f < 4) --f;
+  return (int)f;
+}
+
+// fp32 partials follow the scheduler counters, 256-byte aligned
+float* splitk_partial(void* ws) {
+  const uintptr_t b = reinterpret_cast<uintptr_t>(ws) + kGemmWorkspaceBytes;
+  return reinterpret_cast<float*>((b + 255) & ~uintptr_t(255));
+}
 
 template <int BN, int BM, int WN, int WM, int EPI>
 hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
@@ -740,16 +850,19 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
   p.c_bf16 = static_cast<uint16_t*>(a.c_bf16); p.c_q = a.c_q; p.c_sf = a.c_sf; p.c_debug = a.c_debug;
   p.sched = static_cast<int*>(a.ws);
   p.n_tiles = (int)((a.N + BN - 1) / BN);
+  p.nks_total = (int)(a.K / BK);
+  p.ksplit = 1;
+  p.partial = nullptr;
   if (a.M == 0) return hipSuccess;
   if (g_cu_count == 0) {
-    int dev = 0;
-    hipError_t err = hipGetDevice(&dev);
-    if (err != hipSuccess) return err;
-    err = hipDeviceGetAttribute(&g_cu_count, hipDeviceAttributeMultiprocessorCount, dev);
+    hipError_t err = query_cu_count();
     if (err != hipSuccess) return err;
   }
-  const int64_t m_tiles = (a.M + BM - 1) / BM + a.E;   // upper bound on sum ceil(count/BM)
-  const int64_t tiles = m_tiles * p.n_tiles;
+  if (EPI == kEpiPartial) {
+    p.ksplit = splitk_factor(a.epilogue, a.M, a.N, a.K, a.E, g_cu_count);
+    p.partial = splitk_partial(a.ws);
+  }
+  const int64_t tiles = tile_bound(a.M, a.N, a.E) * p.ksplit;
   int64_t grid = g_cu_count;                              // one block per CU (LDS-limited)
   if (grid > tiles) grid = tiles;
   grid = (grid + 7) / 8 * 8;
@@ -765,15 +878,34 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
   }
   zero_ints_kernel<<<1, 64, 0, stream>>>(p.sched, 8);   // a kernel, not a memset: graph-safe
   kern<<<(unsigned)grid, C::NT, lds, stream>>>(p);
+  if (EPI == kEpiPartial) {
+    const int64_t vecs = a.M * a.N / 8;
+    int64_t blocks = (vecs + 255) / 256;
+    if (blocks > 8 * (int64_t)g_cu_count) blocks = 8 * (int64_t)g_cu_count;
+    splitk_reduce_kernel<<<(unsigned)blocks, 256, 0, stream>>>(
+        p.partial, p.ksplit, a.M, a.N, a.offsets, a.E, static_cast<uint16_t*>(a.c_bf16));
+  }
   return hipGetLastError();
 }
 
 }  // namespace
 
+size_t gemm_splitk_ws_bytes(int epilogue, int64_t M, int64_t N, int64_t K, int E) {
+  if (g_cu_count == 0 && query_cu_count() != hipSuccess) return kGemmWorkspaceBytes;
+  const int f = splitk_factor(epilogue, M, N, K, E, g_cu_count);
+  if (f <= 1) return kGemmWorkspaceBytes;
+  return kGemmWorkspaceBytes + 255 + (size_t)f * (size_t)M * (size_t)N * sizeof(float);
+}
+
 hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t stream) {
   if (a.epilogue == NVFP4_EPI_SWIGLU_NVFP4)
-    return launch_cfg<512, 128, 4, 1, NVFP4_EPI_SWIGLU_NVFP4>(a, stream);
-  return launch_cfg<512, 128, 4, 1, NVFP4_EPI_BF16>(a, stream);
+    return launch_cfg<kBN, kBM, 4, 1, NVFP4_EPI_SWIGLU_NVFP4>(a, stream);
+  // split K only when the caller's workspace holds the partials
+  if (a.M > 0 && a.ws_bytes > kGemmWorkspaceBytes &&
+      a.ws_bytes >= gemm_splitk_ws_bytes(a.epilogue, a.M, a.N, a.K, a.E) &&
+      splitk_factor(a.epilogue, a.M, a.N, a.K, a.E, g_cu_count) > 1)
+    return launch_cfg<kBN, kBM, 4, 1, kEpiPartial>(a, stream);
+  return launch_cfg<kBN, kBM, 4, 1, NVFP4_EPI_BF16>(a, stream);
 }
 
 }  // namespace nvfp4

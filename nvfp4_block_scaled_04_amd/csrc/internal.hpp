@@ -54,9 +54,14 @@ struct GemmArgs {
   uint8_t* c_q;
   uint8_t* c_sf;
   float* c_debug;
-  void* ws;         // kGemmWorkspaceBytes: the tile scheduler's counters
+  void* ws;         // the tile scheduler's counters (kGemmWorkspaceBytes), then
+                    // room for split-K partials if ws_bytes allows
+  size_t ws_bytes;
 };
 constexpr size_t kGemmWorkspaceBytes = 256;
+// workspace with which a launch of this shape splits K (kGemmWorkspaceBytes
+// when it would not split)
+size_t gemm_splitk_ws_bytes(int epilogue, int64_t M, int64_t N, int64_t K, int E);
 hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t stream);
 constexpr int kRouterMaxExperts = 1024;
 hipError_t launch_router_topk(const float* logits, int64_t T, int E, int k, int32_t* topk_ids,

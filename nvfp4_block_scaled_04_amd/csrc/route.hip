@@ -5,11 +5,13 @@
 // quantise the compact rows, then place them.
 //
 // The flat pairs f = t*k + j are cut into C chunks of `chunk` entries.
-//   route_hist     grid C:  LDS histogram of each chunk -> ws[c][E+1]
-//                           (bucket E collects ids outside [0, E))
-//   route_scan     1 block: per bucket, exclusive prefix over chunks; then an
-//                           exclusive scan over buckets -> expert offsets;
-//                           ws[c][b] becomes chunk c's first output row of b
+//   route_hist     grid C:  LDS histogram of each chunk -> hist[b][c], bucket-
+//                           major (bucket E collects ids outside [0, E))
+//   route_scan     1 block: one wave per bucket at a time: the bucket's total
+//                           over chunks, an exclusive scan of the totals over
+//                           buckets -> expert offsets, then the wave's
+//                           exclusive scan over chunks turns hist[b][c] into
+//                           chunk c's first output row of bucket b
 //   route_scatter  grid C, one wave: walks its chunk in order, 64 entries at
 //                           a time; a lane's rank among equal buckets of the
 //                           batch comes from a ballot, so every bucket keeps
@@ -23,7 +25,7 @@ namespace {
 
 constexpr int kHistThreads = 256;
 constexpr int kScanThreads = 1024;
-constexpr int64_t kMinChunk = 1024;
+constexpr int64_t kMinChunk = 256;
 constexpr int64_t kMaxChunks = 1024;
 
 int64_t chunk_size(int64_t M) {
@@ -37,7 +39,8 @@ __device__ __forceinline__ int bucket_of(int32_t id, int E) {
 }
 
 __global__ __launch_bounds__(kHistThreads) void route_hist_kernel(
-    const int32_t* __restrict__ ids, int64_t M, int64_t chunk, int E, int32_t* __restrict__ hist) {
+    const int32_t* __restrict__ ids, int64_t M, int64_t chunk, int64_t C, int E,
+    int32_t* __restrict__ hist) {
   extern __shared__ int32_t cnt[];
   const int nb = E + 1;
   for (int b = threadIdx.x; b < nb; b += kHistThreads) cnt[b] = 0;
@@ -48,8 +51,17 @@ __global__ __launch_bounds__(kHistThreads) void route_hist_kernel(
     atomicAdd(&cnt[bucket_of(ids[f], E)], 1);
   }
   __syncthreads();
-  int32_t* h = hist + (int64_t)blockIdx.x * nb;
-  for (int b = threadIdx.x; b < nb; b += kHistThreads) h[b] = cnt[b];
+  for (int b = threadIdx.x; b < nb; b += kHistThreads) hist[(int64_t)b * C + blockIdx.x] = cnt[b];
+}
+
+// inclusive prefix sum over the 64 lanes of a wave
+__device__ __forceinline__ int32_t wave_incl_scan(int32_t v, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int32_t u = __shfl_up(v, off, 64);
+    if (lane >= off) v += u;
+  }
+  return v;
 }
 
 __global__ __launch_bounds__(kScanThreads) void route_scan_kernel(
@@ -59,15 +71,16 @@ __global__ __launch_bounds__(kScanThreads) void route_scan_kernel(
   const int nb = E + 1;
   int32_t* total = sm;
   int32_t* part = sm + nb;
-  // per-bucket exclusive prefix over chunks
-  for (int b = threadIdx.x; b < nb; b += kScanThreads) {
-    int32_t run = 0;
-    for (int64_t c = 0; c < C; ++c) {
-      const int32_t v = hist[c * nb + b];
-      hist[c * nb + b] = run;
-      run += v;
-    }
-    total[b] = run;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int kWaves = kScanThreads / 64;
+  // per-bucket total over chunks (one wave per bucket)
+  for (int b = wave; b < nb; b += kWaves) {
+    const int32_t* h = hist + (int64_t)b * C;
+    int32_t s = 0;
+    for (int64_t c = lane; c < C; c += 64) s += h[c];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
+    if (lane == 0) total[b] = s;
   }
   __syncthreads();
   // exclusive scan of total[0..nb): each thread owns a contiguous segment
@@ -94,9 +107,18 @@ __global__ __launch_bounds__(kScanThreads) void route_scan_kernel(
     }
   }
   __syncthreads();
-  for (int b = threadIdx.x; b < nb; b += kScanThreads) {
-    offsets[b] = total[b];
-    for (int64_t c = 0; c < C; ++c) hist[c * nb + b] += total[b];
+  // hist[b][c] -> base of b + rows of b in chunks before c
+  for (int b = wave; b < nb; b += kWaves) {
+    int32_t* h = hist + (int64_t)b * C;
+    int32_t base = total[b];
+    for (int64_t c0 = 0; c0 < C; c0 += 64) {
+      const int64_t c = c0 + lane;
+      const int32_t v = c < C ? h[c] : 0;
+      const int32_t incl = wave_incl_scan(v, lane);
+      if (c < C) h[c] = base + incl - v;
+      base += __shfl(incl, 63, 64);
+    }
+    if (lane == 0) offsets[b] = total[b];
   }
   if (threadIdx.x == 0 && invalid_count != nullptr) {
     // bucket E's size: M - offsets[E], recovered from the last segment
@@ -105,13 +127,12 @@ __global__ __launch_bounds__(kScanThreads) void route_scan_kernel(
 }
 
 __global__ __launch_bounds__(64) void route_scatter_kernel(
-    const int32_t* __restrict__ ids, int64_t M, int64_t chunk, int E,
+    const int32_t* __restrict__ ids, int64_t M, int64_t chunk, int64_t C, int E,
     const int32_t* __restrict__ hist, int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm) {
   extern __shared__ int32_t cur[];
   const int nb = E + 1;
   const int lane = threadIdx.x;
-  const int32_t* h = hist + (int64_t)blockIdx.x * nb;
-  for (int b = lane; b < nb; b += 64) cur[b] = h[b];
+  for (int b = lane; b < nb; b += 64) cur[b] = hist[(int64_t)b * C + blockIdx.x];
   __syncthreads();
   const int64_t lo = (int64_t)blockIdx.x * chunk;
   const int64_t hi = lo + chunk < M ? lo + chunk : M;
@@ -167,12 +188,12 @@ hipError_t launch_route(const int32_t* topk_ids, int64_t T, int k, int E, int32_
   int32_t* hist = static_cast<int32_t*>(ws);
   const size_t lds_hist = (size_t)(E + 1) * sizeof(int32_t);
   if (C > 0) {
-    route_hist_kernel<<<(unsigned)C, kHistThreads, lds_hist, stream>>>(topk_ids, M, ch, E, hist);
+    route_hist_kernel<<<(unsigned)C, kHistThreads, lds_hist, stream>>>(topk_ids, M, ch, C, E, hist);
   }
   route_scan_kernel<<<1, kScanThreads, lds_hist + kScanThreads * sizeof(int32_t), stream>>>(
       hist, C, E, offsets, invalid_count);
   if (C > 0) {
-    route_scatter_kernel<<<(unsigned)C, 64, lds_hist, stream>>>(topk_ids, M, ch, E, hist, perm,
+    route_scatter_kernel<<<(unsigned)C, 64, lds_hist, stream>>>(topk_ids, M, ch, C, E, hist, perm,
                                                                 inv_perm);
   }
   return hipGetLastError();

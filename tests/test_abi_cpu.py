@@ -107,6 +107,11 @@ def test_gemm_rejects(L):
 def test_gemm_workspace(L):
     need = L.nvfp4_grouped_gemm_workspace_size()
     assert need >= 32                                     # eight 32-bit counters
+    # the split-K size is never below the minimum (and is the minimum for
+    # invalid shapes or when no device can be queried)
+    assert L.nvfp4_grouped_gemm_splitk_workspace_size(0, 4096, 2048, 7168, 1) >= need
+    assert L.nvfp4_grouped_gemm_splitk_workspace_size(0, -1, 2048, 7168, 1) == need
+    assert L.nvfp4_grouped_gemm_splitk_workspace_size(1, 4096, 2048, 7168, 1) == need  # SwiGLU
     assert _gemm(L, ws=None, wsb=0) == -3
     assert _gemm(L, wsb=need - 1) == -3
     assert _gemm(L, ws=FAKE + 2) == -3                    # not 4-byte aligned

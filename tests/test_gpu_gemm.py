@@ -21,7 +21,7 @@ def _randn(shape, seed, std=1.0):
     return (torch.randn(shape, generator=g, device=DEV) * std).to(torch.bfloat16)
 
 
-def _grouped_case(counts, N, K, seed, epi, gather_k=None, T=0):
+def _grouped_case(counts, N, K, seed, epi, gather_k=None, T=0, split_ws=False):
     """Random grouped problem with the given rows per expert, or (gather_k)
     T tokens routed to gather_k distinct experts each, rows gathered by perm."""
     E = len(counts)
@@ -48,8 +48,13 @@ def _grouped_case(counts, N, K, seed, epi, gather_k=None, T=0):
     b_q, b_sf, gs_b = nv.quantize(w, groups=E)
     b = nv.pack_weights(b_q.view(E, N, K // 2), b_sf.view(E, N, K // 16))
     gs_out = torch.tensor([64.0], device=DEV)
+    ws = None
+    if split_ws:
+        nbytes = nv.gemm_splitk_workspace_bytes(epi, M, N, K, E)
+        print(f"[case] split-K workspace {nbytes} bytes", flush=True)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
     res = nv.grouped_gemm(epi, a_q, a_sf, gs_a, off, b, gs_b, M, a_row_src=src,
-                          a_row_div=gather_k or 1, gs_out=gs_out, debug=True)
+                          a_row_div=gather_k or 1, gs_out=gs_out, debug=True, workspace=ws)
     torch.cuda.synchronize()
     # oracle from the same bf16 inputs
     aq, asf, ga = Q.quantize_nvfp4(host(x))
@@ -66,6 +71,30 @@ def _grouped_case(counts, N, K, seed, epi, gather_k=None, T=0):
 ])
 def test_grouped_bf16_epilogue(counts, N, K):
     res, (aq, asf, ga, bq, bsf, gb, off, rows) = _grouped_case(counts, N, K, 11, nv.EPI_BF16)
+    got = bf16_values(host(res))
+    for e in range(len(counts)):
+        lo, hi = off[e], off[e + 1]
+        if hi == lo:
+            continue
+        ref = bf16_values(O.round_to_bf16(
+            O.nvfp4_matmul(aq[rows[lo:hi]], asf[rows[lo:hi]], ga, bq[e], bsf[e], gb[e])))
+        assert_close(got[lo:hi], ref, f"expert {e}")
+
+
+@pytest.mark.parametrize("counts,N,K", [
+    ([5, 0, 130, 1, 64, 200], 96, 1024),      # 8 K stages: 2 parts
+    ([5, 0, 130, 1, 64, 200], 96, 1152),      # 9 stages: parts of 4 and 5
+    ([300], 512, 2048),                       # 16 stages: 4 parts
+    ([0, 1], 32, 512),                        # one row, 4 stages: no split
+])
+def test_grouped_bf16_split_k(counts, N, K):
+    """Launches with few tiles split K when the workspace allows it; each
+    part's fp32 partials are summed in order by a second kernel."""
+    res, (aq, asf, ga, bq, bsf, gb, off, rows) = _grouped_case(counts, N, K, 13, nv.EPI_BF16,
+                                                               split_ws=True)
+    nbytes = nv.gemm_splitk_workspace_bytes(nv.EPI_BF16, int(sum(counts)), N, K, len(counts))
+    if K // 128 >= 8:
+        assert nbytes > nv.gemm_workspace_bytes(), "this launch is expected to split K"
     got = bf16_values(host(res))
     for e in range(len(counts)):
         lo, hi = off[e], off[e + 1]
@@ -96,7 +125,8 @@ def test_grouped_swiglu_epilogue(counts, N, K, gk, T):
         assert_requant_matches(gq[lo:hi], gsf[lo:hi], ref_h, 64.0, f"requant expert {e}")
 
 
-def test_dense_linear_config2_sampled_rows():
+@pytest.mark.parametrize("split", [False, True])
+def test_dense_linear_config2_sampled_rows(split):
     w = I.WORKLOADS["dense"]
     M, K, N = w.dense_mkn
     print(f"[case] dense M={M} K={K} N={N}", flush=True)
@@ -105,8 +135,15 @@ def test_dense_linear_config2_sampled_rows():
     bk = nv.weight_layout(b.view(1, K, N), False)[0]              # (N, K)
     b_q, b_sf, gs_b = nv.quantize(bk)
     off = torch.tensor([0, M], dtype=torch.int32, device=DEV)
+    ws = None
+    if split:
+        nbytes = nv.gemm_splitk_workspace_bytes(nv.EPI_BF16, M, N, K, 1)
+        print(f"[case] dense split-K workspace {nbytes} bytes", flush=True)
+        assert nbytes > nv.gemm_workspace_bytes(), "128 tiles on 256 CUs are expected to split K"
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
     c = nv.grouped_gemm(nv.EPI_BF16, a_q, a_sf, gs_a, off,
-                        nv.pack_weights(b_q.view(1, N, K // 2), b_sf.view(1, N, K // 16)), gs_b, M)
+                        nv.pack_weights(b_q.view(1, N, K // 2), b_sf.view(1, N, K // 16)), gs_b, M,
+                        workspace=ws)
     torch.cuda.synchronize()
     ab, bb = host(a), host(b)
     gsa = Q.global_scale(ab)
