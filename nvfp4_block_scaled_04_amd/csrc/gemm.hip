@@ -404,23 +404,29 @@ struct Tile {
 };
 
 // Tile number `logical` (< number of tiles) of the expert-ordered tile list
-// (m tiles of BM rows, n tiles innermost).  tprefix: per-expert m-tile
-// prefix (E <= 4096).  The fields are wave-uniform: readfirstlane keeps them
-// in scalar registers.
+// (per expert: n tiles, and inside each n tile the expert's m tiles of BM
+// rows, so the tiles that read one weight n tile are neighbours in the list
+// and run side by side; split-K parts innermost).  tprefix: per-expert
+// m-tile prefix (E <= 4096).  The fields are wave-uniform: readfirstlane
+// keeps them in scalar registers.
 template <int BN, int BM>
 __device__ __forceinline__ void tile_at(const Params& p, const int* tprefix, int logical, Tile& t) {
   const int tix = logical / p.ksplit;
   const int split = logical - tix * p.ksplit;
-  const int mt = tix / p.n_tiles;
-  const int nt = tix - mt * p.n_tiles;
-  // expert owning m tile mt: the largest e with tprefix[e] <= mt (fixed
-  // steps, no loop: tprefix is non-decreasing and tprefix[0] = 0)
+  // expert e owns tiles [tprefix[e] * n_tiles, tprefix[e + 1] * n_tiles):
+  // the largest e with tprefix[e] <= tix / n_tiles (fixed steps, no loop:
+  // tprefix is non-decreasing and tprefix[0] = 0)
+  const int mg = tix / p.n_tiles;
   int e = 0;
 #pragma unroll
   for (int step = 2048; step > 0; step >>= 1)
-    if (e + step < p.E && tprefix[e + step] <= mt) e += step;
+    if (e + step < p.E && tprefix[e + step] <= mg) e += step;
   t.e = __builtin_amdgcn_readfirstlane(e);
-  t.row0 = __builtin_amdgcn_readfirstlane(p.offsets[t.e] + (mt - tprefix[t.e]) * BM);
+  const int mcount = tprefix[t.e + 1] - tprefix[t.e];
+  const int local = tix - tprefix[t.e] * p.n_tiles;
+  const int nt = local / mcount;
+  const int mt = local - nt * mcount;
+  t.row0 = __builtin_amdgcn_readfirstlane(p.offsets[t.e] + mt * BM);
   t.nrows = __builtin_amdgcn_readfirstlane(min(BM, p.offsets[t.e + 1] - t.row0));
   t.n0 = (int64_t)__builtin_amdgcn_readfirstlane(nt) * BN;
   t.jv = (t.nrows + 31) / 32;
