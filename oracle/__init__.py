@@ -22,4 +22,4 @@ format definitions, closed forms, brute force and hand-worked fixtures under
 ``tests/golden/``.  No function is "parity unpinned".
 """
 
-from . import formats, quantize, route, layout, moe  # noqa: F401
+from . import formats, quantize, route, layout, moe, mx  # noqa: F401
