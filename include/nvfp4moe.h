@@ -215,6 +215,52 @@ nvfp4_status nvfp4_grouped_gemm(int epilogue, const uint8_t* a_q, const uint8_t*
                                 size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * MX variant: NVFP4 re-encoded for the block-scaled FP4 matrix instructions.
+ * README "What We Have", grouped GEMM, carries E2M1 values with E4M3 scales
+ * per 16 elements; gfx950's scaled FP4 MFMA (v_mfma_scale_f32_32x32x64_f8f6f4)
+ * takes E2M1 values with one power-of-two E8M0 scale per 32 elements (OCP
+ * Microscaling).  These entry points re-encode NVFP4 data into that form and
+ * run the grouped GEMM and the whole forward on it.  The re-encoding rounds:
+ * results approximate the NVFP4 ones (they are not the NVFP4 results up to
+ * summation order, as nvfp4_grouped_gemm's are).
+ *
+ * nvfp4_to_mx: q uint8 [rows][cols/2] E2M1 codes and sf uint8 [rows][cols/16]
+ * E4M3 scales (as written by nvfp4_quantize) -> q_mx [rows][cols/2] and
+ * sc_mx [rows][cols/16].  Per 32-block j of a row (NVFP4 blocks 2j, 2j+1):
+ *   u_i = E2M1(q_i) * E4M3(sf) (exact); amax = max |u_i|;
+ *   amax == 0: scale byte 0, codes 0;
+ *   else X = 2^(floor(log2 amax) - 2) (MX conversion, E2M1 emax 2), E8M0 byte
+ *   floor(log2 amax) - 2 + 127, code_i = signbit(q_i) << 3 | E2M1(min(|u_i|/X, 6))
+ *   (nearest, ties to the even code);
+ *   the E8M0 byte is stored at sc_mx bytes 2j and 2j+1 (the NVFP4 scale
+ *   layout, so nvfp4_pack_weights packs MX weights unchanged).
+ * The global scale of the NVFP4 data carries over unchanged.
+ * Shapes: rows >= 0, cols % 32 == 0.  In place (q_mx == q, sc_mx == sf) is
+ * allowed; otherwise outputs must not overlap inputs.  No workspace.
+ *
+ * nvfp4_mx_grouped_gemm: nvfp4_grouped_gemm (same arguments, rules, shapes,
+ * split K and workspace) on MXFP4 operands: a_q/a_sc from nvfp4_to_mx,
+ * b_q/b_sc = nvfp4_pack_weights of nvfp4_to_mx output;
+ *   acc[d][n] = sum_k E2M1(a) * E8M0(a) * E2M1(b) * E8M0(b) / (gs_a * gs_b[e]).
+ * The SwiGLU epilogue still writes NVFP4 (E4M3 scales) with gs_out.
+ *
+ * moe_expert_forward_mx: moe_expert_forward (same arguments, workspace and
+ * taps) with w1/w2 packed from nvfp4_to_mx of the NVFP4 weights; the
+ * quantised x and the requantised h are re-encoded in place with nvfp4_to_mx
+ * before the GEMM that reads them, so the taps a_q/a_sf and h_q/h_sf receive
+ * the MX forms.
+ * ---------------------------------------------------------------------- */
+nvfp4_status nvfp4_to_mx(const uint8_t* q, const uint8_t* sf, int64_t rows, int64_t cols,
+                         uint8_t* q_mx, uint8_t* sc_mx, void* stream);
+nvfp4_status nvfp4_mx_grouped_gemm(int epilogue, const uint8_t* a_q, const uint8_t* a_sc,
+                                   const float* gs_a, const int32_t* a_row_src, int a_row_div,
+                                   const int32_t* expert_offsets, int E, int64_t M, int64_t N,
+                                   int64_t K, const uint8_t* b_q, const uint8_t* b_sc,
+                                   const float* gs_b, const float* gs_out, void* c_bf16,
+                                   uint8_t* c_q, uint8_t* c_sf, float* c_debug_f32, void* ws,
+                                   size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Routing-weighted combine.
  * README "What We Have", MoE runner step 6: scatter with routing weights.
  *
@@ -270,6 +316,14 @@ nvfp4_status moe_expert_forward(const void* x_bf16, int64_t T, int64_t H, int64_
                                 const uint8_t* w2_q, const uint8_t* w2_sf, const float* gs_w2,
                                 const float* gs_h, void* out_bf16, const nvfp4_moe_taps* taps,
                                 void* ws, size_t ws_bytes, void* stream);
+
+/* MX variant of moe_expert_forward (see nvfp4_to_mx above). */
+nvfp4_status moe_expert_forward_mx(const void* x_bf16, int64_t T, int64_t H, int64_t I, int E,
+                                   int k, const int32_t* topk_ids, const float* topk_w,
+                                   const uint8_t* w1_q, const uint8_t* w1_sc, const float* gs_w1,
+                                   const uint8_t* w2_q, const uint8_t* w2_sc, const float* gs_w2,
+                                   const float* gs_h, void* out_bf16, const nvfp4_moe_taps* taps,
+                                   void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -46,6 +46,7 @@ SIGNATURES = {
                                    c_int, c_int64, c_int64, c_int64, c_void_p, c_void_p, c_void_p,
                                    c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                    c_size_t, c_void_p]),
+    "nvfp4_to_mx": (c_int, [c_void_p, c_void_p, c_int64, c_int64, c_void_p, c_void_p, c_void_p]),
     "nvfp4_moe_combine": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_int64, c_int, c_int,
                                   c_int64, c_void_p, c_void_p]),
     "moe_expert_forward_workspace_size": (c_size_t, [c_int64, c_int64, c_int64, c_int, c_int]),
@@ -54,6 +55,9 @@ SIGNATURES = {
                                    c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
                                    c_void_p]),
 }
+# the MX variants take the same arguments as their NVFP4 counterparts
+SIGNATURES["nvfp4_mx_grouped_gemm"] = SIGNATURES["nvfp4_grouped_gemm"]
+SIGNATURES["moe_expert_forward_mx"] = SIGNATURES["moe_expert_forward"]
 
 
 class Taps(ctypes.Structure):
@@ -153,6 +157,23 @@ def pack_weights(q, sf):
     return PackedWeight(qp, sfp, E, N, K)
 
 
+def to_mx(q, sf, out=None):
+    """NVFP4 (q (R, C/2), E4M3 sf (R, C/16)) -> MXFP4 (q_mx (R, C/2), E8M0
+    sc_mx (R, C/16), each scale byte stored twice); out may be (q, sf) for an
+    in-place re-encoding."""
+    _dev(q, torch.uint8, "q")
+    R, Ch = q.shape[0], q.shape[-1]
+    C = Ch * 2
+    _dev(sf, torch.uint8, "sf")
+    if sf.numel() != q.numel() // 8:
+        raise ValueError("sf must hold one byte per 16 elements of q")
+    rows = q.numel() // Ch
+    qm, sm = out if out is not None else (torch.empty_like(q), torch.empty_like(sf))
+    _check(lib().nvfp4_to_mx(_ptr(q), _ptr(sf), rows, C, _ptr(qm), _ptr(sm), _stream(q.device)),
+           "nvfp4_to_mx")
+    return qm, sm
+
+
 def quantize(x, groups=1, gs_in=None, out=None):
     """x (R, C) bf16 -> (q (R, C/2) u8, sf (R, C/16) u8, gs (groups,) f32)."""
     _dev(x, torch.bfloat16, "x")
@@ -220,7 +241,7 @@ def gemm_splitk_workspace_bytes(epilogue, M, N, K, E):
 
 
 def grouped_gemm(epilogue, a_q, a_sf, gs_a, offsets, b: PackedWeight, gs_b, M, a_row_src=None,
-                 a_row_div=1, gs_out=None, debug=False, out=None, workspace=None):
+                 a_row_div=1, gs_out=None, debug=False, out=None, workspace=None, mx=False):
     """Expert-grouped NVFP4 GEMM with packed B.  BF16 epilogue returns c (M, N)
     bf16; the SwiGLU epilogue returns (c_q (M, N/4), c_sf (M, N/32), h f32
     (M, N/2) or None).  workspace: uint8 tensor of at least
@@ -252,10 +273,11 @@ def grouped_gemm(epilogue, a_q, a_sf, gs_a, offsets, b: PackedWeight, gs_b, M, a
     ws = workspace if workspace is not None else torch.empty(gemm_workspace_bytes(), dtype=torch.uint8,
                                                              device=dev)
     _dev(ws, torch.uint8, "workspace")
-    _check(lib().nvfp4_grouped_gemm(epilogue, _ptr(a_q), _ptr(a_sf), _ptr(gs_a), _ptr(a_row_src),
-                                    a_row_div, _ptr(offsets), E, M, N, K, _ptr(b.q), _ptr(b.sf),
-                                    _ptr(gs_b), _ptr(gs_out), _ptr(c), _ptr(c_q), _ptr(c_sf),
-                                    _ptr(dbg), _ptr(ws), ws.numel(), _stream(dev)), "nvfp4_grouped_gemm")
+    fn = lib().nvfp4_mx_grouped_gemm if mx else lib().nvfp4_grouped_gemm
+    _check(fn(epilogue, _ptr(a_q), _ptr(a_sf), _ptr(gs_a), _ptr(a_row_src), a_row_div, _ptr(offsets),
+              E, M, N, K, _ptr(b.q), _ptr(b.sf), _ptr(gs_b), _ptr(gs_out), _ptr(c), _ptr(c_q),
+              _ptr(c_sf), _ptr(dbg), _ptr(ws), ws.numel(), _stream(dev)),
+           "nvfp4_mx_grouped_gemm" if mx else "nvfp4_grouped_gemm")
     return c if epilogue == EPI_BF16 else (c_q, c_sf, dbg)
 
 
@@ -279,9 +301,10 @@ class ExpertWeights:
     interleaved gate/up) and L2 (`w2`) weights with per-expert global scales;
     optionally the row-major NVFP4 arrays they were packed from."""
 
-    def __init__(self, w1: PackedWeight, gs_w1, w2: PackedWeight, gs_w2, rowmajor=None):
+    def __init__(self, w1: PackedWeight, gs_w1, w2: PackedWeight, gs_w2, rowmajor=None, mx=False):
         self.w1, self.gs_w1, self.w2, self.gs_w2 = w1, gs_w1, w2, gs_w2
         self.rowmajor = rowmajor or {}
+        self.mx = mx          # packed from nvfp4_to_mx output (MX variant)
 
     @property
     def E(self):
@@ -323,11 +346,11 @@ def moe_expert_forward(x, topk_ids, topk_w, w: ExpertWeights, gs_h, out=None, ta
     tp = None
     if taps:
         tp = Taps(**{name: t.data_ptr() for name, t in taps.items()})
-    _check(L.moe_expert_forward(_ptr(x), T, H, I, E, k, _ptr(topk_ids), _ptr(topk_w), _ptr(w.w1.q),
-                                _ptr(w.w1.sf), _ptr(w.gs_w1), _ptr(w.w2.q), _ptr(w.w2.sf),
-                                _ptr(w.gs_w2), _ptr(gs_h), _ptr(o),
-                                ctypes.byref(tp) if tp is not None else None, _ptr(ws), ws.numel(),
-                                _stream(dev)), "moe_expert_forward")
+    fn = L.moe_expert_forward_mx if w.mx else L.moe_expert_forward
+    _check(fn(_ptr(x), T, H, I, E, k, _ptr(topk_ids), _ptr(topk_w), _ptr(w.w1.q), _ptr(w.w1.sf),
+              _ptr(w.gs_w1), _ptr(w.w2.q), _ptr(w.w2.sf), _ptr(w.gs_w2), _ptr(gs_h), _ptr(o),
+              ctypes.byref(tp) if tp is not None else None, _ptr(ws), ws.numel(), _stream(dev)),
+           "moe_expert_forward_mx" if w.mx else "moe_expert_forward")
     return o
 
 
@@ -355,3 +378,17 @@ def prepare_expert_weights(w1_list, w2_list, device, keep_rowmajor=True):
     p1, p2 = pack_weights(w1q, w1s), pack_weights(w2q, w2s)
     rm = dict(w1_q=w1q, w1_sf=w1s, w2_q=w2q, w2_sf=w2s) if keep_rowmajor else None
     return ExpertWeights(p1, cat(g1), p2, cat(g2), rm)
+
+
+def mx_expert_weights(w: ExpertWeights, keep_rowmajor=True):
+    """The MX variant's weights: the row-major NVFP4 arrays of ``w`` (built
+    with keep_rowmajor=True) re-encoded with nvfp4_to_mx and packed; the
+    global scales carry over."""
+    if not w.rowmajor:
+        raise ValueError("mx_expert_weights needs the row-major NVFP4 weights (keep_rowmajor=True)")
+    r = w.rowmajor
+    q1, s1 = to_mx(r["w1_q"], r["w1_sf"])
+    q2, s2 = to_mx(r["w2_q"], r["w2_sf"])
+    p1, p2 = pack_weights(q1, s1), pack_weights(q2, s2)
+    rm = dict(w1_q=q1, w1_sf=s1, w2_q=q2, w2_sf=s2) if keep_rowmajor else None
+    return ExpertWeights(p1, w.gs_w1, p2, w.gs_w2, rm, mx=True)

@@ -286,15 +286,18 @@ size_t nvfp4_grouped_gemm_splitk_workspace_size(int epilogue, int64_t M, int64_t
   return nvfp4::gemm_splitk_ws_bytes(epilogue, M, N, K, E);
 }
 
-nvfp4_status nvfp4_grouped_gemm(int epilogue, const uint8_t* a_q, const uint8_t* a_sf,
-                                const float* gs_a, const int32_t* a_row_src, int a_row_div,
-                                const int32_t* expert_offsets, int E, int64_t M, int64_t N,
-                                int64_t K, const uint8_t* b_q, const uint8_t* b_sf,
-                                const float* gs_b, const float* gs_out, void* c_bf16,
-                                uint8_t* c_q, uint8_t* c_sf, float* c_debug_f32, void* ws,
-                                size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+nvfp4_status grouped_gemm_impl(int mx, int epilogue, const uint8_t* a_q, const uint8_t* a_sf,
+                               const float* gs_a, const int32_t* a_row_src, int a_row_div,
+                               const int32_t* expert_offsets, int E, int64_t M, int64_t N,
+                               int64_t K, const uint8_t* b_q, const uint8_t* b_sf,
+                               const float* gs_b, const float* gs_out, void* c_bf16,
+                               uint8_t* c_q, uint8_t* c_sf, float* c_debug_f32, void* ws,
+                               size_t ws_bytes, void* stream) {
   nvfp4::GemmArgs a{epilogue, a_q, a_sf, gs_a, a_row_src, a_row_div, expert_offsets, E, M, N, K,
-                    b_q, b_sf, gs_b, gs_out, c_bf16, c_q, c_sf, c_debug_f32, ws, ws_bytes};
+                    b_q, b_sf, gs_b, gs_out, c_bf16, c_q, c_sf, c_debug_f32, ws, ws_bytes, mx};
   nvfp4_status st = check_gemm(a);
   if (st != NVFP4_OK) return st;
   if (M == 0) return NVFP4_OK;
@@ -305,7 +308,56 @@ nvfp4_status nvfp4_grouped_gemm(int epilogue, const uint8_t* a_q, const uint8_t*
   st = check_arch();
   if (st != NVFP4_OK) return st;
   return finish(nvfp4::launch_grouped_gemm(a, static_cast<hipStream_t>(stream)),
-                "nvfp4_grouped_gemm launch");
+                mx ? "nvfp4_mx_grouped_gemm launch" : "nvfp4_grouped_gemm launch");
+}
+}  // namespace
+
+extern "C" {
+
+nvfp4_status nvfp4_grouped_gemm(int epilogue, const uint8_t* a_q, const uint8_t* a_sf,
+                                const float* gs_a, const int32_t* a_row_src, int a_row_div,
+                                const int32_t* expert_offsets, int E, int64_t M, int64_t N,
+                                int64_t K, const uint8_t* b_q, const uint8_t* b_sf,
+                                const float* gs_b, const float* gs_out, void* c_bf16,
+                                uint8_t* c_q, uint8_t* c_sf, float* c_debug_f32, void* ws,
+                                size_t ws_bytes, void* stream) {
+  return grouped_gemm_impl(0, epilogue, a_q, a_sf, gs_a, a_row_src, a_row_div, expert_offsets, E,
+                           M, N, K, b_q, b_sf, gs_b, gs_out, c_bf16, c_q, c_sf, c_debug_f32, ws,
+                           ws_bytes, stream);
+}
+
+nvfp4_status nvfp4_mx_grouped_gemm(int epilogue, const uint8_t* a_q, const uint8_t* a_sc,
+                                   const float* gs_a, const int32_t* a_row_src, int a_row_div,
+                                   const int32_t* expert_offsets, int E, int64_t M, int64_t N,
+                                   int64_t K, const uint8_t* b_q, const uint8_t* b_sc,
+                                   const float* gs_b, const float* gs_out, void* c_bf16,
+                                   uint8_t* c_q, uint8_t* c_sf, float* c_debug_f32, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  return grouped_gemm_impl(1, epilogue, a_q, a_sc, gs_a, a_row_src, a_row_div, expert_offsets, E,
+                           M, N, K, b_q, b_sc, gs_b, gs_out, c_bf16, c_q, c_sf, c_debug_f32, ws,
+                           ws_bytes, stream);
+}
+
+nvfp4_status nvfp4_to_mx(const uint8_t* q, const uint8_t* sf, int64_t rows, int64_t cols,
+                         uint8_t* q_mx, uint8_t* sc_mx, void* stream) {
+  if (rows < 0) return fail(NVFP4_ERR_SHAPE, "rows must be >= 0");
+  if (cols < 32 || cols % 32) return fail(NVFP4_ERR_SHAPE, "cols must be a positive multiple of 32 (got %lld)", (long long)cols);
+  if (rows * (cols / 32) >= (int64_t(1) << 40)) return fail(NVFP4_ERR_SHAPE, "tensor too large");
+  if (rows == 0) return NVFP4_OK;
+  if (!q || !sf || !q_mx || !sc_mx) return fail(NVFP4_ERR_INVALID_ARG, "all pointers must be non-NULL");
+  if (!aligned(q, 16) || !aligned(q_mx, 16) || !aligned(sf, 2) || !aligned(sc_mx, 2))
+    return fail(NVFP4_ERR_INVALID_ARG, "codes must be 16-byte and scales 2-byte aligned");
+  const int64_t qb = rows * cols / 2, sb = rows * cols / 16;
+  auto overlap = [](const uint8_t* a, int64_t na, const uint8_t* b, int64_t nb) {
+    return a < b + nb && b < a + na;
+  };
+  if ((q != q_mx && overlap(q, qb, q_mx, qb)) || (sf != sc_mx && overlap(sf, sb, sc_mx, sb)))
+    return fail(NVFP4_ERR_INVALID_ARG, "outputs must be the inputs (in place) or not overlap them");
+  nvfp4_status st = check_arch();
+  if (st != NVFP4_OK) return st;
+  return finish(nvfp4::launch_mx_reencode(q, sf, rows, cols, q_mx, sc_mx,
+                                          static_cast<hipStream_t>(stream)),
+                "nvfp4_to_mx launch");
 }
 
 nvfp4_status nvfp4_moe_combine(const void* y_bf16, const int32_t* inv_perm, const float* topk_w,
@@ -326,12 +378,15 @@ size_t moe_expert_forward_workspace_size(int64_t T, int64_t H, int64_t I, int E,
   return fwd_layout(T, H, I, E, k).total;
 }
 
-nvfp4_status moe_expert_forward(const void* x_bf16, int64_t T, int64_t H, int64_t I, int E, int k,
-                                const int32_t* topk_ids, const float* topk_w, const uint8_t* w1_q,
-                                const uint8_t* w1_sf, const float* gs_w1, const uint8_t* w2_q,
-                                const uint8_t* w2_sf, const float* gs_w2, const float* gs_h,
-                                void* out_bf16, const nvfp4_moe_taps* taps, void* ws,
-                                size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+nvfp4_status forward_impl(int mx, const void* x_bf16, int64_t T, int64_t H, int64_t I, int E,
+                          int k, const int32_t* topk_ids, const float* topk_w, const uint8_t* w1_q,
+                          const uint8_t* w1_sf, const float* gs_w1, const uint8_t* w2_q,
+                          const uint8_t* w2_sf, const float* gs_w2, const float* gs_h,
+                          void* out_bf16, const nvfp4_moe_taps* taps, void* ws, size_t ws_bytes,
+                          void* stream) {
   if (T < 0) return fail(NVFP4_ERR_SHAPE, "T must be >= 0");
   if (H < 128 || H % 128) return fail(NVFP4_ERR_SHAPE, "H must be a positive multiple of 128 (got %lld)", (long long)H);
   if (I < 128 || I % 128) return fail(NVFP4_ERR_SHAPE, "I must be a positive multiple of 128 (got %lld)", (long long)I);
@@ -375,6 +430,10 @@ nvfp4_status moe_expert_forward(const void* x_bf16, int64_t T, int64_t H, int64_
     err = nvfp4::launch_quantize(x_bf16, 1, T, H, nullptr, a_q, a_sf, gs_a,
                                  reinterpret_cast<float*>(base + L.qws), s);
     if (err != hipSuccess) return hip_fail(err, "moe_expert_forward quantize");
+    if (mx) {
+      err = nvfp4::launch_mx_reencode(a_q, a_sf, T, H, a_q, a_sf, s);
+      if (err != hipSuccess) return hip_fail(err, "moe_expert_forward_mx re-encode x");
+    }
   } else {
     nvfp4::fill_f32(gs_a, 1.0f, 1, s);
   }
@@ -383,17 +442,44 @@ nvfp4_status moe_expert_forward(const void* x_bf16, int64_t T, int64_t H, int64_
   if (M > 0) {
     nvfp4::GemmArgs l1{NVFP4_EPI_SWIGLU_NVFP4, a_q, a_sf, gs_a, perm, k, off, E, M, 2 * I, H,
                        w1_q, w1_sf, gs_w1, gs_h, nullptr, h_q, h_sf, tp.h_f32, base + L.gws,
-                       nvfp4::kGemmWorkspaceBytes};
+                       nvfp4::kGemmWorkspaceBytes, mx};
     err = nvfp4::launch_grouped_gemm(l1, s);
     if (err != hipSuccess) return hip_fail(err, "moe_expert_forward L1");
+    if (mx) {
+      err = nvfp4::launch_mx_reencode(h_q, h_sf, M, I, h_q, h_sf, s);
+      if (err != hipSuccess) return hip_fail(err, "moe_expert_forward_mx re-encode h");
+    }
     nvfp4::GemmArgs l2{NVFP4_EPI_BF16, h_q, h_sf, gs_h, nullptr, 1, off, E, M, H, I,
                        w2_q, w2_sf, gs_w2, nullptr, y, nullptr, nullptr, nullptr, base + L.gws,
-                       nvfp4::kGemmWorkspaceBytes};
+                       nvfp4::kGemmWorkspaceBytes, mx};
     err = nvfp4::launch_grouped_gemm(l2, s);
     if (err != hipSuccess) return hip_fail(err, "moe_expert_forward L2");
   }
   err = nvfp4::launch_combine(y, inv, topk_w, off, T, k, E, H, out_bf16, s);
   return finish(err, "moe_expert_forward combine");
+}
+}  // namespace
+
+extern "C" {
+
+nvfp4_status moe_expert_forward(const void* x_bf16, int64_t T, int64_t H, int64_t I, int E, int k,
+                                const int32_t* topk_ids, const float* topk_w, const uint8_t* w1_q,
+                                const uint8_t* w1_sf, const float* gs_w1, const uint8_t* w2_q,
+                                const uint8_t* w2_sf, const float* gs_w2, const float* gs_h,
+                                void* out_bf16, const nvfp4_moe_taps* taps, void* ws,
+                                size_t ws_bytes, void* stream) {
+  return forward_impl(0, x_bf16, T, H, I, E, k, topk_ids, topk_w, w1_q, w1_sf, gs_w1, w2_q, w2_sf,
+                      gs_w2, gs_h, out_bf16, taps, ws, ws_bytes, stream);
+}
+
+nvfp4_status moe_expert_forward_mx(const void* x_bf16, int64_t T, int64_t H, int64_t I, int E,
+                                   int k, const int32_t* topk_ids, const float* topk_w,
+                                   const uint8_t* w1_q, const uint8_t* w1_sc, const float* gs_w1,
+                                   const uint8_t* w2_q, const uint8_t* w2_sc, const float* gs_w2,
+                                   const float* gs_h, void* out_bf16, const nvfp4_moe_taps* taps,
+                                   void* ws, size_t ws_bytes, void* stream) {
+  return forward_impl(1, x_bf16, T, H, I, E, k, topk_ids, topk_w, w1_q, w1_sc, gs_w1, w2_q, w2_sc,
+                      gs_w2, gs_h, out_bf16, taps, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

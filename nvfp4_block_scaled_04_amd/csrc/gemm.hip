@@ -36,6 +36,14 @@
 // 128 K are double-buffered in LDS through registers.  In an expert's last
 // m tile, 32-token column blocks past the expert's rows are skipped.
 //
+// MX mode.  The same tiles, loads and epilogues run on MXFP4 operands (E2M1
+// codes, one E8M0 scale per 32 elements stored once per 16-element block, as
+// written by the NVFP4 -> MX re-encoding): the codes in LDS go straight into
+// v_mfma_scale_f32_32x32x64_f8f6f4 with the scales as its per-lane scale
+// operands, with no decode step.  Lane half hf holds K chunk 2hf + h (32
+// elements) of each row for MFMA h of a stage, whose E8M0 scale is byte 2h
+// of the lane's scale dword (bytes 4hf..4hf+3 of the row's 8 stage bytes).
+//
 // Split K.  When the tile list is too short to occupy every CU (a dense
 // linear of few rows), each tile's K stages are split into ksplit equal
 // ranges run as separate work items; they write fp32 partials (already
@@ -58,6 +66,10 @@ namespace {
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef _Float16 half8v __attribute__((ext_vector_type(8)));
 typedef float float16v __attribute__((ext_vector_type(16)));
+typedef int int8v __attribute__((ext_vector_type(8)));
+
+constexpr int kFmtNvfp4 = 0;   // E4M3 per 16: decode to FP16, FP16 MFMA
+constexpr int kFmtMx = 1;      // E8M0 per 32: scaled FP4 MFMA
 
 constexpr int BK = 128;            // K elements per stage
 constexpr int ROW_BYTES = BK / 2;  // 64 bytes of codes per row per stage
@@ -387,6 +399,80 @@ __device__ __forceinline__ void k_stage(KState<BN, BM, WN, WM, JV>& st, int ks, 
   }
   NVFP4_MFMAS(st.av1, st.bv1); NVFP4_INTERLEAVE(0);
 }
+// ---- MX mode: no decode; each stage is two sets of FN x JV scaled FP4
+// MFMAs (K chunks 2hf and 2hf + 1 of the lane's row)
+__device__ __forceinline__ int8v widen(const uint4& q) {
+  int8v v;
+  v[0] = (int)q.x; v[1] = (int)q.y; v[2] = (int)q.z; v[3] = (int)q.w;
+  v[4] = 0; v[5] = 0; v[6] = 0; v[7] = 0;
+  return v;
+}
+// OPSEL picks the scale byte of the lane's dword: 0 for K chunk 2hf, 2 for 2hf + 1
+#define NVFP4_MFMAS_MX(WA, TB, WS, TS, OPSEL)                                                   \
+  do {                                                                                          \
+    _Pragma("unroll") for (int i = 0; i < FN; ++i)                                              \
+      _Pragma("unroll") for (int j = 0; j < JV; ++j)                                            \
+        st.acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                         \
+            widen(WA[i]), widen(TB[j]), st.acc[i][j], 4, 4, OPSEL, (int)WS[i], OPSEL, (int)TS[j]); \
+  } while (0)
+
+// Waits for stage 0, synchronises the block and reads half 0 of its
+// fragments and its scales.
+template <int BN, int BM, int WN, int WM, int JV>
+__device__ __forceinline__ void k_begin_mx(KState<BN, BM, WN, WM, JV>& st, int nks,
+                                           const uint8_t* __restrict__ b0) {
+  using C = Cfg<BN, BM, WN, WM>;
+  constexpr int FN = C::FN, TN = C::TN, TM = C::TM;
+  static_assert(C::LOADS == 12, "vmcnt immediates assume 12 loads per stage");
+  if (nks > 1) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  stage_barrier();
+  NVFP4_READ_HALF(b0, 0, st.fa, st.ta);
+  NVFP4_READ_SF(b0, st.wsr, st.tsr);
+}
+
+// One MX stage ks (buffers as in k_stage):
+//   issue all loads of stage ks+2 into bw (its last reader, stage ks-1,
+//     finished before the mid-stage barrier of ks-1);
+//   read half 1 of stage ks; MFMAs on half 0;
+//   wait until stage ks+1 has landed and this wave's LDS reads are done,
+//     synchronise the block;
+//   read half 0 and the scales of stage ks+1 while the MFMAs on half 1 run.
+template <int BN, int BM, int WN, int WM, int JV, int LOADS>
+__device__ __forceinline__ void k_stage_mx(KState<BN, BM, WN, WM, JV>& st, int ks, int nks,
+                                           int wave, const uint32_t* coff, const uint32_t* soff,
+                                           const uint8_t* __restrict__ wq,
+                                           const uint8_t* __restrict__ wsf,
+                                           const uint8_t* __restrict__ aq,
+                                           const uint8_t* __restrict__ asf,
+                                           const uint8_t* __restrict__ br,
+                                           const uint8_t* __restrict__ bm,
+                                           uint8_t* __restrict__ bw) {
+  using C = Cfg<BN, BM, WN, WM>;
+  constexpr int FN = C::FN, TN = C::TN, TM = C::TM;
+  NVFP4_LOAD_CONSTS;
+  const bool more1 = LOADS || ks + 1 < nks;
+  if (LOADS) NVFP4_ISSUE(ks + 2, bw, -1);
+  NVFP4_READ_HALF(br, 1, st.fb, st.tb);
+  NVFP4_MFMAS_MX(st.fa, st.ta, st.wsr, st.tsr, 0);
+  if (LOADS) asm volatile("s_waitcnt vmcnt(12) lgkmcnt(0)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+  stage_barrier();
+  uint32_t wsn[C::FN], tsn[C::FM];
+  if (more1) {
+    NVFP4_READ_HALF(bm, 0, st.fa, st.ta);
+    NVFP4_READ_SF(bm, wsn, tsn);
+  }
+  NVFP4_MFMAS_MX(st.fb, st.tb, st.wsr, st.tsr, 2);
+  if (more1) {
+#pragma unroll
+    for (int i = 0; i < FN; ++i) st.wsr[i] = wsn[i];
+#pragma unroll
+    for (int j = 0; j < JV; ++j) st.tsr[j] = tsn[j];
+  }
+}
+#undef NVFP4_MFMAS_MX
+
 #undef NVFP4_ISSUE
 #undef NVFP4_LOAD_CONSTS
 #undef NVFP4_READ_HALF
@@ -536,7 +622,7 @@ __device__ __forceinline__ void tile_offsets(const Params& p, const Tile& t, int
 // the tile were issued by the caller with the load offsets coff/soff; after
 // the K loop the stages 0 and 1 of the next tile (if any) are issued, with
 // coff/soff rewritten for it, so that their latency overlaps the epilogue.
-template <int BN, int BM, int WN, int WM, int EPI, int JV>
+template <int BN, int BM, int WN, int WM, int EPI, int FMT, int JV>
 __device__ __forceinline__ bool run_tile(const Params& p, uint8_t* smem, const int* tprefix,
                                          Sched& sc, const Tile& cur, uint32_t* coff,
                                          uint32_t* soff, int& claim, Tile& nxt) {
@@ -565,22 +651,42 @@ __device__ __forceinline__ bool run_tile(const Params& p, uint8_t* smem, const i
 
   // three LDS stage buffers, stage ks in buffer ks % 3
   const int nks = cur.nks;
-  k_begin(st, nks, smem);
-  int buf = 0;
-  int ks = 0;
-  for (; ks + 2 < nks; ++ks) {
-    const int buf1 = buf == 2 ? 0 : buf + 1, buf2 = buf == 0 ? 2 : buf - 1;
-    k_stage<BN, BM, WN, WM, JV, 1>(st, ks, nks, wave, coff, soff, wbase, wsbase, abase, asbase,
-                                   smem + buf * C::STAGE_BYTES, smem + buf1 * C::STAGE_BYTES,
-                                   smem + buf2 * C::STAGE_BYTES);
-    buf = buf1;
-  }
-  for (; ks < nks; ++ks) {
-    const int buf1 = buf == 2 ? 0 : buf + 1, buf2 = buf == 0 ? 2 : buf - 1;
-    k_stage<BN, BM, WN, WM, JV, 0>(st, ks, nks, wave, coff, soff, wbase, wsbase, abase, asbase,
-                                   smem + buf * C::STAGE_BYTES, smem + buf1 * C::STAGE_BYTES,
-                                   smem + buf2 * C::STAGE_BYTES);
-    buf = buf1;
+  if constexpr (FMT == kFmtMx) {
+    k_begin_mx(st, nks, smem);
+    int buf = 0;
+    int ks = 0;
+    for (; ks + 2 < nks; ++ks) {
+      const int buf1 = buf == 2 ? 0 : buf + 1, buf2 = buf == 0 ? 2 : buf - 1;
+      k_stage_mx<BN, BM, WN, WM, JV, 1>(st, ks, nks, wave, coff, soff, wbase, wsbase, abase,
+                                        asbase, smem + buf * C::STAGE_BYTES,
+                                        smem + buf1 * C::STAGE_BYTES, smem + buf2 * C::STAGE_BYTES);
+      buf = buf1;
+    }
+    for (; ks < nks; ++ks) {
+      const int buf1 = buf == 2 ? 0 : buf + 1, buf2 = buf == 0 ? 2 : buf - 1;
+      k_stage_mx<BN, BM, WN, WM, JV, 0>(st, ks, nks, wave, coff, soff, wbase, wsbase, abase,
+                                        asbase, smem + buf * C::STAGE_BYTES,
+                                        smem + buf1 * C::STAGE_BYTES, smem + buf2 * C::STAGE_BYTES);
+      buf = buf1;
+    }
+  } else {
+    k_begin(st, nks, smem);
+    int buf = 0;
+    int ks = 0;
+    for (; ks + 2 < nks; ++ks) {
+      const int buf1 = buf == 2 ? 0 : buf + 1, buf2 = buf == 0 ? 2 : buf - 1;
+      k_stage<BN, BM, WN, WM, JV, 1>(st, ks, nks, wave, coff, soff, wbase, wsbase, abase, asbase,
+                                     smem + buf * C::STAGE_BYTES, smem + buf1 * C::STAGE_BYTES,
+                                     smem + buf2 * C::STAGE_BYTES);
+      buf = buf1;
+    }
+    for (; ks < nks; ++ks) {
+      const int buf1 = buf == 2 ? 0 : buf + 1, buf2 = buf == 0 ? 2 : buf - 1;
+      k_stage<BN, BM, WN, WM, JV, 0>(st, ks, nks, wave, coff, soff, wbase, wsbase, abase, asbase,
+                                     smem + buf * C::STAGE_BYTES, smem + buf1 * C::STAGE_BYTES,
+                                     smem + buf2 * C::STAGE_BYTES);
+      buf = buf1;
+    }
   }
   float16v (&acc)[FN][FM] = st.acc;
   // the last stage waited for every load, the pending claim included
@@ -708,7 +814,7 @@ __device__ __forceinline__ bool run_tile(const Params& p, uint8_t* smem, const i
   return has_next;
 }
 
-template <int BN, int BM, int WN, int WM, int EPI>
+template <int BN, int BM, int WN, int WM, int EPI, int FMT>
 __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_gemm_kernel(Params p) {
   using C = Cfg<BN, BM, WN, WM>;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -764,12 +870,12 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_gemm_kernel(Params p)
     Tile nxt;
     bool more = false;
     if (cur.jv >= C::FM) {
-      more = run_tile<BN, BM, WN, WM, EPI, C::FM>(p, smem, tprefix, sc, cur, coff, soff, claim, nxt);
+      more = run_tile<BN, BM, WN, WM, EPI, FMT, C::FM>(p, smem, tprefix, sc, cur, coff, soff, claim, nxt);
     } else if constexpr (C::FM > 1) {
-      if (cur.jv == 1) more = run_tile<BN, BM, WN, WM, EPI, 1>(p, smem, tprefix, sc, cur, coff, soff, claim, nxt);
+      if (cur.jv == 1) more = run_tile<BN, BM, WN, WM, EPI, FMT, 1>(p, smem, tprefix, sc, cur, coff, soff, claim, nxt);
       else if constexpr (C::FM > 2) {
-        if (cur.jv == 2) more = run_tile<BN, BM, WN, WM, EPI, 2>(p, smem, tprefix, sc, cur, coff, soff, claim, nxt);
-        else if constexpr (C::FM > 3) more = run_tile<BN, BM, WN, WM, EPI, 3>(p, smem, tprefix, sc, cur, coff, soff, claim, nxt);
+        if (cur.jv == 2) more = run_tile<BN, BM, WN, WM, EPI, FMT, 2>(p, smem, tprefix, sc, cur, coff, soff, claim, nxt);
+        else if constexpr (C::FM > 3) more = run_tile<BN, BM, WN, WM, EPI, FMT, 3>(p, smem, tprefix, sc, cur, coff, soff, claim, nxt);
       }
     }
     cur = nxt;
@@ -846,7 +952,7 @@ float* splitk_partial(void* ws) {
   return reinterpret_cast<float*>((b + 255) & ~uintptr_t(255));
 }
 
-template <int BN, int BM, int WN, int WM, int EPI>
+template <int BN, int BM, int WN, int WM, int EPI, int FMT>
 hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
   using C = Cfg<BN, BM, WN, WM>;
   Params p;
@@ -873,7 +979,7 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
   if (grid > tiles) grid = tiles;
   grid = (grid + 7) / 8 * 8;
   const size_t lds = (size_t)C::LDS_BYTES + sizeof(int) * (size_t)(a.E + 1);
-  auto kern = grouped_gemm_kernel<BN, BM, WN, WM, EPI>;
+  auto kern = grouped_gemm_kernel<BN, BM, WN, WM, EPI, FMT>;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -903,15 +1009,20 @@ size_t gemm_splitk_ws_bytes(int epilogue, int64_t M, int64_t N, int64_t K, int E
   return kGemmWorkspaceBytes + 255 + (size_t)f * (size_t)M * (size_t)N * sizeof(float);
 }
 
-hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t stream) {
+template <int FMT>
+hipError_t launch_fmt(const GemmArgs& a, hipStream_t stream) {
   if (a.epilogue == NVFP4_EPI_SWIGLU_NVFP4)
-    return launch_cfg<kBN, kBM, 4, 1, NVFP4_EPI_SWIGLU_NVFP4>(a, stream);
+    return launch_cfg<kBN, kBM, 4, 1, NVFP4_EPI_SWIGLU_NVFP4, FMT>(a, stream);
   // split K only when the caller's workspace holds the partials
   if (a.M > 0 && a.ws_bytes > kGemmWorkspaceBytes &&
       a.ws_bytes >= gemm_splitk_ws_bytes(a.epilogue, a.M, a.N, a.K, a.E) &&
       splitk_factor(a.epilogue, a.M, a.N, a.K, a.E, g_cu_count) > 1)
-    return launch_cfg<kBN, kBM, 4, 1, kEpiPartial>(a, stream);
-  return launch_cfg<kBN, kBM, 4, 1, NVFP4_EPI_BF16>(a, stream);
+    return launch_cfg<kBN, kBM, 4, 1, kEpiPartial, FMT>(a, stream);
+  return launch_cfg<kBN, kBM, 4, 1, NVFP4_EPI_BF16, FMT>(a, stream);
+}
+
+hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t stream) {
+  return a.mx ? launch_fmt<kFmtMx>(a, stream) : launch_fmt<kFmtNvfp4>(a, stream);
 }
 
 }  // namespace nvfp4

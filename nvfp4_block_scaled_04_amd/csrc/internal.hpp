@@ -57,12 +57,19 @@ struct GemmArgs {
   void* ws;         // the tile scheduler's counters (kGemmWorkspaceBytes), then
                     // room for split-K partials if ws_bytes allows
   size_t ws_bytes;
+  int mx = 0;       // operands are MXFP4 (nvfp4 -> mx re-encoding), not NVFP4
 };
 constexpr size_t kGemmWorkspaceBytes = 256;
 // workspace with which a launch of this shape splits K (kGemmWorkspaceBytes
 // when it would not split)
 size_t gemm_splitk_ws_bytes(int epilogue, int64_t M, int64_t N, int64_t K, int E);
 hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t stream);
+
+// mx.hip: NVFP4 (q [rows][cols/2], E4M3 sf [rows][cols/16]) -> MXFP4 codes
+// and E8M0 scales in the same shapes (each scale byte stored twice);
+// cols % 32 == 0; in place allowed
+hipError_t launch_mx_reencode(const uint8_t* q, const uint8_t* sf, int64_t rows, int64_t cols,
+                              uint8_t* q_mx, uint8_t* sc_mx, hipStream_t stream);
 constexpr int kRouterMaxExperts = 1024;
 hipError_t launch_router_topk(const float* logits, int64_t T, int E, int k, int32_t* topk_ids,
                               float* topk_w, hipStream_t stream);

@@ -96,3 +96,58 @@ def mx_matmul(a_q, a_sc, gs_a, b_q, b_sc, gs_b):
     a = mx_block_values(a_q, a_sc)
     b = mx_block_values(b_q, b_sc)
     return (a @ b.T) / (np.float64(gs_a) * np.float64(gs_b))
+
+
+def prepare_weights_mx(wts):
+    """Per-expert NVFP4 weight operands (``moe.prepare_weights``) re-encoded:
+    the global scales carry over."""
+    out = dict(wts)
+    for q, s in (("w1_q", "w1_sf"), ("w2_q", "w2_sf")):
+        pairs = [nvfp4_to_mx(wts[q][e], wts[s][e]) for e in range(len(wts[q]))]
+        out[q] = np.stack([p[0] for p in pairs])
+        out[s] = np.stack([p[1] for p in pairs])
+    return out
+
+
+def moe_forward_mx(x_bits, topk_ids, topk_w, wts_mx, gs_h, E):
+    """The MX variant of ``moe.moe_forward``: x is quantised to NVFP4 as
+    there and re-encoded; L1 and L2 are exact products of MX operands
+    (``wts_mx`` from ``prepare_weights_mx``); the SwiGLU output is requantised
+    to NVFP4 with gs_h as there and re-encoded before L2.  Returns the same
+    intermediates (a_q/a_sf and h_q/h_sf in their MX forms, scales per 32)."""
+    from .moe import silu, combine
+    from .layout import deinterleave_cols
+    from .route import route
+    from .formats import round_to_bf16
+    from .quantize import quantize_nvfp4, quantize_blocks
+
+    T, k = topk_ids.shape
+    K = x_bits.shape[1]
+    a_q, a_sf, gs_a = quantize_nvfp4(x_bits)
+    gs_a = gs_a[0]
+    a_q, a_sc = nvfp4_to_mx(a_q, a_sf)
+    offsets, perm, inv_perm, n_invalid = route(topk_ids, E)
+    M = T * k
+    I = wts_mx["w1_q"][0].shape[0] // 2
+    h = np.zeros((M, I), dtype=np.float32)
+    h_q = np.zeros((M, I // 2), dtype=np.uint8)
+    h_sc = np.zeros((M, I // 32), dtype=np.uint8)
+    y = np.zeros((M, K), dtype=np.uint16)
+    gs_h = np.float32(gs_h)
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        tok = perm[lo:hi] // k
+        acc = mx_matmul(a_q[tok], a_sc[tok], gs_a, wts_mx["w1_q"][e], wts_mx["w1_sf"][e],
+                        wts_mx["gs_w1"][e])
+        gate, up = deinterleave_cols(acc)
+        h_e = (silu(gate) * up).astype(np.float32)
+        c_e, s_e = quantize_blocks(h_e, gs_h)
+        hq_e, hsc_e = nvfp4_to_mx(pack_codes(c_e), s_e)
+        h[lo:hi], h_q[lo:hi], h_sc[lo:hi] = h_e, hq_e, hsc_e
+        y[lo:hi] = round_to_bf16(mx_matmul(hq_e, hsc_e, gs_h, wts_mx["w2_q"][e],
+                                           wts_mx["w2_sf"][e], wts_mx["gs_w2"][e]))
+    out = combine(y, inv_perm, topk_w, int(offsets[E]))
+    return dict(a_q=a_q, a_sc=a_sc, gs_a=gs_a, offsets=offsets, perm=perm, inv_perm=inv_perm,
+                n_invalid=n_invalid, h=h, h_q=h_q, h_sc=h_sc, y=y, out=out)

@@ -153,3 +153,25 @@ def test_packed_weight_sizes_and_rejects(L):
     assert L.nvfp4_pack_weights(FAKE, FAKE, 2, 100, 200, FAKE, FAKE, None) == -2
     assert L.nvfp4_pack_weights(None, FAKE, 2, 100, 256, FAKE, FAKE, None) == -1
     assert L.nvfp4_pack_weights(FAKE, FAKE, 2, 100, 256, FAKE, FAKE + 8, None) == -1
+
+
+def test_mx_entry_points_reject(L):
+    B = 1 << 20
+    assert L.nvfp4_to_mx(FAKE, FAKE, 4, 48, FAKE + B, FAKE + B, None) == -2     # cols % 32
+    assert L.nvfp4_to_mx(FAKE, FAKE, -1, 64, FAKE + B, FAKE + B, None) == -2
+    assert L.nvfp4_to_mx(None, FAKE, 4, 64, FAKE + B, FAKE + B, None) == -1
+    assert L.nvfp4_to_mx(FAKE + 8, FAKE, 4, 64, FAKE + B, FAKE + B, None) == -1  # misaligned codes
+    assert L.nvfp4_to_mx(FAKE, FAKE, 4, 64, FAKE + 16, FAKE + B, None) == -1     # partial overlap
+    assert L.nvfp4_to_mx(None, None, 0, 64, None, None, None) == 0               # nothing to do
+    # the MX GEMM validates like the NVFP4 one
+    args = lambda **kw: (kw.get("epi", 0), FAKE, FAKE, FAKE, None, 1, FAKE, 4, 64,
+                         kw.get("N", 64), kw.get("K", 256), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                         FAKE, None, FAKE, 1 << 20, None)
+    assert L.nvfp4_mx_grouped_gemm(*args(K=200)) == -2
+    assert L.nvfp4_mx_grouped_gemm(*args(N=48)) == -2
+    assert L.nvfp4_mx_grouped_gemm(*args(epi=7)) == -1
+    f = lambda **kw: L.moe_expert_forward_mx(
+        FAKE, 4, kw.get("H", 256), 128, 4, 2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+        FAKE, FAKE, None, FAKE, kw.get("wsb", 1 << 30), None)
+    assert f(H=200) == -2
+    assert f(wsb=16) == -3

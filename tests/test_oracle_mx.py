@@ -138,3 +138,28 @@ def test_mx_matmul_matches_triple_loop():
                 s += (e2m1_decode(a_codes[i, k]) * 2.0 ** (int(a_sc[i, k // 32]) - 127) *
                       e2m1_decode(b_codes[j, k]) * 2.0 ** (int(b_sc[j, k // 32]) - 127))
             assert got[i, j] == pytest.approx(s / 1.5, rel=1e-12)
+
+
+def test_mx_forward_is_close_to_but_not_the_exact_path():
+    """Composition check of the MX forward on the tiny workload: its output
+    lies within the error a 32-element power-of-two re-encoding of x, W1, h
+    and W2 can add (cosine 0.952 against the exact NVFP4 forward at this
+    seed; the band is 0.9-0.99999), and differs from it (a path that skipped
+    a re-encoding, or read E8M0 bytes as E4M3, lands far outside this band or
+    on the exact result)."""
+    from nvfp4_block_scaled_04_amd import inputs as I
+    from oracle import moe as O
+    from oracle.formats import bf16_bits_to_f32
+    w = I.WORKLOADS["tiny"]
+    x = I.bf16_to_bits(I.make_x(w))
+    ids, tw = I.make_routing(w)
+    pairs = [I.make_expert_weights(w, e) for e in range(w.E)]
+    w1 = np.stack([I.bf16_to_bits(p[0]) for p in pairs])
+    w2 = np.stack([I.bf16_to_bits(p[1]) for p in pairs])
+    wts = O.prepare_weights(w1, w2)
+    ref = O.moe_forward(x, ids, tw, wts, np.float32(w.gs_h), w.E)
+    got = X.moe_forward_mx(x, ids, tw, X.prepare_weights_mx(wts), np.float32(w.gs_h), w.E)
+    a = bf16_bits_to_f32(ref["out"]).astype(np.float64).ravel()
+    b = bf16_bits_to_f32(got["out"]).astype(np.float64).ravel()
+    cos = a @ b / np.linalg.norm(a) / np.linalg.norm(b)
+    assert 0.9 < cos < 0.99999, cos
