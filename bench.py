@@ -64,7 +64,7 @@ def moe_flops(T, H, Iw, k):
     return 2.0 * T * k * (H * 2 * Iw + Iw * H)
 
 
-def build_weights(w, dev, chunk=32):
+def build_weights(w, dev, chunk=32, keep_rowmajor=False):
     w1s, w2s = [], []
     for e0 in range(0, w.E, chunk):
         es = range(e0, min(w.E, e0 + chunk))
@@ -72,7 +72,7 @@ def build_weights(w, dev, chunk=32):
         w1s.append(torch.stack([p[0] for p in pairs]))
         w2s.append(torch.stack([p[1] for p in pairs]))
         del pairs
-    ew = nv.prepare_expert_weights(w1s, w2s, dev, keep_rowmajor=False)
+    ew = nv.prepare_expert_weights(w1s, w2s, dev, keep_rowmajor=keep_rowmajor)
     del w1s, w2s
     torch.cuda.empty_cache()
     return ew
@@ -121,14 +121,15 @@ def timed_steps(fn, steps):
     return mean, pct
 
 
-def roofline(kernel, flops, nbytes, ms, traffic=None):
-    """Roofline object for one kernel: MFMA-bound (FP16 peak) when its
-    arithmetic intensity is above the ridge, else HBM-bound."""
-    if flops / max(nbytes, 1.0) >= RIDGE:
+def roofline(kernel, flops, nbytes, ms, traffic=None, peak=FP16_MFMA_PEAK_TFLOPS):
+    """Roofline object for one kernel: MFMA-bound (against the MFMA peak of
+    its operand dtype) when its arithmetic intensity is above that ridge,
+    else HBM-bound."""
+    if flops / max(nbytes, 1.0) >= peak * 1e12 / (HBM_PEAK_GBS * 1e9):
         a = flops / (ms * 1e-3) / 1e12
         return {"kernel": kernel, "bound": "mfma", "achieved": round(a, 2),
-                "peak": FP16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(a / FP16_MFMA_PEAK_TFLOPS, 4), "traffic": traffic}
+                "peak": peak, "unit": "TFLOP/s",
+                "frac": round(a / peak, 4), "traffic": traffic}
     a = nbytes / (ms * 1e-3) / 1e9
     return {"kernel": kernel, "bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(a / HBM_PEAK_GBS, 4), "traffic": traffic}
@@ -143,10 +144,11 @@ def time_loop(fn, steps):
     return ev.ms() / steps
 
 
-def bench_moe(w, steps, warmup, dev):
-    log(f"[bench] building weights for {w.name}: E={w.E} H={w.H} I={w.I}")
+def bench_moe(w, steps, warmup, dev, mx=False):
+    log(f"[bench] building weights for {w.name}: E={w.E} H={w.H} I={w.I}" + (" (MX variant)" if mx else ""))
     t0 = time.time()
-    ew = build_weights(w, dev)
+    ew_nv = build_weights(w, dev, keep_rowmajor=mx)
+    ew = nv.mx_expert_weights(ew_nv, keep_rowmajor=False) if mx else ew_nv
     x = I.make_x(w, dev)
     ids_h, tw_h = I.make_routing(w)
     ids = torch.from_numpy(ids_h).to(dev)
@@ -172,18 +174,28 @@ def bench_moe(w, steps, warmup, dev):
     h_sf = torch.empty((M, Iw // 16), dtype=torch.uint8, device=dev)
     y = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
     qbuf = (a_q, a_sf, gs_a)
+    if mx:          # the GEMMs read MX operands: re-encode once, as the forward does
+        nv.to_mx(a_q, a_sf, out=(a_q, a_sf))
     l1 = lambda: nv.grouped_gemm(nv.EPI_SWIGLU_NVFP4, a_q, a_sf, gs_a, off, ew.w1,
                                  ew.gs_w1, M, a_row_src=perm, a_row_div=k, gs_out=gs_h,
-                                 out=(h_q, h_sf, None))
+                                 out=(h_q, h_sf, None), mx=mx)
+    if mx:
+        l1()
+        nv.to_mx(h_q, h_sf, out=(h_q, h_sf))
     l2 = lambda: nv.grouped_gemm(nv.EPI_BF16, h_q, h_sf, gs_h, off, ew.w2, ew.gs_w2,
-                                 M, out=y)
+                                 M, out=y, mx=mx)
+    qx = torch.empty_like(a_q), torch.empty_like(a_sf), torch.empty_like(gs_a)
     stages = {
-        "quantize": lambda: nv.quantize(x, out=qbuf),
+        "quantize": lambda: nv.quantize(x, out=qx),
         "route": lambda: nv.moe_route(ids, E),
         "l1_gemm_swiglu_requant": l1,
         "l2_gemm": l2,
         "combine": lambda: nv.moe_combine(y, inv, tw, off, out=out),
     }
+    if mx:
+        stages["to_mx_x"] = lambda: nv.to_mx(qx[0], qx[1], out=(qx[0], qx[1]))
+        hq2, hs2 = torch.empty_like(h_q), torch.empty_like(h_sf)
+        stages["to_mx_h"] = lambda: nv.to_mx(h_q, h_sf, out=(hq2, hs2))
     st_ms = {}
     for name, fn in stages.items():
         fn()
@@ -207,15 +219,17 @@ def bench_moe(w, steps, warmup, dev):
     w1_bytes, w2_bytes = n_live * nvfp4_bytes(2 * Iw, H), n_live * nvfp4_bytes(H, Iw)
     l1_bytes = w1_bytes + nvfp4_bytes(M, H) + nvfp4_bytes(M, Iw)
     l2_bytes = w2_bytes + nvfp4_bytes(M, Iw) + 2.0 * M * H
-    roof = roofline("grouped_gemm_kernel<SwiGLU+NVFP4 epilogue> (L1)", l1_flops, l1_bytes,
-                    st_ms["l1_gemm_swiglu_requant"],
-                    TRAFFIC.get((w.name, "l1")) if TRAFFIC_SRC_SHA == gemm_src_sha() else None)
+    peak = FP4_MFMA_PEAK_TFLOPS if mx else FP16_MFMA_PEAK_TFLOPS
+    roof = roofline("grouped_gemm_kernel<SwiGLU+NVFP4 epilogue> (L1)" + (" MX" if mx else ""),
+                    l1_flops, l1_bytes, st_ms["l1_gemm_swiglu_requant"],
+                    None if mx else (TRAFFIC.get((w.name, "l1")) if TRAFFIC_SRC_SHA == gemm_src_sha() else None),
+                    peak=peak)
     extra = {
         "ms_percentiles": pct,
         "live_experts": n_live,
         "weight_stream_gbs": (w1_bytes + w2_bytes) / (ms_step * 1e-3) / 1e9,
-        "l2_roofline": roofline("grouped_gemm_kernel<BF16 epilogue> (L2)", l2_flops, l2_bytes,
-                                st_ms["l2_gemm"]),
+        "l2_roofline": roofline("grouped_gemm_kernel<BF16 epilogue> (L2)" + (" MX" if mx else ""),
+                                l2_flops, l2_bytes, st_ms["l2_gemm"], peak=peak),
         "tokens_per_s": T / (ms_step * 1e-3),
         "l2_gemm_tflops": l2_flops / (st_ms["l2_gemm"] * 1e-3) / 1e12,
         "quantize_gbs": (2 * T * H + 0.5625 * T * H) / (st_ms["quantize"] * 1e-3) / 1e9,
@@ -223,10 +237,18 @@ def bench_moe(w, steps, warmup, dev):
         "stages_ms": {n: round(v, 4) for n, v in st_ms.items()},
         "router_topk_ms": round(router_ms, 4),
     }
-    return flops / (ms_step * 1e-3) / 1e12, ms_step, roof, extra, (x, ids_h, tw_h, ew)
+    if mx:
+        # error study: the MX forward against the exact NVFP4 forward, same inputs
+        ref = nv.moe_expert_forward(x, ids, tw, ew_nv, gs_h)
+        got = nv.moe_expert_forward(x, ids, tw, ew, gs_h)
+        a, b = ref.float().ravel(), got.float().ravel()
+        extra["mx_vs_exact_cosine"] = round(float((a @ b) / (a.norm() * b.norm())), 6)
+        extra["mx_vs_exact_maxabs_over_rms"] = round(float((a - b).abs().max() / a.pow(2).mean().sqrt()), 4)
+        log(f"[bench] MX vs exact NVFP4 forward: cosine {extra['mx_vs_exact_cosine']}")
+    return flops / (ms_step * 1e-3) / 1e12, ms_step, roof, extra, (x, ids_h, tw_h, ew_nv)
 
 
-def bench_dense(w, steps, warmup, dev):
+def bench_dense(w, steps, warmup, dev, mx=False):
     """The single NVFP4 linear (one expert): quantise A, then the GEMM with a
     BF16 epilogue; each timed alone, and both together as the step."""
     M, K, N = w.dense_mkn
@@ -235,6 +257,10 @@ def bench_dense(w, steps, warmup, dev):
     bk = nv.weight_layout(b.view(1, K, N), False)[0]                     # (N, K)
     b_q, b_sf, gs_b = nv.quantize(bk)
     bp = nv.pack_weights(b_q.view(1, N, K // 2), b_sf.view(1, N, K // 16))
+    bp_nv = bp
+    if mx:
+        bmq, bms = nv.to_mx(b_q, b_sf)
+        bp = nv.pack_weights(bmq.view(1, N, K // 2), bms.view(1, N, K // 16))
     a_q, a_sf, gs_a = nv.quantize(a)
     off = torch.tensor([0, M], dtype=torch.int32, device=dev)
     c = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
@@ -242,9 +268,12 @@ def bench_dense(w, steps, warmup, dev):
     gws = torch.empty(nv.gemm_splitk_workspace_bytes(nv.EPI_BF16, M, N, K, 1), dtype=torch.uint8,
                       device=dev)
     qbuf = (a_q, a_sf, gs_a)
-    quant = lambda: nv.quantize(a, out=qbuf)
+    def quant():
+        nv.quantize(a, out=qbuf)
+        if mx:
+            nv.to_mx(a_q, a_sf, out=(a_q, a_sf))
     gemm = lambda: nv.grouped_gemm(nv.EPI_BF16, a_q, a_sf, gs_a, off, bp, gs_b, M, out=c,
-                                   workspace=gws)
+                                   workspace=gws, mx=mx)
 
     def step():
         quant()
@@ -257,7 +286,9 @@ def bench_dense(w, steps, warmup, dev):
         ", ".join(f"{n}={v:.4f}" for n, v in st_ms.items()))
     flops = 2.0 * M * N * K
     nbytes = nvfp4_bytes(M, K) + nvfp4_bytes(N, K) + 2.0 * M * N
-    roof = roofline("grouped_gemm_kernel<BF16 epilogue> (dense)", flops, nbytes, st_ms["gemm"])
+    roof = roofline("grouped_gemm_kernel<BF16 epilogue> (dense)" + (" MX" if mx else ""), flops,
+                    nbytes, st_ms["gemm"],
+                    peak=FP4_MFMA_PEAK_TFLOPS if mx else FP16_MFMA_PEAK_TFLOPS)
     extra = {"ms_percentiles": pct, "stages_ms": {n: round(v, 4) for n, v in st_ms.items()},
              "gemm_tflops": round(flops / (st_ms["gemm"] * 1e-3) / 1e12, 2),
              "split_k": gws.numel() > nv.gemm_workspace_bytes(),
@@ -321,6 +352,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="prefill", choices=sorted(I.WORKLOADS))
+    ap.add_argument("--variant", default="nvfp4", choices=["nvfp4", "mx"],
+                    help="nvfp4: exact E4M3/16 path (FP16 MFMA); mx: NVFP4 re-encoded to "
+                         "E8M0/32 on the scaled FP4 MFMA")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -341,12 +375,14 @@ def main():
     dev = "cuda:0"
     torch.cuda.set_device(0)
     w = I.WORKLOADS[args.workload]
+    mx = args.variant == "mx"
     common = {"n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
-              "scaling": "weak", "vs_baseline": None, "dtype": "fp16",
+              "scaling": "weak", "vs_baseline": None, "dtype": "fp4" if mx else "fp16",
+              "variant": "mx (E2M1 + E8M0/32, scaled FP4 MFMA)" if mx else "nvfp4 (exact decode, FP16 MFMA)",
               "data": "synthetic (seeded; weights N(0,0.02), activations N(0,1))"}
     if w.dense_mkn:
         M, K, N = w.dense_mkn
-        value, ms_step, roof, extra = bench_dense(w, args.steps, args.warmup, dev)
+        value, ms_step, roof, extra = bench_dense(w, args.steps, args.warmup, dev, mx)
         line = {"metric": f"NVFP4 dense linear TFLOPS, M={M} K={K} N={N} (quantize A + GEMM)",
                 "value": round(value, 3), "unit": "TFLOPS", "ms_per_step": round(ms_step, 4),
                 **common,
@@ -357,7 +393,7 @@ def main():
                 "roofline": roof, **extra, "cpu_baseline": None}
         print(json.dumps(line), flush=True)
         return
-    value, ms_step, roof, extra, keep = bench_moe(w, args.steps, args.warmup, dev)
+    value, ms_step, roof, extra, keep = bench_moe(w, args.steps, args.warmup, dev, mx)
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample")
@@ -384,6 +420,7 @@ def main():
         "quantize_gbs": round(extra["quantize_gbs"], 1),
         "combine_gbs": round(extra["combine_gbs"], 1),
         "cpu_baseline": cpu,
+        **{n: extra[n] for n in ("mx_vs_exact_cosine", "mx_vs_exact_maxabs_over_rms") if n in extra},
     }
     print(json.dumps(line), flush=True)
 
