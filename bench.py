@@ -42,8 +42,8 @@ RIDGE = FP16_MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)   # flop per byte
 # each scaled by the ratio of known bytes to the counter's reading for a plain
 # 1 GiB device copy (--copy-calibration).  Reported only while the GEMM
 # sources hash to the value the counters were taken with; otherwise null.
-TRAFFIC = {("prefill", "l1"): 10024521143}
-TRAFFIC_SRC_SHA = "0e71fb3699d67992"
+TRAFFIC = {("prefill", "l1", "nvfp4"): 8886700000, ("prefill", "l1", "mx"): 8429700000}
+TRAFFIC_SRC_SHA = "2a52a2900b76ba88"
 
 
 def gemm_src_sha():
@@ -222,7 +222,8 @@ def bench_moe(w, steps, warmup, dev, mx=False):
     peak = FP4_MFMA_PEAK_TFLOPS if mx else FP16_MFMA_PEAK_TFLOPS
     roof = roofline("grouped_gemm_kernel<SwiGLU+NVFP4 epilogue> (L1)" + (" MX" if mx else ""),
                     l1_flops, l1_bytes, st_ms["l1_gemm_swiglu_requant"],
-                    None if mx else (TRAFFIC.get((w.name, "l1")) if TRAFFIC_SRC_SHA == gemm_src_sha() else None),
+                    TRAFFIC.get((w.name, "l1", "mx" if mx else "nvfp4"))
+                    if TRAFFIC_SRC_SHA == gemm_src_sha() else None,
                     peak=peak)
     extra = {
         "ms_percentiles": pct,
