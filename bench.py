@@ -64,10 +64,11 @@ def moe_flops(T, H, Iw, k):
     return 2.0 * T * k * (H * 2 * Iw + Iw * H)
 
 
-def build_weights(w, dev, chunk=32, keep_rowmajor=False):
+def build_weights(w, dev, chunk=32, keep_rowmajor=False, n_experts=None):
     w1s, w2s = [], []
-    for e0 in range(0, w.E, chunk):
-        es = range(e0, min(w.E, e0 + chunk))
+    n = w.E if n_experts is None else n_experts
+    for e0 in range(0, n, chunk):
+        es = range(e0, min(n, e0 + chunk))
         pairs = [I.make_expert_weights(w, e, dev) for e in es]
         w1s.append(torch.stack([p[0] for p in pairs]))
         w2s.append(torch.stack([p[1] for p in pairs]))
@@ -142,6 +143,27 @@ def time_loop(fn, steps):
         for _ in range(steps):
             fn()
     return ev.ms() / steps
+
+
+def bench_shared(w, steps, warmup, dev):
+    """The forward plus one shared expert (E + 1 experts, the shared one
+    last, every token through it with weight 1): whole-forward time only."""
+    log(f"[bench] building weights for {w.name} + shared expert: E={w.E}+1 H={w.H} I={w.I}")
+    ew = build_weights(w, dev, n_experts=w.E + 1)
+    x = I.make_x(w, dev)
+    ids_h, tw_h = I.make_routing(w)
+    ids = torch.from_numpy(ids_h).to(dev)
+    tw = torch.from_numpy(tw_h).to(dev)
+    gs_h = torch.tensor([w.gs_h], dtype=torch.float32, device=dev)
+    out = torch.empty((w.T, w.H), dtype=torch.bfloat16, device=dev)
+    ws = nv.forward_shared_workspace(w.T, w.H, w.I, w.E, w.k, dev)
+    step = lambda: nv.moe_expert_forward_shared(x, ids, tw, ew, gs_h, out=out, workspace=ws)
+    for _ in range(warmup):
+        step()
+    ms_step, pct = timed_steps(step, steps)
+    log(f"[bench] forward + shared expert {ms_step:.3f} ms/step")
+    flops = moe_flops(w.T, w.H, w.I, w.k + 1)
+    return flops / (ms_step * 1e-3) / 1e12, ms_step, pct
 
 
 def bench_moe(w, steps, warmup, dev, mx=False):
@@ -356,6 +378,8 @@ def main():
     ap.add_argument("--variant", default="nvfp4", choices=["nvfp4", "mx"],
                     help="nvfp4: exact E4M3/16 path (FP16 MFMA); mx: NVFP4 re-encoded to "
                          "E8M0/32 on the scaled FP4 MFMA")
+    ap.add_argument("--shared", action="store_true",
+                    help="add one shared expert (every token, weight 1) to the MoE forward")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -392,6 +416,18 @@ def main():
                 "frac_fp16_mfma_peak": round(value / FP16_MFMA_PEAK_TFLOPS, 4),
                 "frac_fp4_mfma_peak": round(value / FP4_MFMA_PEAK_TFLOPS, 4),
                 "roofline": roof, **extra, "cpu_baseline": None}
+        print(json.dumps(line), flush=True)
+        return
+    if args.shared:
+        value, ms_step, pct = bench_shared(w, args.steps, args.warmup, dev)
+        line = {"metric": f"NVFP4 MoE fwd + shared expert TFLOPS, T={w.T} E={w.E}+1 top-{w.k}",
+                "value": round(value, 3), "unit": "TFLOPS", "ms_per_step": round(ms_step, 4),
+                **common,
+                "config": {"workload": f"{w.name} + shared expert T={w.T} H={w.H} I={w.I} "
+                                       f"E={w.E}+1 top-{w.k}+1", "parallelism": "single GPU"},
+                "tokens_per_s": round(w.T / (ms_step * 1e-3), 1),
+                "frac_fp16_mfma_peak": round(value / FP16_MFMA_PEAK_TFLOPS, 4),
+                "ms_percentiles": pct, "cpu_baseline": None}
         print(json.dumps(line), flush=True)
         return
     value, ms_step, roof, extra, keep = bench_moe(w, args.steps, args.warmup, dev, mx)

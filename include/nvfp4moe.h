@@ -317,6 +317,32 @@ nvfp4_status moe_expert_forward(const void* x_bf16, int64_t T, int64_t H, int64_
                                 const float* gs_h, void* out_bf16, const nvfp4_moe_taps* taps,
                                 void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * The expert forward with a shared expert.
+ * README "NVFP4 MegaMoE Kernel", "What We Have": the single-expert NVFP4
+ * linear serves the shared experts; CURRENT_BUG.md "What Works" lists the
+ * shared expert among the NVFP4 layers.  Every token also goes through one
+ * shared expert (an expert MLP of the same shape), whose output is added in
+ * the combine:
+ *   out[t] = bf16_rne( sum_{j<k} w[t][j] * y[route j of t] + y_shared[t] ),
+ * fp32 sum in slot order with the shared term last.
+ * Weights: E + 1 experts packed as for moe_expert_forward, the routed ones
+ * first and the shared expert last (index E); gs_w1, gs_w2 [E+1].
+ * Internally every token gets slot k = expert E with weight 1 (routed ids
+ * outside [0, E) stay invalid) and the forward runs with E + 1 experts and
+ * k + 1 slots: taps are sized for T*(k+1) rows and E+2 offsets.
+ * Shapes: as moe_expert_forward with 1 <= k <= 63, 1 <= E <= 4095.
+ * Workspace: moe_expert_forward_shared_workspace_size() bytes.
+ * ---------------------------------------------------------------------- */
+size_t moe_expert_forward_shared_workspace_size(int64_t T, int64_t H, int64_t I, int E, int k);
+nvfp4_status moe_expert_forward_shared(const void* x_bf16, int64_t T, int64_t H, int64_t I, int E,
+                                       int k, const int32_t* topk_ids, const float* topk_w,
+                                       const uint8_t* w1_q, const uint8_t* w1_sf,
+                                       const float* gs_w1, const uint8_t* w2_q,
+                                       const uint8_t* w2_sf, const float* gs_w2, const float* gs_h,
+                                       void* out_bf16, const nvfp4_moe_taps* taps, void* ws,
+                                       size_t ws_bytes, void* stream);
+
 /* MX variant of moe_expert_forward (see nvfp4_to_mx above). */
 nvfp4_status moe_expert_forward_mx(const void* x_bf16, int64_t T, int64_t H, int64_t I, int E,
                                    int k, const int32_t* topk_ids, const float* topk_w,

@@ -8,6 +8,7 @@ seeded synthetic workloads.
 
 from .binding import (  # noqa: F401
     EPI_BF16, EPI_SWIGLU_NVFP4, ExpertWeights, Nvfp4Error, PackedWeight, Taps, forward_workspace,
+    forward_shared_workspace, moe_expert_forward_shared,
     gemm_splitk_workspace_bytes, gemm_workspace_bytes,
     grouped_gemm, lib, moe_combine, moe_expert_forward, moe_route, mx_expert_weights, pack_weights,
     prepare_expert_weights, quantize, router_topk, to_mx, weight_layout,

@@ -58,6 +58,8 @@ SIGNATURES = {
 # the MX variants take the same arguments as their NVFP4 counterparts
 SIGNATURES["nvfp4_mx_grouped_gemm"] = SIGNATURES["nvfp4_grouped_gemm"]
 SIGNATURES["moe_expert_forward_mx"] = SIGNATURES["moe_expert_forward"]
+SIGNATURES["moe_expert_forward_shared"] = SIGNATURES["moe_expert_forward"]
+SIGNATURES["moe_expert_forward_shared_workspace_size"] = SIGNATURES["moe_expert_forward_workspace_size"]
 
 
 class Taps(ctypes.Structure):
@@ -351,6 +353,41 @@ def moe_expert_forward(x, topk_ids, topk_w, w: ExpertWeights, gs_h, out=None, ta
               _ptr(w.gs_w1), _ptr(w.w2.q), _ptr(w.w2.sf), _ptr(w.gs_w2), _ptr(gs_h), _ptr(o),
               ctypes.byref(tp) if tp is not None else None, _ptr(ws), ws.numel(), _stream(dev)),
            "moe_expert_forward_mx" if w.mx else "moe_expert_forward")
+    return o
+
+
+def forward_shared_workspace(T, H, I, E, k, device):
+    return _workspace(lib().moe_expert_forward_shared_workspace_size(T, H, I, E, k), device)
+
+
+def moe_expert_forward_shared(x, topk_ids, topk_w, w: ExpertWeights, gs_h, out=None, taps=None,
+                              workspace=None):
+    """The expert forward plus one shared expert: ``w`` holds E + 1 experts,
+    the routed ones first and the shared expert last; topk_ids index the E
+    routed ones.  Taps are sized for T*(k+1) rows and E+2 offsets."""
+    _dev(x, torch.bfloat16, "x")
+    T, H = x.shape
+    E, I = w.E - 1, w.I
+    k = topk_ids.shape[1]
+    dev = x.device
+    _dev(topk_ids, torch.int32, "topk_ids", (T, k))
+    _dev(topk_w, torch.float32, "topk_w", (T, k))
+    if w.mx:
+        raise ValueError("the shared-expert forward takes the NVFP4 weights")
+    if E < 1 or w.H != H or w.w2.N != H or w.w2.K != I:
+        raise ValueError("weight shapes do not match x (E + 1 experts expected)")
+    _dev(w.gs_w1, torch.float32, "gs_w1", (E + 1,))
+    _dev(w.gs_w2, torch.float32, "gs_w2", (E + 1,))
+    _dev(gs_h, torch.float32, "gs_h", (1,))
+    o = out if out is not None else torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    L = lib()
+    ws = workspace if workspace is not None else forward_shared_workspace(T, H, I, E, k, dev)
+    tp = Taps(**{name: t.data_ptr() for name, t in taps.items()}) if taps else None
+    _check(L.moe_expert_forward_shared(_ptr(x), T, H, I, E, k, _ptr(topk_ids), _ptr(topk_w),
+                                       _ptr(w.w1.q), _ptr(w.w1.sf), _ptr(w.gs_w1), _ptr(w.w2.q),
+                                       _ptr(w.w2.sf), _ptr(w.gs_w2), _ptr(gs_h), _ptr(o),
+                                       ctypes.byref(tp) if tp is not None else None, _ptr(ws),
+                                       ws.numel(), _stream(dev)), "moe_expert_forward_shared")
     return o
 
 

@@ -386,7 +386,7 @@ nvfp4_status forward_impl(int mx, const void* x_bf16, int64_t T, int64_t H, int6
                           const uint8_t* w1_sf, const float* gs_w1, const uint8_t* w2_q,
                           const uint8_t* w2_sf, const float* gs_w2, const float* gs_h,
                           void* out_bf16, const nvfp4_moe_taps* taps, void* ws, size_t ws_bytes,
-                          void* stream) {
+                          void* stream, bool check_only = false) {
   if (T < 0) return fail(NVFP4_ERR_SHAPE, "T must be >= 0");
   if (H < 128 || H % 128) return fail(NVFP4_ERR_SHAPE, "H must be a positive multiple of 128 (got %lld)", (long long)H);
   if (I < 128 || I % 128) return fail(NVFP4_ERR_SHAPE, "I must be a positive multiple of 128 (got %lld)", (long long)I);
@@ -423,6 +423,7 @@ nvfp4_status forward_impl(int mx, const void* x_bf16, int64_t T, int64_t H, int6
     return fail(NVFP4_ERR_INVALID_ARG, "tap buffers must be 16-byte (codes, y) and 8-byte (scales) aligned");
   nvfp4_status st = check_arch();
   if (st != NVFP4_OK) return st;
+  if (check_only) return NVFP4_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t M = T * k;
   hipError_t err = hipSuccess;
@@ -470,6 +471,46 @@ nvfp4_status moe_expert_forward(const void* x_bf16, int64_t T, int64_t H, int64_
                                 size_t ws_bytes, void* stream) {
   return forward_impl(0, x_bf16, T, H, I, E, k, topk_ids, topk_w, w1_q, w1_sf, gs_w1, w2_q, w2_sf,
                       gs_w2, gs_h, out_bf16, taps, ws, ws_bytes, stream);
+}
+
+size_t moe_expert_forward_shared_workspace_size(int64_t T, int64_t H, int64_t I, int E, int k) {
+  if (T < 0 || H <= 0 || I <= 0 || E < 1 || k < 1) return 0;
+  return fwd_layout(T, H, I, E + 1, k + 1).total + 2 * align256(sizeof(int32_t) * (size_t)(T * (k + 1)));
+}
+
+nvfp4_status moe_expert_forward_shared(const void* x_bf16, int64_t T, int64_t H, int64_t I, int E,
+                                       int k, const int32_t* topk_ids, const float* topk_w,
+                                       const uint8_t* w1_q, const uint8_t* w1_sf,
+                                       const float* gs_w1, const uint8_t* w2_q,
+                                       const uint8_t* w2_sf, const float* gs_w2, const float* gs_h,
+                                       void* out_bf16, const nvfp4_moe_taps* taps, void* ws,
+                                       size_t ws_bytes, void* stream) {
+  if (T < 0) return fail(NVFP4_ERR_SHAPE, "T must be >= 0");
+  if (k < 1 || k > 63) return fail(NVFP4_ERR_SHAPE, "k must be in [1, 63] with a shared expert (got %d)", k);
+  if (E < 1 || E > 4095) return fail(NVFP4_ERR_SHAPE, "E must be in [1, 4095] with a shared expert (got %d)", E);
+  if (H <= 0 || I <= 0) return fail(NVFP4_ERR_SHAPE, "H and I must be positive");
+  if (T * (k + 1) >= (int64_t(1) << 31)) return fail(NVFP4_ERR_SHAPE, "T*(k+1) must be < 2^31");
+  if (T > 0 && (!topk_ids || !topk_w)) return fail(NVFP4_ERR_INVALID_ARG, "topk_ids and topk_w must be non-NULL");
+  const size_t core = fwd_layout(T, H, I, E + 1, k + 1).total;
+  const size_t need = moe_expert_forward_shared_workspace_size(T, H, I, E, k);
+  if (ws == nullptr || ws_bytes < need)
+    return fail(NVFP4_ERR_WORKSPACE, "moe_expert_forward_shared needs %zu workspace bytes (got %zu)", need, ws_bytes);
+  if (!aligned(ws, 256)) return fail(NVFP4_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  int32_t* ids2 = reinterpret_cast<int32_t*>(base + core);
+  float* w2 = reinterpret_cast<float*>(base + core + align256(sizeof(int32_t) * (size_t)(T * (k + 1))));
+  if (T > 0) {
+    // the checks of the routed forward run first, so nothing is enqueued on a bad call
+    const nvfp4_status st = forward_impl(0, x_bf16, T, H, I, E + 1, k + 1, ids2, w2, w1_q, w1_sf,
+                                         gs_w1, w2_q, w2_sf, gs_w2, gs_h, out_bf16, taps, ws, core,
+                                         nullptr, /*check_only=*/true);
+    if (st != NVFP4_OK) return st;
+    const hipError_t err = nvfp4::launch_route_add_shared(topk_ids, topk_w, T, k, E, ids2, w2,
+                                                          static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return hip_fail(err, "moe_expert_forward_shared routing");
+  }
+  return forward_impl(0, x_bf16, T, H, I, E + 1, k + 1, ids2, w2, w1_q, w1_sf, gs_w1, w2_q, w2_sf,
+                      gs_w2, gs_h, out_bf16, taps, ws, core, stream, false);
 }
 
 nvfp4_status moe_expert_forward_mx(const void* x_bf16, int64_t T, int64_t H, int64_t I, int E,

@@ -28,6 +28,10 @@ hipError_t launch_route(const int32_t* topk_ids, int64_t T, int k, int E, int32_
                         int32_t* perm, int32_t* inv_perm, int32_t* invalid_count, void* ws,
                         hipStream_t stream);
 
+// slot k of every token -> expert E with weight 1 (ids [T][k+1], w [T][k+1])
+hipError_t launch_route_add_shared(const int32_t* ids, const float* w, int64_t T, int k, int E,
+                                   int32_t* ids_out, float* w_out, hipStream_t stream);
+
 // layout.hip
 int64_t packed_rows(int64_t N);
 hipError_t launch_pack_weights(const uint8_t* q, const uint8_t* sf, int64_t E, int64_t N, int64_t K,

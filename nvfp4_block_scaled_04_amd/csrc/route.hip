@@ -165,7 +165,39 @@ __global__ __launch_bounds__(64) void route_scatter_kernel(
   }
 }
 
+// Routing with a shared expert: slot k of every token is expert E with
+// weight 1; routed ids outside [0, E) become -1 so that they stay invalid
+// (and are never taken for the shared expert E).
+__global__ __launch_bounds__(256) void route_add_shared_kernel(
+    const int32_t* __restrict__ ids, const float* __restrict__ w, int64_t T, int k, int E,
+    int32_t* __restrict__ ids_out, float* __restrict__ w_out) {
+  const int64_t n = T * (k + 1);
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t t = i / (k + 1);
+    const int j = (int)(i - t * (k + 1));
+    if (j < k) {
+      const int32_t id = ids[t * k + j];
+      ids_out[i] = (id >= 0 && id < E) ? id : -1;
+      w_out[i] = w[t * k + j];
+    } else {
+      ids_out[i] = E;
+      w_out[i] = 1.0f;
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_route_add_shared(const int32_t* ids, const float* w, int64_t T, int k, int E,
+                                   int32_t* ids_out, float* w_out, hipStream_t stream) {
+  const int64_t n = T * (k + 1);
+  if (n == 0) return hipSuccess;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  route_add_shared_kernel<<<(unsigned)blocks, 256, 0, stream>>>(ids, w, T, k, E, ids_out, w_out);
+  return hipGetLastError();
+}
 
 int64_t route_chunks(int64_t T, int k) {
   const int64_t M = T * k;

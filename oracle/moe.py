@@ -131,3 +131,35 @@ def moe_forward(x_bits, topk_ids, topk_w, wts, gs_h, E, experts=None):
     return dict(a_q=a_q, a_sf=a_sf, gs_a=gs_a, offsets=offsets, perm=perm,
                 inv_perm=inv_perm, n_invalid=n_invalid, h=h, h_q=h_q, h_sf=h_sf,
                 y=y, out=out)
+
+
+def moe_forward_shared(x_bits, topk_ids, topk_w, wts, gs_h, E):
+    """The expert forward with one shared expert added in the combine.
+
+    README ("NVFP4 MegaMoE Kernel"), section "What We Have": the single-expert
+    NVFP4 linear serves the shared experts; CURRENT_BUG.md, "What Works",
+    lists the shared expert among the NVFP4 layers.  Reading: the shared
+    expert is an expert MLP of the routed shape (L1 -> SwiGLU -> requantise
+    -> L2) applied to every token's quantised row, and its BF16 output is
+    added with weight 1 after the k routed terms:
+        out[t] = bf16( sum_j w[t, j] * y[route j of t] + y_shared[t] ).
+    ``wts`` holds E + 1 experts; index E is the shared one.
+    """
+    T, k = topk_ids.shape
+    routed = moe_forward(x_bits, topk_ids, topk_w, wts, gs_h, E)
+    a_q, a_sf, gs_a = routed["a_q"], routed["a_sf"], routed["gs_a"]
+    gs_h = F32(gs_h)
+    h_s = l1_swiglu(a_q, a_sf, gs_a, wts["w1_q"][E], wts["w1_sf"][E], wts["gs_w1"][E])
+    c_s, s_s = quantize_blocks(h_s, gs_h)
+    y_s = l2(pack_codes(c_s), s_s, gs_h, wts["w2_q"][E], wts["w2_sf"][E], wts["gs_w2"][E])
+    y = bf16_bits_to_f32(routed["y"]).astype(np.float64)
+    w = np.asarray(topk_w, dtype=np.float32).astype(np.float64)
+    n_valid = int(routed["offsets"][E])
+    out = np.zeros((T, y.shape[1]), dtype=np.float64)
+    for j in range(k):
+        d = routed["inv_perm"].reshape(T, k)[:, j]
+        ok = d < n_valid
+        out += w[:, j:j + 1] * np.where(ok[:, None], y[np.minimum(d, y.shape[0] - 1)], 0.0)
+    out += bf16_bits_to_f32(y_s).astype(np.float64)
+    routed.update(h_shared=h_s, y_shared=y_s, out=round_to_bf16(out))
+    return routed

@@ -175,3 +175,17 @@ def test_mx_entry_points_reject(L):
         FAKE, FAKE, None, FAKE, kw.get("wsb", 1 << 30), None)
     assert f(H=200) == -2
     assert f(wsb=16) == -3
+
+
+def test_shared_forward_rejects(L):
+    f = lambda **kw: L.moe_expert_forward_shared(
+        FAKE, kw.get("T", 4), kw.get("H", 256), 128, kw.get("E", 4), kw.get("k", 2), FAKE, FAKE,
+        FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, kw.get("ws", FAKE),
+        kw.get("wsb", 1 << 30), None)
+    assert f(k=64) == -2                      # k + 1 slots must fit 64
+    assert f(E=4096) == -2                    # E + 1 experts must fit 4096
+    assert f(H=200) == -2                     # checked by the routed forward before anything runs
+    assert f(wsb=16) == -3
+    assert f(ws=FAKE + 16) == -3
+    need = L.moe_expert_forward_shared_workspace_size(64, 256, 128, 4, 2)
+    assert need > L.moe_expert_forward_workspace_size(64, 256, 128, 5, 3)

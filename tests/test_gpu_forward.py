@@ -193,3 +193,43 @@ def test_forward_full_size_sampled_tokens(name):
         ref_out = bf16_values(O.round_to_bf16(acc))
         if not tie:
             assert_close(bf16_values(host(out)[t]), ref_out, f"{name} t={t} out")
+
+
+# ----------------------------------------------------------- shared expert
+
+@pytest.mark.parametrize("name,invalid", [("tiny", False), ("tiny", True)])
+def test_forward_with_shared_expert(name, invalid):
+    """Every token also through a shared expert (index E of E + 1 experts),
+    added in the combine; against the oracle's own formulation (routed sum
+    plus the shared MLP per token)."""
+    w = I.WORKLOADS[name]
+    pairs = [I.make_expert_weights(w, e, DEV) for e in range(w.E + 1)]
+    w1 = torch.stack([p[0] for p in pairs])
+    w2 = torch.stack([p[1] for p in pairs])
+    ew = nv.prepare_expert_weights([w1], [w2], DEV)
+    x = I.make_x(w, DEV)
+    ids, tw = I.make_routing(w)
+    if invalid:                       # an id equal to E must not reach the shared expert
+        ids = ids.copy()
+        ids[3, 0] = w.E
+        ids[5, 1] = -2
+    T, k, H, Iw = w.T, w.k, w.H, w.I
+    M = T * (k + 1)
+    z = lambda shape, dt: torch.zeros(shape, dtype=dt, device=DEV)
+    taps = dict(expert_offsets=z((w.E + 2,), torch.int32), invalid_count=z((1,), torch.int32),
+                h_f32=z((M, Iw), torch.float32), y_bf16=z((M, H), torch.bfloat16))
+    print(f"[case] forward + shared expert {name} invalid={invalid}", flush=True)
+    out = nv.moe_expert_forward_shared(x, torch.from_numpy(ids).to(DEV), torch.from_numpy(tw).to(DEV),
+                                       ew, torch.tensor([w.gs_h], dtype=torch.float32, device=DEV),
+                                       taps=taps)
+    torch.cuda.synchronize()
+    wts = O.prepare_weights(host(w1), host(w2))
+    ref = O.moe_forward_shared(host(x), ids, tw, wts, np.float32(w.gs_h), w.E)
+    off = host(taps["expert_offsets"])
+    assert off[w.E + 1] - off[w.E] == T                      # every token in the shared expert
+    assert host(taps["invalid_count"])[0] == (2 if invalid else 0)
+    assert np.array_equal(off[:w.E + 1], ref["offsets"][:w.E + 1])
+    # shared rows are the last T valid rows, in token order
+    hs = host(taps["h_f32"])[off[w.E]:off[w.E + 1]]
+    assert_close(hs, ref["h_shared"], "shared h")
+    assert_close(bf16_values(host(out)), bf16_values(ref["out"]), "out with shared expert")

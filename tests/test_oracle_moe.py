@@ -181,3 +181,51 @@ def test_nvfp4_forward_close_to_bf16_math():
     assert 0.97 < c < 0.9999
     # the global scales are divided out: magnitudes agree too
     assert 0.95 < np.linalg.norm(got) / np.linalg.norm(ref) < 1.05
+
+
+def _shared_case(seed=5, T=24, H=128, I=128, E=4, k=2):
+    rng = np.random.default_rng(seed)
+    bits = lambda a: (np.asarray(a, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    x = bits(rng.standard_normal((T, H)))
+    w1 = bits(rng.standard_normal((E + 1, H, 2 * I)) * 0.05)
+    w2 = bits(rng.standard_normal((E + 1, I, H)) * 0.05)
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    tw = rng.random((T, k)).astype(np.float32)
+    return x, w1, w2, ids, tw
+
+
+def test_shared_expert_with_zero_weights_is_the_routed_forward():
+    x, w1, w2, ids, tw = _shared_case()
+    w1[-1] = 0
+    w2[-1] = 0
+    wts = O.prepare_weights(w1, w2)
+    a = O.moe_forward_shared(x, ids, tw, wts, np.float32(64.0), 4)["out"]
+    b = O.moe_forward(x, ids, tw, wts, np.float32(64.0), 4)["out"]
+    assert np.array_equal(a, b)
+
+
+def test_shared_expert_alone_is_the_dense_mlp():
+    """Routing weights 0: out is the shared expert's own BF16 output,
+    composed here from the quantiser and the GEMMs on all tokens."""
+    x, w1, w2, ids, tw = _shared_case(6)
+    wts = O.prepare_weights(w1, w2)
+    got = O.moe_forward_shared(x, ids, np.zeros_like(tw), wts, np.float32(64.0), 4)["out"]
+    aq, asf, ga = Q.quantize_nvfp4(x)
+    h = O.l1_swiglu(aq, asf, ga[0], wts["w1_q"][4], wts["w1_sf"][4], wts["gs_w1"][4])
+    c, s = Q.quantize_blocks(h, np.float32(64.0))
+    y = O.l2(Q.pack_codes(c), s, np.float32(64.0), wts["w2_q"][4], wts["w2_sf"][4], wts["gs_w2"][4])
+    assert np.array_equal(got, y)
+
+
+def test_shared_expert_equals_one_more_routed_slot():
+    """The shared expert is an expert every token visits with weight 1, added
+    after the routed slots: routing each token to it as slot k gives the same
+    output bit for bit."""
+    x, w1, w2, ids, tw = _shared_case(7)
+    wts = O.prepare_weights(w1, w2)
+    got = O.moe_forward_shared(x, ids, tw, wts, np.float32(64.0), 4)["out"]
+    T, k = ids.shape
+    ids2 = np.concatenate([ids, np.full((T, 1), 4, np.int32)], axis=1)
+    tw2 = np.concatenate([tw, np.ones((T, 1), np.float32)], axis=1)
+    ref = O.moe_forward(x, ids2, tw2, wts, np.float32(64.0), 5)["out"]
+    assert np.array_equal(got, ref)
