@@ -7,15 +7,15 @@
 // The flat pairs f = t*k + j are cut into C chunks of `chunk` entries.
 //   route_hist     grid C:  LDS histogram of each chunk -> hist[b][c], bucket-
 //                           major (bucket E collects ids outside [0, E))
-//   route_scan     1 block: one wave per bucket at a time: the bucket's total
-//                           over chunks, an exclusive scan of the totals over
-//                           buckets -> expert offsets, then the wave's
-//                           exclusive scan over chunks turns hist[b][c] into
-//                           chunk c's first output row of bucket b
-//   route_scatter  grid C, one wave: walks its chunk in order, 64 entries at
-//                           a time; a lane's rank among equal buckets of the
-//                           batch comes from a ballot, so every bucket keeps
-//                           increasing f (a stable counting sort).
+//   route_scan     grid E+1, one wave per bucket b: hist[b][c] becomes the
+//                           rows of b in chunks before c (exclusive scan over
+//                           chunks); total[b] = rows of b
+//   route_scatter  grid C, one wave: exclusive scan of total[] over buckets
+//                           (the bucket bases; block 0 writes them as the
+//                           expert offsets), then walks its chunk in order,
+//                           64 entries at a time; a lane's rank among equal
+//                           buckets of the batch comes from a ballot, so every
+//                           bucket keeps increasing f (a stable counting sort).
 // All integer; integer atomics only in LDS, where order cannot matter.
 #include "internal.hpp"
 
@@ -24,7 +24,6 @@ namespace nvfp4 {
 namespace {
 
 constexpr int kHistThreads = 256;
-constexpr int kScanThreads = 1024;
 constexpr int64_t kMinChunk = 256;
 constexpr int64_t kMaxChunks = 1024;
 
@@ -64,75 +63,49 @@ __device__ __forceinline__ int32_t wave_incl_scan(int32_t v, int lane) {
   return v;
 }
 
-__global__ __launch_bounds__(kScanThreads) void route_scan_kernel(
-    int32_t* __restrict__ hist, int64_t C, int E, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ invalid_count) {
-  extern __shared__ int32_t sm[];        // total[E+1] then part[kScanThreads]
-  const int nb = E + 1;
-  int32_t* total = sm;
-  int32_t* part = sm + nb;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  constexpr int kWaves = kScanThreads / 64;
-  // per-bucket total over chunks (one wave per bucket)
-  for (int b = wave; b < nb; b += kWaves) {
-    const int32_t* h = hist + (int64_t)b * C;
-    int32_t s = 0;
-    for (int64_t c = lane; c < C; c += 64) s += h[c];
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
-    if (lane == 0) total[b] = s;
+__global__ __launch_bounds__(64) void route_scan_kernel(int32_t* __restrict__ hist, int64_t C,
+                                                        int32_t* __restrict__ total) {
+  const int lane = threadIdx.x;
+  int32_t* h = hist + (int64_t)blockIdx.x * C;
+  int32_t run = 0;
+  for (int64_t c0 = 0; c0 < C; c0 += 64) {
+    const int64_t c = c0 + lane;
+    const int32_t v = c < C ? h[c] : 0;
+    const int32_t incl = wave_incl_scan(v, lane);
+    if (c < C) h[c] = run + incl - v;
+    run += __shfl(incl, 63, 64);
   }
-  __syncthreads();
-  // exclusive scan of total[0..nb): each thread owns a contiguous segment
-  const int seg = (nb + kScanThreads - 1) / kScanThreads;
-  const int s0 = threadIdx.x * seg;
-  int32_t local = 0;
-  for (int i = 0; i < seg; ++i)
-    if (s0 + i < nb) local += total[s0 + i];
-  part[threadIdx.x] = local;
-  __syncthreads();
-  for (int off = 1; off < kScanThreads; off <<= 1) {
-    const int32_t v = threadIdx.x >= (unsigned)off ? part[threadIdx.x - off] : 0;
-    __syncthreads();
-    part[threadIdx.x] += v;
-    __syncthreads();
-  }
-  int32_t run = part[threadIdx.x] - local;  // exclusive prefix of this segment
-  for (int i = 0; i < seg; ++i) {
-    const int b = s0 + i;
-    if (b < nb) {
-      const int32_t t = total[b];
-      total[b] = run;                        // total[] now holds bucket bases
-      run += t;
-    }
-  }
-  __syncthreads();
-  // hist[b][c] -> base of b + rows of b in chunks before c
-  for (int b = wave; b < nb; b += kWaves) {
-    int32_t* h = hist + (int64_t)b * C;
-    int32_t base = total[b];
-    for (int64_t c0 = 0; c0 < C; c0 += 64) {
-      const int64_t c = c0 + lane;
-      const int32_t v = c < C ? h[c] : 0;
-      const int32_t incl = wave_incl_scan(v, lane);
-      if (c < C) h[c] = base + incl - v;
-      base += __shfl(incl, 63, 64);
-    }
-    if (lane == 0) offsets[b] = total[b];
-  }
-  if (threadIdx.x == 0 && invalid_count != nullptr) {
-    // bucket E's size: M - offsets[E], recovered from the last segment
-    invalid_count[0] = part[kScanThreads - 1] - total[E];
-  }
+  if (lane == 0) total[blockIdx.x] = run;
 }
 
 __global__ __launch_bounds__(64) void route_scatter_kernel(
     const int32_t* __restrict__ ids, int64_t M, int64_t chunk, int64_t C, int E,
-    const int32_t* __restrict__ hist, int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm) {
+    const int32_t* __restrict__ hist, const int32_t* __restrict__ total,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ invalid_count,
+    int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm) {
   extern __shared__ int32_t cur[];
   const int nb = E + 1;
   const int lane = threadIdx.x;
-  for (int b = lane; b < nb; b += 64) cur[b] = hist[(int64_t)b * C + blockIdx.x];
+  // bucket bases: each lane sums a contiguous segment of total[], then an
+  // exclusive scan of the segment sums across the wave
+  const int seg = (nb + 63) / 64;
+  const int s0 = lane * seg;
+  int32_t local = 0;
+  for (int i = 0; i < seg; ++i)
+    if (s0 + i < nb) local += total[s0 + i];
+  int32_t run = wave_incl_scan(local, lane) - local;
+  for (int i = 0; i < seg; ++i) {
+    const int b = s0 + i;
+    if (b < nb) {
+      if (blockIdx.x == 0) offsets[b] = run;
+      cur[b] = run + hist[(int64_t)b * C + blockIdx.x];
+      run += total[b];
+    }
+  }
+  if (blockIdx.x == 0 && invalid_count != nullptr && lane == (E / seg)) {
+    // the lane owning bucket E: its rows are the invalid pairs
+    invalid_count[0] = total[E];
+  }
   __syncthreads();
   const int64_t lo = (int64_t)blockIdx.x * chunk;
   const int64_t hi = lo + chunk < M ? lo + chunk : M;
@@ -207,7 +180,7 @@ int64_t route_chunks(int64_t T, int k) {
 
 size_t route_ws_bytes(int64_t T, int k, int E) {
   const int64_t C = route_chunks(T, k);
-  const int64_t n = (C > 0 ? C : 1) * (int64_t)(E + 1);
+  const int64_t n = (C > 0 ? C : 1) * (int64_t)(E + 1) + (E + 1);   // hist, then total
   return (size_t)n * sizeof(int32_t);
 }
 
@@ -217,17 +190,19 @@ hipError_t launch_route(const int32_t* topk_ids, int64_t T, int k, int E, int32_
   const int64_t M = T * k;
   const int64_t ch = chunk_size(M);
   const int64_t C = (M + ch - 1) / ch;
+  if (C == 0) {                    // no pairs: every offset and the invalid count are 0
+    fill_i32(offsets, 0, E + 1, stream);
+    if (invalid_count != nullptr) fill_i32(invalid_count, 0, 1, stream);
+    return hipGetLastError();
+  }
   int32_t* hist = static_cast<int32_t*>(ws);
+  int32_t* total = hist + C * (int64_t)(E + 1);
   const size_t lds_hist = (size_t)(E + 1) * sizeof(int32_t);
-  if (C > 0) {
-    route_hist_kernel<<<(unsigned)C, kHistThreads, lds_hist, stream>>>(topk_ids, M, ch, C, E, hist);
-  }
-  route_scan_kernel<<<1, kScanThreads, lds_hist + kScanThreads * sizeof(int32_t), stream>>>(
-      hist, C, E, offsets, invalid_count);
-  if (C > 0) {
-    route_scatter_kernel<<<(unsigned)C, 64, lds_hist, stream>>>(topk_ids, M, ch, C, E, hist, perm,
-                                                                inv_perm);
-  }
+  route_hist_kernel<<<(unsigned)C, kHistThreads, lds_hist, stream>>>(topk_ids, M, ch, C, E, hist);
+  route_scan_kernel<<<(unsigned)(E + 1), 64, 0, stream>>>(hist, C, total);
+  route_scatter_kernel<<<(unsigned)C, 64, lds_hist, stream>>>(topk_ids, M, ch, C, E, hist, total,
+                                                              offsets, invalid_count, perm,
+                                                              inv_perm);
   return hipGetLastError();
 }
 
