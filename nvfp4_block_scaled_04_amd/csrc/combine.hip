@@ -15,6 +15,7 @@ namespace nvfp4 {
 namespace {
 
 constexpr int kThreads = 128;
+constexpr int kBatch = 8;                   // rows whose loads are in flight together
 
 __global__ __launch_bounds__(kThreads) void combine_kernel(
     const uint4* __restrict__ y, const int32_t* __restrict__ inv_perm,
@@ -25,16 +26,28 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
   const int32_t n_valid = offsets[E];
   for (int64_t v = threadIdx.x; v < hv; v += kThreads) {
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int j = 0; j < k; ++j) {
-      const int32_t d = inv_perm[t * k + j];
-      if (d >= n_valid) continue;
-      const float w = topk_w[t * k + j];
-      const uint4 r = y[(int64_t)d * hv + v];
-      const uint32_t p[4] = {r.x, r.y, r.z, r.w};
+    for (int j0 = 0; j0 < k; j0 += kBatch) {
+      // issue the batch's row loads first, then accumulate in slot order
+      uint4 r[kBatch];
+      float w[kBatch];
+      bool ok[kBatch];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc[2 * i] = fmaf(w, bf16_to_f32(p[i] & 0xFFFFu), acc[2 * i]);
-        acc[2 * i + 1] = fmaf(w, bf16_to_f32(p[i] >> 16), acc[2 * i + 1]);
+      for (int b = 0; b < kBatch; ++b) {
+        const int j = j0 + b;
+        const int32_t d = j < k ? inv_perm[t * k + j] : n_valid;
+        ok[b] = d < n_valid;          // slots past k and invalid expert ids add nothing
+        w[b] = ok[b] ? topk_w[t * k + j] : 0.0f;
+        r[b] = ok[b] ? y[(int64_t)d * hv + v] : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) {
+        if (!ok[b]) continue;
+        const uint32_t p[4] = {r[b].x, r[b].y, r[b].z, r[b].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[2 * i] = fmaf(w[b], bf16_to_f32(p[i] & 0xFFFFu), acc[2 * i]);
+          acc[2 * i + 1] = fmaf(w[b], bf16_to_f32(p[i] >> 16), acc[2 * i + 1]);
+        }
       }
     }
     uint4 o;

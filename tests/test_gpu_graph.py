@@ -55,6 +55,48 @@ def test_graph_capture_replays_match_eager(w):
         assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), f"replay {r}"
 
 
+@pytest.mark.parametrize("variant", ["mx", "shared"])
+def test_graph_capture_variants(variant):
+    """The MX variant and the shared-expert forward replay from a graph bit
+    for bit like the eager call."""
+    w = I.custom("graph_var", T=300, H=512, I=256, E=16, k=4, seed=9)
+    print(f"[case] graph {variant}", flush=True)
+    nexp = w.E + 1 if variant == "shared" else w.E
+    pairs = [I.make_expert_weights(w, e, DEV) for e in range(nexp)]
+    ew = nv.prepare_expert_weights([torch.stack([p[0] for p in pairs])],
+                                   [torch.stack([p[1] for p in pairs])], DEV)
+    if variant == "mx":
+        ew = nv.mx_expert_weights(ew)
+    x = I.make_x(w, DEV)
+    ids_h, tw_h = I.make_routing(w)
+    ids, tw = torch.from_numpy(ids_h).to(DEV), torch.from_numpy(tw_h).to(DEV)
+    gs_h = torch.tensor([w.gs_h], dtype=torch.float32, device=DEV)
+    out = torch.empty((w.T, w.H), dtype=torch.bfloat16, device=DEV)
+    if variant == "shared":
+        ws = nv.forward_shared_workspace(w.T, w.H, w.I, w.E, w.k, DEV)
+        call = lambda: nv.moe_expert_forward_shared(x, ids, tw, ew, gs_h, out=out, workspace=ws)
+    else:
+        ws = nv.forward_workspace(w.T, w.H, w.I, w.E, w.k, DEV)
+        call = lambda: nv.moe_expert_forward(x, ids, tw, ew, gs_h, out=out, workspace=ws)
+    call()
+    torch.cuda.synchronize()
+    ref = out.clone()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            call()
+    torch.cuda.synchronize()
+    for r in range(3):
+        out.fill_(0)
+        ws.fill_(0x5A)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), f"{variant} replay {r}"
+
+
 def test_forward_is_deterministic():
     w = I.custom("determinism", T=500, H=384, I=256, E=32, k=6, routing="zipf", seed=10)
     print(f"[case] determinism {w.name}", flush=True)
