@@ -512,8 +512,17 @@ __device__ __forceinline__ void tile_at(const Params& p, const int* tprefix, int
   const int local = tix - tprefix[t.e] * p.n_tiles;
   const int nt = local / mcount;
   const int mt = local - nt * mcount;
-  t.row0 = __builtin_amdgcn_readfirstlane(p.offsets[t.e] + mt * BM);
-  t.nrows = __builtin_amdgcn_readfirstlane(min(BM, p.offsets[t.e + 1] - t.row0));
+  // The expert's 32-row blocks are spread evenly over its m tiles (at most
+  // BM/32 each, the larger shares first): with 9 blocks the tiles take 3, 3, 3
+  // rather than 4, 4, 1, since a one-block tile decodes the whole weight
+  // tile for a quarter of the MFMAs and is VALU-bound.
+  const int rows_e = p.offsets[t.e + 1] - p.offsets[t.e];
+  const int nblk = (rows_e + 31) / 32;
+  const int per = nblk / mcount, rem = nblk - per * mcount;
+  const int blk0 = mt * per + min(mt, rem);
+  const int nblk_t = per + (mt < rem ? 1 : 0);
+  t.row0 = __builtin_amdgcn_readfirstlane(p.offsets[t.e] + 32 * blk0);
+  t.nrows = __builtin_amdgcn_readfirstlane(min(32 * nblk_t, p.offsets[t.e + 1] - t.row0));
   t.n0 = (int64_t)__builtin_amdgcn_readfirstlane(nt) * BN;
   t.jv = (t.nrows + 31) / 32;
   t.split = __builtin_amdgcn_readfirstlane(split);
