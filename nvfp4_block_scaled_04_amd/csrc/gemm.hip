@@ -33,8 +33,9 @@
 // Tiling.  A block is 4 waves stacked along N (wave tile 128 N x 128 tokens,
 // 4x4 MFMA blocks, 256 fp32 accumulators per lane); decoding is done per wave
 // from packed codes in LDS, so each decoded element feeds 4 MFMAs.  Stages of
-// 128 K are double-buffered in LDS through registers.  In an expert's last
-// m tile, 32-token column blocks past the expert's rows are skipped.
+// 128 K go from HBM straight into LDS (global_load_lds), triple-buffered.  An
+// expert's rows are cut into ceil(rows/128) m tiles with its 32-row blocks
+// spread evenly over them; column blocks past a tile's rows are skipped.
 //
 // MX mode.  The same tiles, loads and epilogues run on MXFP4 operands (E2M1
 // codes, one E8M0 scale per 32 elements stored once per 16-element block, as
@@ -50,12 +51,13 @@
 // scaled by the global scales) to a caller workspace and a reduction kernel
 // sums them in split order and rounds to BF16.
 //
-// Scheduling.  A persistent grid (a multiple of 8 blocks) walks tiles in
-// windows of gridDim.x; within a window the 8 XCDs each take a contiguous
-// slice, so the blocks of one XCD share an expert's weights and tokens in
-// their L2.  Tiles are ordered expert by expert (device offsets, no host
-// sync); a block finds its expert by binary search of a per-expert tile
-// prefix kept in LDS.
+// Scheduling.  A persistent grid (one block per CU, a multiple of 8).  The
+// tile list runs expert by expert and, inside an expert, n tile by n tile
+// with the expert's m tiles innermost (device offsets, no host sync); XCD x
+// owns a contiguous eighth of it, so the tiles that share a weight n tile run
+// side by side in one L2, and its blocks claim tiles from a per-XCD counter,
+// stealing from other XCDs' ranges at the end.  A block finds a tile's expert
+// by binary search of a per-expert m-tile prefix kept in LDS.
 #include "internal.hpp"
 #include "device.hpp"
 

@@ -13,7 +13,7 @@ from nvfp4_block_scaled_04_amd import inputs as I
 from oracle import moe as O
 from oracle import quantize as Q
 from oracle import route as R
-from parity import host, bf16_values, assert_close, assert_requant_matches
+from parity import host, bf16_values, assert_close, assert_requant_matches, TAU
 import oracle_pool
 
 pytestmark = pytest.mark.gpu
@@ -233,3 +233,113 @@ def test_forward_with_shared_expert(name, invalid):
     hs = host(taps["h_f32"])[off[w.E]:off[w.E + 1]]
     assert_close(hs, ref["h_shared"], "shared h")
     assert_close(bf16_values(host(out)), bf16_values(ref["out"]), "out with shared expert")
+
+
+def test_mx_forward_prefill_sampled_token():
+    """The MX variant at full prefill size: one token's k expert rows and its
+    output against the MX oracle (weights re-encoded on both sides and
+    compared bit-exactly)."""
+    from oracle import mx as X
+    w = I.WORKLOADS["prefill"]
+    ew_mx = nv.mx_expert_weights(_big_weights(w))
+    x = I.make_x(w, DEV)
+    ids, tw = I.make_routing(w)
+    T, k, H, Iw = w.T, w.k, w.H, w.I
+    M = T * k
+    z = lambda shape, dt: torch.zeros(shape, dtype=dt, device=DEV)
+    taps = dict(a_q=z((T, H // 2), torch.uint8), a_sf=z((T, H // 16), torch.uint8),
+                gs_a=z((1,), torch.float32), inv_perm=z((M,), torch.int32),
+                h_f32=z((M, Iw), torch.float32), y_bf16=z((M, H), torch.bfloat16))
+    print("[case] mx forward prefill (sampled token)", flush=True)
+    out = nv.moe_expert_forward(x, torch.from_numpy(ids).to(DEV), torch.from_numpy(tw).to(DEV),
+                                ew_mx, torch.tensor([w.gs_h], dtype=torch.float32, device=DEV),
+                                taps=taps)
+    torch.cuda.synchronize()
+    tp = {n: host(t) for n, t in taps.items()}
+    xb = host(x)
+    gs_a = Q.global_scale(xb)
+    assert tp["gs_a"][0] == gs_a
+    t = T // 5
+    aq, asf = Q.quantize_blocks(xb[t:t + 1], gs_a)
+    amq, amsc = X.nvfp4_to_mx(Q.pack_codes(aq), asf)
+    assert np.array_equal(tp["a_q"][t], amq[0])
+    assert np.array_equal(tp["a_sf"][t], np.repeat(amsc[0], 2))
+    experts = [int(e) for e in ids[t]]
+    bf = {e: tuple(host(a) for a in I.make_expert_weights(w, e, DEV)) for e in experts}
+    ctx = mp.get_context("spawn")
+    with cf.ProcessPoolExecutor(max_workers=len(experts), mp_context=ctx) as ex:
+        res = list(ex.map(oracle_pool.expert_rows_mx, [bf[e][0] for e in experts],
+                          [bf[e][1] for e in experts], [amq] * k, [amsc] * k, [gs_a] * k,
+                          [np.float32(w.gs_h)] * k))
+    rw = ew_mx.rowmajor
+    acc = np.zeros(H)
+    tie = False
+    for j, (e, r) in enumerate(zip(experts, res)):
+        assert np.array_equal(host(rw["w1_q"][e]), r["w1_q"])
+        assert np.array_equal(host(rw["w1_sf"][e]), np.repeat(r["w1_sc"], 2, axis=1))
+        d = int(tp["inv_perm"][t * k + j])
+        assert_close(tp["h_f32"][d:d + 1], r["h"], f"mx t={t} j={j} h")
+        # a requant decision within TAU of a rounding boundary may go either
+        # way; such rows are reported and kept out of the strict y/out bound
+        near = bool(Q.near_ties(r["h"], np.float32(w.gs_h), TAU)[0].any())
+        tie |= near
+        if not near:
+            assert_close(bf16_values(tp["y_bf16"][d:d + 1]), bf16_values(r["y"]), f"mx t={t} j={j} y")
+        acc += np.float64(tw[t, j]) * bf16_values(r["y"][0])
+    print(f"[case] mx prefill token {t}: near-tie rows present: {tie}", flush=True)
+    if not tie:
+        assert_close(bf16_values(host(out)[t]), bf16_values(O.round_to_bf16(acc)), f"mx t={t} out")
+
+
+def test_shared_forward_prefill_sampled_token():
+    """The shared-expert forward at full prefill size: one token's k routed
+    rows plus its shared-expert row, and its output, against the oracle."""
+    w = I.WORKLOADS["prefill"]
+    print("[case] shared forward prefill (sampled token)", flush=True)
+    base = _big_weights(w)                                  # routed experts 0..E-1
+    sw1, sw2 = I.make_expert_weights(w, w.E, DEV)          # the shared expert
+    shared = nv.prepare_expert_weights([sw1[None]], [sw2[None]], DEV)
+    cat = lambda a, b: torch.cat([a, b])
+    rw, rs = base.rowmajor, shared.rowmajor
+    w1 = nv.pack_weights(cat(rw["w1_q"], rs["w1_q"]), cat(rw["w1_sf"], rs["w1_sf"]))
+    w2 = nv.pack_weights(cat(rw["w2_q"], rs["w2_q"]), cat(rw["w2_sf"], rs["w2_sf"]))
+    both = nv.ExpertWeights(w1, cat(base.gs_w1, shared.gs_w1), w2, cat(base.gs_w2, shared.gs_w2))
+    x = I.make_x(w, DEV)
+    ids, tw = I.make_routing(w)
+    T, k, H, Iw = w.T, w.k, w.H, w.I
+    M = T * (k + 1)
+    z = lambda shape, dt: torch.zeros(shape, dtype=dt, device=DEV)
+    taps = dict(inv_perm=z((M,), torch.int32), h_f32=z((M, Iw), torch.float32),
+                y_bf16=z((M, H), torch.bfloat16))
+    out = nv.moe_expert_forward_shared(x, torch.from_numpy(ids).to(DEV),
+                                       torch.from_numpy(tw).to(DEV), both,
+                                       torch.tensor([w.gs_h], dtype=torch.float32, device=DEV),
+                                       taps=taps)
+    torch.cuda.synchronize()
+    tp = {n: host(t) for n, t in taps.items()}
+    xb = host(x)
+    gs_a = Q.global_scale(xb)
+    t = T // 7
+    aq, asf = Q.quantize_blocks(xb[t:t + 1], gs_a)
+    aq = Q.pack_codes(aq)
+    experts = [int(e) for e in ids[t]] + [w.E]
+    bf = {e: tuple(host(a) for a in I.make_expert_weights(w, e, DEV)) for e in experts}
+    ctx = mp.get_context("spawn")
+    with cf.ProcessPoolExecutor(max_workers=len(experts), mp_context=ctx) as ex:
+        res = list(ex.map(oracle_pool.expert_rows, [bf[e][0] for e in experts],
+                          [bf[e][1] for e in experts], [aq] * (k + 1), [asf] * (k + 1),
+                          [gs_a] * (k + 1), [np.float32(w.gs_h)] * (k + 1)))
+    acc = np.zeros(H)
+    tie = False
+    for j, r in enumerate(res):
+        d = int(tp["inv_perm"][t * (k + 1) + j])
+        assert_close(tp["h_f32"][d:d + 1], r["h"], f"shared t={t} slot {j} h")
+        near = bool(Q.near_ties(r["h"], np.float32(w.gs_h), TAU)[0].any())
+        tie |= near
+        if not near:
+            assert_close(bf16_values(tp["y_bf16"][d:d + 1]), bf16_values(r["y"]), f"shared t={t} y {j}")
+        wj = np.float64(tw[t, j]) if j < k else 1.0
+        acc += wj * bf16_values(r["y"][0])
+    print(f"[case] shared prefill token {t}: near-tie rows present: {tie}", flush=True)
+    if not tie:
+        assert_close(bf16_values(host(out)[t]), bf16_values(O.round_to_bf16(acc)), f"shared t={t} out")
