@@ -58,6 +58,8 @@
 // side by side in one L2, and its blocks claim tiles from a per-XCD counter,
 // stealing from other XCDs' ranges at the end.  A block finds a tile's expert
 // by binary search of a per-expert m-tile prefix kept in LDS.
+#include <atomic>
+
 #include "internal.hpp"
 #include "device.hpp"
 
@@ -927,13 +929,28 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   }
 }
 
-int g_cu_count = 0;
+// Per-device launch facts, cached on first use with that device current:
+// the CU count (grid size, split-K choice) and, per kernel instantiation,
+// whether its dynamic LDS limit has been raised.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cus[kMaxDevices];
 
-hipError_t query_cu_count() {
-  int dev = 0;
+hipError_t current_device(int& dev) {
   hipError_t err = hipGetDevice(&dev);
   if (err != hipSuccess) return err;
-  return hipDeviceGetAttribute(&g_cu_count, hipDeviceAttributeMultiprocessorCount, dev);
+  return (dev >= 0 && dev < kMaxDevices) ? hipSuccess : hipErrorInvalidDevice;
+}
+
+hipError_t device_cus(int& cus) {
+  int dev = 0;
+  hipError_t err = current_device(dev);
+  if (err != hipSuccess) return err;
+  cus = g_cus[dev].load(std::memory_order_relaxed);
+  if (cus > 0) return hipSuccess;
+  err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (err != hipSuccess) return err;
+  g_cus[dev].store(cus, std::memory_order_relaxed);
+  return hipSuccess;
 }
 
 constexpr int kBN = 512, kBM = 128;   // the tile every launch uses
@@ -977,34 +994,35 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
   p.ksplit = 1;
   p.partial = nullptr;
   if (a.M == 0) return hipSuccess;
-  if (g_cu_count == 0) {
-    hipError_t err = query_cu_count();
-    if (err != hipSuccess) return err;
-  }
+  int dev = 0, cus = 0;
+  hipError_t err = current_device(dev);
+  if (err != hipSuccess) return err;
+  err = device_cus(cus);
+  if (err != hipSuccess) return err;
   if (EPI == kEpiPartial) {
-    p.ksplit = splitk_factor(a.epilogue, a.M, a.N, a.K, a.E, g_cu_count);
+    p.ksplit = splitk_factor(a.epilogue, a.M, a.N, a.K, a.E, cus);
     p.partial = splitk_partial(a.ws);
   }
   const int64_t tiles = tile_bound(a.M, a.N, a.E) * p.ksplit;
-  int64_t grid = g_cu_count;                              // one block per CU (LDS-limited)
+  int64_t grid = cus;                                     // one block per CU (LDS-limited)
   if (grid > tiles) grid = tiles;
   grid = (grid + 7) / 8 * 8;
   const size_t lds = (size_t)C::LDS_BYTES + sizeof(int) * (size_t)(a.E + 1);
   auto kern = grouped_gemm_kernel<BN, BM, WN, WM, EPI, FMT>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize,
-                                         (int)(C::LDS_BYTES + sizeof(int) * 4097));
+  static std::atomic<bool> attr_set[kMaxDevices];
+  if (!attr_set[dev].load(std::memory_order_relaxed)) {
+    err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                              hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)(C::LDS_BYTES + sizeof(int) * 4097));
     if (err != hipSuccess) return err;
-    attr_set = true;
+    attr_set[dev].store(true, std::memory_order_relaxed);
   }
   zero_ints_kernel<<<1, 64, 0, stream>>>(p.sched, 8);   // a kernel, not a memset: graph-safe
   kern<<<(unsigned)grid, C::NT, lds, stream>>>(p);
   if (EPI == kEpiPartial) {
     const int64_t vecs = a.M * a.N / 8;
     int64_t blocks = (vecs + 255) / 256;
-    if (blocks > 8 * (int64_t)g_cu_count) blocks = 8 * (int64_t)g_cu_count;
+    if (blocks > 8 * (int64_t)cus) blocks = 8 * (int64_t)cus;
     splitk_reduce_kernel<<<(unsigned)blocks, 256, 0, stream>>>(
         p.partial, p.ksplit, a.M, a.N, a.offsets, a.E, static_cast<uint16_t*>(a.c_bf16));
   }
@@ -1014,8 +1032,9 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
 }  // namespace
 
 size_t gemm_splitk_ws_bytes(int epilogue, int64_t M, int64_t N, int64_t K, int E) {
-  if (g_cu_count == 0 && query_cu_count() != hipSuccess) return kGemmWorkspaceBytes;
-  const int f = splitk_factor(epilogue, M, N, K, E, g_cu_count);
+  int cus = 0;
+  if (device_cus(cus) != hipSuccess) return kGemmWorkspaceBytes;
+  const int f = splitk_factor(epilogue, M, N, K, E, cus);
   if (f <= 1) return kGemmWorkspaceBytes;
   return kGemmWorkspaceBytes + 255 + (size_t)f * (size_t)M * (size_t)N * sizeof(float);
 }
@@ -1026,8 +1045,8 @@ hipError_t launch_fmt(const GemmArgs& a, hipStream_t stream) {
     return launch_cfg<kBN, kBM, 4, 1, NVFP4_EPI_SWIGLU_NVFP4, FMT>(a, stream);
   // split K only when the caller's workspace holds the partials
   if (a.M > 0 && a.ws_bytes > kGemmWorkspaceBytes &&
-      a.ws_bytes >= gemm_splitk_ws_bytes(a.epilogue, a.M, a.N, a.K, a.E) &&
-      splitk_factor(a.epilogue, a.M, a.N, a.K, a.E, g_cu_count) > 1)
+      gemm_splitk_ws_bytes(a.epilogue, a.M, a.N, a.K, a.E) > kGemmWorkspaceBytes &&
+      a.ws_bytes >= gemm_splitk_ws_bytes(a.epilogue, a.M, a.N, a.K, a.E))
     return launch_cfg<kBN, kBM, 4, 1, kEpiPartial, FMT>(a, stream);
   return launch_cfg<kBN, kBM, 4, 1, NVFP4_EPI_BF16, FMT>(a, stream);
 }

@@ -84,3 +84,16 @@ def test_router_logits_are_the_router_workloads_draw():
     rid, rtw = R.router_topk(I.make_router_logits(w), w.k)
     assert np.array_equal(ids, rid)
     np.testing.assert_allclose(tw, rtw, rtol=1e-6)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: --gpus N > 1 exits with status 2 and says so,
+    before touching a device."""
+    import subprocess
+    import sys
+    import os
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
