@@ -50,3 +50,29 @@ def test_router_prefill_shape_and_empty():
     _check(lg, 8, "prefill shape")
     ids, w = nv.router_topk(torch.zeros((0, 16), dtype=torch.float32, device=DEV), 2)
     assert ids.shape == (0, 2) and w.shape == (0, 2)
+
+
+def test_router_feeds_the_forward():
+    """Router -> expert forward on the device, end to end, against the oracle
+    router -> oracle forward (ids bit-exact, output to the floating-point bar).
+    The oracle forward takes the GPU's fp32 routing weights only after they
+    have been checked against its own to fp32 rounding."""
+    from oracle import moe as O
+    from parity import bf16_values, assert_close
+    w = I.custom("router_fwd", T=96, H=256, I=128, E=8, k=2, seed=21)
+    print("[case] router -> forward", flush=True)
+    lg = np.random.default_rng(22).standard_normal((w.T, w.E)).astype(np.float32)
+    pairs = [I.make_expert_weights(w, e, DEV) for e in range(w.E)]
+    w1 = torch.stack([p[0] for p in pairs])
+    w2 = torch.stack([p[1] for p in pairs])
+    ew = nv.prepare_expert_weights([w1], [w2], DEV)
+    x = I.make_x(w, DEV)
+    ids, tw = nv.router_topk(torch.from_numpy(lg).to(DEV), w.k)
+    out = nv.moe_expert_forward(x, ids, tw, ew, torch.tensor([w.gs_h], dtype=torch.float32, device=DEV))
+    torch.cuda.synchronize()
+    rid, rw = R.router_topk(lg, w.k)
+    assert np.array_equal(host(ids), rid)
+    np.testing.assert_allclose(host(tw), rw, rtol=2e-6, atol=1e-7)
+    ref = O.moe_forward(host(x), rid, rw.astype(np.float32), O.prepare_weights(host(w1), host(w2)),
+                        np.float32(w.gs_h), w.E)
+    assert_close(bf16_values(host(out)), bf16_values(ref["out"]), "router -> forward out")
