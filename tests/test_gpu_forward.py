@@ -235,12 +235,13 @@ def test_forward_with_shared_expert(name, invalid):
     assert_close(bf16_values(host(out)), bf16_values(ref["out"]), "out with shared expert")
 
 
-def test_mx_forward_prefill_sampled_token():
-    """The MX variant at full prefill size: one token's k expert rows and its
-    output against the MX oracle (weights re-encoded on both sides and
-    compared bit-exactly)."""
+@pytest.mark.parametrize("name", ["prefill", "decode", "skewed"])
+def test_mx_forward_sampled_token(name):
+    """The MX variant at full size: one token's k expert rows and its output
+    against the MX oracle (weights re-encoded on both sides and compared
+    bit-exactly)."""
     from oracle import mx as X
-    w = I.WORKLOADS["prefill"]
+    w = I.WORKLOADS[name]
     ew_mx = nv.mx_expert_weights(_big_weights(w))
     x = I.make_x(w, DEV)
     ids, tw = I.make_routing(w)
@@ -250,7 +251,7 @@ def test_mx_forward_prefill_sampled_token():
     taps = dict(a_q=z((T, H // 2), torch.uint8), a_sf=z((T, H // 16), torch.uint8),
                 gs_a=z((1,), torch.float32), inv_perm=z((M,), torch.int32),
                 h_f32=z((M, Iw), torch.float32), y_bf16=z((M, H), torch.bfloat16))
-    print("[case] mx forward prefill (sampled token)", flush=True)
+    print(f"[case] mx forward {name} (sampled token)", flush=True)
     out = nv.moe_expert_forward(x, torch.from_numpy(ids).to(DEV), torch.from_numpy(tw).to(DEV),
                                 ew_mx, torch.tensor([w.gs_h], dtype=torch.float32, device=DEV),
                                 taps=taps)
@@ -259,7 +260,7 @@ def test_mx_forward_prefill_sampled_token():
     xb = host(x)
     gs_a = Q.global_scale(xb)
     assert tp["gs_a"][0] == gs_a
-    t = T // 5
+    t = _sample_tokens(name, ids)[0] if name == "skewed" else T // 5
     aq, asf = Q.quantize_blocks(xb[t:t + 1], gs_a)
     amq, amsc = X.nvfp4_to_mx(Q.pack_codes(aq), asf)
     assert np.array_equal(tp["a_q"][t], amq[0])
@@ -286,16 +287,17 @@ def test_mx_forward_prefill_sampled_token():
         if not near:
             assert_close(bf16_values(tp["y_bf16"][d:d + 1]), bf16_values(r["y"]), f"mx t={t} j={j} y")
         acc += np.float64(tw[t, j]) * bf16_values(r["y"][0])
-    print(f"[case] mx prefill token {t}: near-tie rows present: {tie}", flush=True)
+    print(f"[case] mx {name} token {t}: near-tie rows present: {tie}", flush=True)
     if not tie:
         assert_close(bf16_values(host(out)[t]), bf16_values(O.round_to_bf16(acc)), f"mx t={t} out")
 
 
-def test_shared_forward_prefill_sampled_token():
-    """The shared-expert forward at full prefill size: one token's k routed
-    rows plus its shared-expert row, and its output, against the oracle."""
-    w = I.WORKLOADS["prefill"]
-    print("[case] shared forward prefill (sampled token)", flush=True)
+@pytest.mark.parametrize("name", ["prefill", "skewed"])
+def test_shared_forward_sampled_token(name):
+    """The shared-expert forward at full size: one token's k routed rows plus
+    its shared-expert row, and its output, against the oracle."""
+    w = I.WORKLOADS[name]
+    print(f"[case] shared forward {name} (sampled token)", flush=True)
     base = _big_weights(w)                                  # routed experts 0..E-1
     sw1, sw2 = I.make_expert_weights(w, w.E, DEV)          # the shared expert
     shared = nv.prepare_expert_weights([sw1[None]], [sw2[None]], DEV)
@@ -319,7 +321,7 @@ def test_shared_forward_prefill_sampled_token():
     tp = {n: host(t) for n, t in taps.items()}
     xb = host(x)
     gs_a = Q.global_scale(xb)
-    t = T // 7
+    t = _sample_tokens(name, ids)[0] if name == "skewed" else T // 7
     aq, asf = Q.quantize_blocks(xb[t:t + 1], gs_a)
     aq = Q.pack_codes(aq)
     experts = [int(e) for e in ids[t]] + [w.E]
@@ -340,6 +342,6 @@ def test_shared_forward_prefill_sampled_token():
             assert_close(bf16_values(tp["y_bf16"][d:d + 1]), bf16_values(r["y"]), f"shared t={t} y {j}")
         wj = np.float64(tw[t, j]) if j < k else 1.0
         acc += wj * bf16_values(r["y"][0])
-    print(f"[case] shared prefill token {t}: near-tie rows present: {tie}", flush=True)
+    print(f"[case] shared {name} token {t}: near-tie rows present: {tie}", flush=True)
     if not tie:
         assert_close(bf16_values(host(out)[t]), bf16_values(O.round_to_bf16(acc)), f"shared t={t} out")
