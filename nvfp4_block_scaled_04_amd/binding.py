@@ -164,7 +164,7 @@ def to_mx(q, sf, out=None):
     sc_mx (R, C/16), each scale byte stored twice); out may be (q, sf) for an
     in-place re-encoding."""
     _dev(q, torch.uint8, "q")
-    R, Ch = q.shape[0], q.shape[-1]
+    Ch = q.shape[-1]
     C = Ch * 2
     _dev(sf, torch.uint8, "sf")
     if sf.numel() != q.numel() // 8:
