@@ -214,6 +214,13 @@ def bench_moe(w, steps, warmup, dev, mx=False):
         "l2_gemm": l2,
         "combine": lambda: nv.moe_combine(y, inv, tw, off, out=out),
     }
+    if not mx:
+        # the alternative A path (not the forward's): quantise each token once
+        # straight into its k expert-order rows, for L1 without the row gather
+        sq = (torch.empty((M, H // 2), dtype=torch.uint8, device=dev),
+              torch.empty((M, H // 16), dtype=torch.uint8, device=dev),
+              torch.empty((1,), dtype=torch.float32, device=dev))
+        stages["quantize_scatter"] = lambda: nv.quantize_scatter(x, inv, off, k, out=sq)
     if mx:
         stages["to_mx_x"] = lambda: nv.to_mx(qx[0], qx[1], out=(qx[0], qx[1]))
         hq2, hs2 = torch.empty_like(h_q), torch.empty_like(h_sf)

@@ -159,6 +159,28 @@ nvfp4_status nvfp4_moe_route(const int32_t* topk_ids, int64_t T, int k, int E,
                              int32_t* invalid_count, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Quantise-and-scatter: the activation quantisation writing expert order.
+ * README "Key Lessons" 4: quantise the compact rows, then place them in the
+ * expert layout.  Same quantisation as nvfp4_quantize with a per-call global
+ * scale (one group); each token row t is quantised once and written to rows
+ * d = inv_perm[t*k + j] (j < k) of q/sf that are below expert_offsets[E]
+ * (routed pairs; rows of invalid expert ids are not written).  With these
+ * rows the L1 grouped GEMM reads its A operand without a gather
+ * (a_row_src = NULL), at the price of k copies of every quantised row.
+ * moe_expert_forward keeps the compact rows and the gather, which costs the
+ * L1 GEMM under 1% of its time, while the k copies cost more than that.
+ * x BF16 [T][H]; inv_perm, expert_offsets from nvfp4_moe_route;
+ * q uint8 [T*k][H/2], sf uint8 [T*k][H/16], gs_out float [1].
+ * Shapes: T >= 0, H % 16 == 0, 1 <= k <= 64, 1 <= E <= 4096, T*k < 2^31.
+ * Workspace: nvfp4_quantize_scatter_workspace_size() bytes (0 when T == 0).
+ * ---------------------------------------------------------------------- */
+size_t nvfp4_quantize_scatter_workspace_size(int64_t T, int64_t H);
+nvfp4_status nvfp4_quantize_scatter(const void* x_bf16, int64_t T, int64_t H, int k,
+                                    const int32_t* inv_perm, const int32_t* expert_offsets, int E,
+                                    uint8_t* q, uint8_t* sf, float* gs_out, void* ws,
+                                    size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Expert-grouped NVFP4 GEMM.
  * README "What We Have", grouped GEMM: A(M,K) x B(E,K,N) -> C(M,N), per-16
  * FP8 scales on A and B, per-expert global scales; "Fused SwiGLU — How It

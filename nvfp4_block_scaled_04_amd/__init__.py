@@ -11,7 +11,7 @@ from .binding import (  # noqa: F401
     forward_shared_workspace, moe_expert_forward_shared,
     gemm_splitk_workspace_bytes, gemm_workspace_bytes,
     grouped_gemm, lib, moe_combine, moe_expert_forward, moe_route, mx_expert_weights, pack_weights,
-    prepare_expert_weights, quantize, router_topk, to_mx, weight_layout,
+    prepare_expert_weights, quantize, quantize_scatter, router_topk, to_mx, weight_layout,
 )
 
 __version__ = "0.1.0"

@@ -46,6 +46,9 @@ SIGNATURES = {
                                    c_int, c_int64, c_int64, c_int64, c_void_p, c_void_p, c_void_p,
                                    c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                    c_size_t, c_void_p]),
+    "nvfp4_quantize_scatter_workspace_size": (c_size_t, [c_int64, c_int64]),
+    "nvfp4_quantize_scatter": (c_int, [c_void_p, c_int64, c_int64, c_int, c_void_p, c_void_p, c_int,
+                                       c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     "nvfp4_to_mx": (c_int, [c_void_p, c_void_p, c_int64, c_int64, c_void_p, c_void_p, c_void_p]),
     "nvfp4_moe_combine": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_int64, c_int, c_int,
                                   c_int64, c_void_p, c_void_p]),
@@ -157,6 +160,29 @@ def pack_weights(q, sf):
     _check(L.nvfp4_pack_weights(_ptr(q), _ptr(sf), E, N, K, _ptr(qp), _ptr(sfp), _stream(q.device)),
            "nvfp4_pack_weights")
     return PackedWeight(qp, sfp, E, N, K)
+
+
+def quantize_scatter(x, inv_perm, offsets, k, out=None):
+    """x (T, H) bf16 -> NVFP4 rows in expert order: (q (T*k, H/2), sf (T*k, H/16),
+    gs (1,)); row inv_perm[t*k+j] holds token t (routed pairs only)."""
+    _dev(x, torch.bfloat16, "x")
+    T, H = x.shape
+    E = offsets.shape[0] - 1
+    _dev(inv_perm, torch.int32, "inv_perm", (T * k,))
+    _dev(offsets, torch.int32, "offsets")
+    dev = x.device
+    if out is not None:
+        q, sf, gs = out
+    else:
+        q = torch.empty((T * k, H // 2), dtype=torch.uint8, device=dev)
+        sf = torch.empty((T * k, H // 16), dtype=torch.uint8, device=dev)
+        gs = torch.empty((1,), dtype=torch.float32, device=dev)
+    L = lib()
+    ws = _workspace(L.nvfp4_quantize_scatter_workspace_size(T, H), dev)
+    _check(L.nvfp4_quantize_scatter(_ptr(x), T, H, k, _ptr(inv_perm), _ptr(offsets), E, _ptr(q),
+                                    _ptr(sf), _ptr(gs), _ptr(ws), ws.numel(), _stream(dev)),
+           "nvfp4_quantize_scatter")
+    return q, sf, gs
 
 
 def to_mx(q, sf, out=None):

@@ -244,6 +244,36 @@ size_t nvfp4_moe_route_workspace_size(int64_t T, int k, int E) {
   return nvfp4::route_ws_bytes(T, k, E);
 }
 
+size_t nvfp4_quantize_scatter_workspace_size(int64_t T, int64_t H) {
+  if (T <= 0 || H < 16 || H % 16) return 0;
+  return sizeof(float) * (size_t)nvfp4::quantize_parts(1, T, H);
+}
+
+nvfp4_status nvfp4_quantize_scatter(const void* x_bf16, int64_t T, int64_t H, int k,
+                                    const int32_t* inv_perm, const int32_t* expert_offsets, int E,
+                                    uint8_t* q, uint8_t* sf, float* gs_out, void* ws,
+                                    size_t ws_bytes, void* stream) {
+  if (T < 0) return fail(NVFP4_ERR_SHAPE, "T must be >= 0");
+  if (H < 16 || H % 16) return fail(NVFP4_ERR_SHAPE, "H must be a positive multiple of 16 (got %lld)", (long long)H);
+  if (k < 1 || k > 64) return fail(NVFP4_ERR_SHAPE, "k must be in [1, 64] (got %d)", k);
+  if (E < 1 || E > 4096) return fail(NVFP4_ERR_SHAPE, "E must be in [1, 4096] (got %d)", E);
+  if (T * k >= (int64_t(1) << 31)) return fail(NVFP4_ERR_SHAPE, "T*k must be < 2^31");
+  if (!gs_out) return fail(NVFP4_ERR_INVALID_ARG, "gs_out is NULL");
+  if (T > 0 && (!x_bf16 || !inv_perm || !expert_offsets || !q || !sf))
+    return fail(NVFP4_ERR_INVALID_ARG, "x, inv_perm, expert_offsets, q and sf must be non-NULL");
+  if (T > 0 && (!aligned(x_bf16, 16) || !aligned(q, 8)))
+    return fail(NVFP4_ERR_INVALID_ARG, "x must be 16-byte and q 8-byte aligned");
+  const size_t need = nvfp4_quantize_scatter_workspace_size(T, H);
+  if (T > 0 && (ws == nullptr || ws_bytes < need || !aligned(ws, 4)))
+    return fail(NVFP4_ERR_WORKSPACE, "quantize_scatter needs %zu 4-byte aligned workspace bytes (got %zu)", need, ws_bytes);
+  nvfp4_status st = check_arch();
+  if (st != NVFP4_OK) return st;
+  return finish(nvfp4::launch_quantize_scatter(x_bf16, T, H, k, inv_perm, expert_offsets, E, q, sf,
+                                               gs_out, static_cast<float*>(ws),
+                                               static_cast<hipStream_t>(stream)),
+                "nvfp4_quantize_scatter launch");
+}
+
 nvfp4_status nvfp4_moe_route(const int32_t* topk_ids, int64_t T, int k, int E,
                              int32_t* expert_offsets, int32_t* perm, int32_t* inv_perm,
                              int32_t* invalid_count, void* ws, size_t ws_bytes, void* stream) {

@@ -21,6 +21,13 @@ hipError_t launch_quantize(const void* x, int64_t groups, int64_t rows_per_group
                            const float* gs_in, uint8_t* q, uint8_t* sf, float* gs_out, float* ws,
                            hipStream_t stream);
 
+// x (T, H) -> NVFP4 with a per-call global scale, each token row written to
+// its k expert-order rows (inv_perm), rows >= offsets[E] skipped
+hipError_t launch_quantize_scatter(const void* x, int64_t T, int64_t H, int k,
+                                   const int32_t* inv_perm, const int32_t* offsets, int E,
+                                   uint8_t* q, uint8_t* sf, float* gs_out, float* ws,
+                                   hipStream_t stream);
+
 // route.hip
 int64_t route_chunks(int64_t T, int k);
 size_t route_ws_bytes(int64_t T, int k, int E);

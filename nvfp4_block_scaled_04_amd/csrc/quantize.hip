@@ -89,7 +89,55 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
   sf[b] = (uint8_t)s;
 }
 
+// Quantise-and-scatter: one thread per 16-element block of a token row; the
+// block is quantised once (same rule as quantize_kernel) and written to the
+// k expert-order rows of that token (rows past offsets[E] skipped).
+__global__ __launch_bounds__(kThreads) void quantize_scatter_kernel(
+    const uint4* __restrict__ x, int64_t T, int64_t blocks_per_row, int k,
+    const int32_t* __restrict__ inv_perm, const int32_t* __restrict__ offsets, int E,
+    const float* __restrict__ gs, uint2* __restrict__ q, uint8_t* __restrict__ sf) {
+  const int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (b >= T * blocks_per_row) return;
+  const int64_t t = b / blocks_per_row, blk = b - t * blocks_per_row;
+  const uint4 v0 = x[2 * b], v1 = x[2 * b + 1];
+  const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+  float xs[16];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    xs[2 * j] = bf16_to_f32(w[j] & 0xFFFFu);
+    xs[2 * j + 1] = bf16_to_f32(w[j] >> 16);
+  }
+  uint32_t lo, hi, s;
+  quantize_block16(xs, gs[0], lo, hi, s);
+  const int32_t n_valid = offsets[E];
+  for (int j = 0; j < k; ++j) {
+    const int32_t d = inv_perm[t * k + j];
+    if (d >= n_valid) continue;
+    q[(int64_t)d * blocks_per_row + blk] = make_uint2(lo, hi);
+    sf[(int64_t)d * blocks_per_row + blk] = (uint8_t)s;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_quantize_scatter(const void* x, int64_t T, int64_t H, int k,
+                                   const int32_t* inv_perm, const int32_t* offsets, int E,
+                                   uint8_t* q, uint8_t* sf, float* gs_out, float* ws,
+                                   hipStream_t stream) {
+  if (T == 0) {
+    fill_f32(gs_out, 1.0f, 1, stream);
+    return hipGetLastError();
+  }
+  const int parts = quantize_parts(1, T, H);
+  amax_partial_kernel<<<dim3(parts, 1), kThreads, 0, stream>>>(static_cast<const uint4*>(x),
+                                                                T * H / 8, parts, ws);
+  gs_finalize_kernel<<<1, kThreads, 0, stream>>>(ws, parts, gs_out);
+  const int64_t nblocks = T * (H / 16);
+  quantize_scatter_kernel<<<(unsigned)((nblocks + kThreads - 1) / kThreads), kThreads, 0, stream>>>(
+      static_cast<const uint4*>(x), T, H / 16, k, inv_perm, offsets, E, gs_out,
+      reinterpret_cast<uint2*>(q), sf);
+  return hipGetLastError();
+}
 
 int quantize_parts(int64_t groups, int64_t rows_per_group, int64_t cols) {
   // chunks per group for the amax pass: enough blocks to fill the chip,

@@ -189,3 +189,17 @@ def test_shared_forward_rejects(L):
     assert f(ws=FAKE + 16) == -3
     need = L.moe_expert_forward_shared_workspace_size(64, 256, 128, 4, 2)
     assert need > L.moe_expert_forward_workspace_size(64, 256, 128, 5, 3)
+
+
+def test_quantize_scatter_rejects(L):
+    f = lambda **kw: L.nvfp4_quantize_scatter(FAKE, kw.get("T", 4), kw.get("H", 256), kw.get("k", 2),
+                                              FAKE, FAKE, kw.get("E", 8), FAKE, FAKE,
+                                              kw.get("gs", FAKE), kw.get("ws", FAKE),
+                                              kw.get("wsb", 1 << 20), None)
+    assert f(H=24) == -2
+    assert f(k=0) == -2
+    assert f(E=0) == -2
+    assert f(gs=None) == -1
+    assert f(wsb=0) == -3
+    assert L.nvfp4_quantize_scatter_workspace_size(0, 256) == 0
+    assert L.nvfp4_quantize_scatter_workspace_size(8192, 7168) >= 4

@@ -231,3 +231,64 @@ def test_combine_rounding_exact_ties():
     r16 = (exact.astype(np.float32).view(np.uint32) & 0xFFFF)
     assert (r16 == 0x8000).sum() > 100                # many exact ties exercised
     assert np.array_equal(host(out).view(np.uint16), ref)
+
+
+@pytest.mark.parametrize("T,H,E,k,invalid", [(37, 256, 8, 3, True), (2048, 7168, 256, 8, False),
+                                             (0, 256, 4, 2, False), (5, 128, 1, 1, False)])
+def test_quantize_scatter_bit_exact(T, H, E, k, invalid):
+    """Quantise-and-scatter: every routed row d holds the oracle's NVFP4 of
+    token perm[d] // k; rows of invalid ids are left untouched."""
+    from oracle import quantize as Q, route as R
+    print(f"[case] quantize_scatter T={T} H={H} E={E} k={k} invalid={invalid}", flush=True)
+    rng = np.random.default_rng(T + H)
+    ids = np.array([rng.permutation(E)[:k] for _ in range(T)], dtype=np.int32).reshape(T, k)
+    if invalid and T > 4:
+        ids[1, 0] = E + 3
+        ids[4, k - 1] = -1
+    g = torch.Generator(device=DEV).manual_seed(T * 7 + 1)
+    x = torch.randn((T, H), generator=g, device=DEV).to(torch.bfloat16)
+    off, perm, inv, bad = nv.moe_route(torch.from_numpy(ids).to(DEV), E)
+    q = torch.full((T * k, H // 2), 0xAB, dtype=torch.uint8, device=DEV)
+    sf = torch.full((T * k, H // 16), 0xAB, dtype=torch.uint8, device=DEV)
+    gs = torch.zeros((1,), dtype=torch.float32, device=DEV)
+    nv.quantize_scatter(x, inv, off, k, out=(q, sf, gs))
+    torch.cuda.synchronize()
+    roff, rperm, _, n_bad = R.route(ids, E)
+    xb = host(x)
+    rq, rsf, rgs = Q.quantize_nvfp4(xb) if T else (np.zeros((0, H // 2), np.uint8), None, [np.float32(1)])
+    assert host(gs)[0] == rgs[0]
+    n_valid = int(roff[E])
+    gq, gsf = host(q), host(sf)
+    if n_valid:
+        src = rperm[:n_valid] // k
+        assert np.array_equal(gq[:n_valid], rq[src])
+        assert np.array_equal(gsf[:n_valid], rsf[src])
+    assert np.all(gq[n_valid:] == 0xAB) and np.all(gsf[n_valid:] == 0xAB)
+    assert n_bad == (2 if invalid and T > 4 else 0)
+
+
+def test_l1_on_scattered_rows_equals_the_gather():
+    """L1 on the quantise-and-scatter rows (no gather) gives the same bytes as
+    L1 gathering the compact rows through perm."""
+    from nvfp4_block_scaled_04_amd import inputs as I
+    w = I.custom("scatter_l1", T=300, H=512, I=256, E=16, k=4, seed=13)
+    print("[case] L1 scattered vs gathered", flush=True)
+    pairs = [I.make_expert_weights(w, e, DEV) for e in range(w.E)]
+    ew = nv.prepare_expert_weights([torch.stack([p[0] for p in pairs])],
+                                   [torch.stack([p[1] for p in pairs])], DEV)
+    x = I.make_x(w, DEV)
+    ids, _ = I.make_routing(w)
+    off, perm, inv, _ = nv.moe_route(torch.from_numpy(ids).to(DEV), w.E)
+    M = w.T * w.k
+    gs_h = torch.tensor([w.gs_h], dtype=torch.float32, device=DEV)
+    a_q, a_sf, gs_a = nv.quantize(x)
+    g_q, g_sf, _ = nv.grouped_gemm(nv.EPI_SWIGLU_NVFP4, a_q, a_sf, gs_a, off, ew.w1, ew.gs_w1, M,
+                                   a_row_src=perm, a_row_div=w.k, gs_out=gs_h)
+    s_q, s_sf, s_gs = nv.quantize_scatter(x, inv, off, w.k)
+    h_q, h_sf, _ = nv.grouped_gemm(nv.EPI_SWIGLU_NVFP4, s_q, s_sf, s_gs, off, ew.w1, ew.gs_w1, M,
+                                   gs_out=gs_h)
+    torch.cuda.synchronize()
+    n = int(host(off)[-1])
+    assert host(s_gs)[0] == host(gs_a)[0]
+    assert np.array_equal(host(h_q)[:n], host(g_q)[:n])
+    assert np.array_equal(host(h_sf)[:n], host(g_sf)[:n])
