@@ -161,19 +161,28 @@ struct Cfg {
   static constexpr int ROWS = BN + BM;                 // LDS rows per stage: weights, tokens
   static constexpr int CODE_BYTES = ROWS * ROW_BYTES;
   static constexpr int STAGE_BYTES = CODE_BYTES + ROWS * SF_BYTES;
-  static constexpr int NBUF = 3;                       // LDS stage buffers
+  // 32-token tiles (experts of a few rows): smaller stages, so four buffers
+  // fit and loads run three stages ahead instead of two.  Every wave still
+  // issues 12 loads per stage: its token code loads move 4 bytes per lane
+  // (two loads fill a wave's 8 of the 32 rows), and its one token scale load
+  // brings all 32 rows' scales (every wave writes the same 256 bytes)
+  static constexpr bool SMALL = BM == 32;
+  static constexpr int MAX_E = SMALL ? 1024 : 4096;    // expert prefix kept in LDS
+  static constexpr int NBUF = SMALL ? 4 : 3;           // LDS stage buffers
+  static constexpr int AHEAD = NBUF - 1;               // stages loaded ahead of use
   static constexpr int LDS_BYTES = NBUF * STAGE_BYTES;
   // direct-to-LDS loads per wave and stage: a code load fills 16 rows; a
   // weight scale load (16 bytes per lane) 128 rows, a token scale load 32 rows
-  static constexpr int CODE_LOADS = ROWS / 16 / NW;
-  static constexpr int CODE_LOADS_W = BN / 16 / NW;    // ... of which weight rows
+  static constexpr int CODE_LOADS_W = BN / 16 / NW;    // weight-row code loads
+  static constexpr int CODE_LOADS = SMALL ? CODE_LOADS_W + 2 : ROWS / 16 / NW;
   static constexpr int SF_LOADS_W = BN / 128 / NW;
-  static constexpr int SF_LOADS_T = BM / 32 / NW;
+  static constexpr int SF_LOADS_T = SMALL ? 1 : BM / 32 / NW;
   static constexpr int SF_LOADS = SF_LOADS_W + SF_LOADS_T;
   static constexpr int LOADS = CODE_LOADS + SF_LOADS;
   static_assert(TN % 32 == 0 && TM % 32 == 0, "wave tile must be a multiple of 32");
-  static_assert(ROWS % (16 * NW) == 0 && BN % (16 * NW) == 0, "code loads must divide evenly");
-  static_assert(BN % (128 * NW) == 0 && BM % (32 * NW) == 0, "scale loads must divide evenly");
+  static_assert(BN % (16 * NW) == 0 && (SMALL ? NW == 4 : ROWS % (16 * NW) == 0),
+                "code loads must divide evenly");
+  static_assert(BN % (128 * NW) == 0 && (SMALL || BM % (32 * NW) == 0), "scale loads must divide evenly");
   static_assert(BN == NVFP4_PACK_ROWS && BK == NVFP4_PACK_K, "tiles follow the packed weight layout");
   static_assert(WM == 1, "column-block skipping assumes one wave row");
 };
@@ -215,7 +224,8 @@ __device__ __forceinline__ void stage_barrier() {
 // of the dependent tile configuration.
 #define NVFP4_LOAD_CONSTS                                                                       \
   constexpr int kNW = C::NW, kCodeLoads = C::CODE_LOADS, kCodeLoadsW = C::CODE_LOADS_W;         \
-  constexpr int kSfLoads = C::SF_LOADS, kSfLoadsW = C::SF_LOADS_W, kCodeBytes = C::CODE_BYTES
+  constexpr int kSfLoads = C::SF_LOADS, kSfLoadsW = C::SF_LOADS_W, kCodeBytes = C::CODE_BYTES;  \
+  constexpr bool kSmall = C::SMALL
 #define NVFP4_ISSUE(ks, dst, part)                                                              \
   do {                                                                                          \
     uint8_t* sbw = (dst);                                                                       \
@@ -224,6 +234,10 @@ __device__ __forceinline__ void stage_barrier() {
         if (c < kCodeLoadsW)                                                                    \
           __builtin_amdgcn_global_load_lds(wq + coff[c] + (uint32_t)(ks) * (BN * ROW_BYTES),    \
                                            sbw + (c * kNW + wave) * 1024, 16, 0, 0);            \
+        else if (kSmall)                                                                        \
+          __builtin_amdgcn_global_load_lds(aq + coff[c] + (uint32_t)(ks) * ROW_BYTES,           \
+                                           sbw + BN * ROW_BYTES +                               \
+                                               ((c - kCodeLoadsW) * kNW + wave) * 256, 4, 0, 0); \
         else                                                                                    \
           __builtin_amdgcn_global_load_lds(aq + coff[c] + (uint32_t)(ks) * ROW_BYTES,           \
                                            sbw + (c * kNW + wave) * 1024, 16, 0, 0);            \
@@ -234,6 +248,9 @@ __device__ __forceinline__ void stage_barrier() {
         if (c < kSfLoadsW)                                                                      \
           __builtin_amdgcn_global_load_lds(wsf + soff[c] + (uint32_t)(ks) * (BN * SF_BYTES),    \
                                            sbw + kCodeBytes + (c * kNW + wave) * 1024, 16, 0, 0); \
+        else if (kSmall)                                                                        \
+          __builtin_amdgcn_global_load_lds(asf + soff[c] + (uint32_t)(ks) * SF_BYTES,           \
+                                           sbw + kCodeBytes + BN * SF_BYTES, 4, 0, 0);          \
         else                                                                                    \
           __builtin_amdgcn_global_load_lds(asf + soff[c] + (uint32_t)(ks) * SF_BYTES,           \
                                            sbw + kCodeBytes + BN * SF_BYTES +                   \
@@ -296,7 +313,7 @@ __device__ __forceinline__ void stage_barrier() {
     }                                                                                           \
   } while (0)
 
-// Direct loads of a tile's stages 0 and 1 into buffers b0 and b1.  The
+// Direct loads of a tile's first AHEAD stages into buffers b0, b1 (, b2).  The
 // pointer parameters are __restrict__ here and in k_stage: LDS reads of one
 // buffer are then known not to alias direct loads into another, so the
 // compiler adds no wait on loads in flight; every wait those reads need is
@@ -308,23 +325,26 @@ __device__ __forceinline__ void k_issue_first(int nks, int wave, const uint32_t*
                                               const uint8_t* __restrict__ wsf,
                                               const uint8_t* __restrict__ aq,
                                               const uint8_t* __restrict__ asf,
-                                              uint8_t* __restrict__ b0, uint8_t* __restrict__ b1) {
+                                              uint8_t* __restrict__ b0, uint8_t* __restrict__ b1,
+                                              uint8_t* __restrict__ b2) {
   using C = Cfg<BN, BM, WN, WM>;
   NVFP4_LOAD_CONSTS;
   NVFP4_ISSUE(0, b0, -1);
   if (nks > 1) NVFP4_ISSUE(1, b1, -1);
+  if (C::AHEAD > 2 && nks > 2) NVFP4_ISSUE(2, b2, -1);
 }
 
-// Waits for stage 0 (in b0; stages 0 and 1 are the last loads issued, later
-// vector memory operations are stores), synchronises the block and decodes
-// step 0.
+// Waits for stage 0 (in b0; the tile's first stages are the last loads
+// issued, later vector memory operations are stores), synchronises the
+// block and decodes step 0.
 template <int BN, int BM, int WN, int WM, int JV>
 __device__ __forceinline__ void k_begin(KState<BN, BM, WN, WM, JV>& st, int nks,
                                         const uint8_t* __restrict__ b0) {
   using C = Cfg<BN, BM, WN, WM>;
   constexpr int FN = C::FN, TN = C::TN, TM = C::TM;
   static_assert(C::LOADS == 12 && kLoadsBeforeBarrier == 8, "vmcnt immediates assume 12 loads per stage");
-  if (nks > 1) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+  if (C::AHEAD > 2 && nks > 2) asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
+  else if (nks > 1) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
   else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   stage_barrier();
   NVFP4_READ_HALF(b0, 0, st.fa, st.ta);
@@ -337,8 +357,12 @@ __device__ __forceinline__ void k_begin(KState<BN, BM, WN, WM, JV>& st, int nks,
 }
 
 // One stage ks, held in br; stage ks+1 is in bm; with LOADS (a literal 1 or
-// 0: whether stage ks+2 exists) its loads go into bw.  LOADS stages have no
-// branches, so the loads and the MFMAs share one scheduling region.
+// 0: whether stage ks+AHEAD exists) its loads go into bw; PEND: whether the
+// loads of stage ks+2 are in flight (with AHEAD 2 those issued here).  LOADS
+// stages have no branches, so the loads and the MFMAs share one scheduling
+// region.  With AHEAD 3 (four buffers) read "ks+3" for "ks+2" below where
+// the loads issued by this stage are meant; stage ks+2 then stays in flight
+// across the mid-stage wait.
 //   steps 0-3: half A fragments (in registers); half B fragments of stage ks
 //     are read from LDS;
 //   after step 3: wait until stage ks+1 has landed (the loads of ks+2 issued
@@ -350,7 +374,7 @@ __device__ __forceinline__ void k_begin(KState<BN, BM, WN, WM, JV>& st, int nks,
 // while it decodes the next step's operands, so decode and MFMA overlap;
 // step 7 decodes step 0 of the next stage.  bw held stage ks-1, last read
 // before the mid-stage barrier of ks-1.
-template <int BN, int BM, int WN, int WM, int JV, int LOADS>
+template <int BN, int BM, int WN, int WM, int JV, int LOADS, int PEND = LOADS>
 __device__ __forceinline__ void k_stage(KState<BN, BM, WN, WM, JV>& st, int ks, int nks, int wave,
                                         const uint32_t* coff, const uint32_t* soff,
                                         const uint8_t* __restrict__ wq,
@@ -366,19 +390,25 @@ __device__ __forceinline__ void k_stage(KState<BN, BM, WN, WM, JV>& st, int ks, 
   // VALU of one step's decode per MFMA of a step
   constexpr int VPM = ((FN + JV) * 8 + FN * JV - 1) / (FN * JV);
   constexpr int NL = LOADS ? 2 : 0;
+  constexpr int AH = C::AHEAD;
+  static_assert(AH == 2 || AH == 3, "two or three stages ahead");
+  static_assert(AH == 3 || PEND == LOADS, "with two stages ahead the pending loads are this stage's");
   NVFP4_READ_HALF(br, 1, st.fb, st.tb);
-  const bool more1 = LOADS || ks + 1 < nks;
+  const bool more1 = LOADS || PEND || ks + 1 < nks;
   // operands of even steps live in av0/bv0, of odd steps in av1/bv1
-  if (LOADS) NVFP4_ISSUE(ks + 2, bw, 0);
+  if (LOADS) NVFP4_ISSUE(ks + AH, bw, 0);
   NVFP4_DECODE(1, st.fa, st.ta, st.wsc, st.tsc, st.av1, st.bv1); NVFP4_MFMAS(st.av0, st.bv0); NVFP4_INTERLEAVE(NL);
-  if (LOADS) NVFP4_ISSUE(ks + 2, bw, 1);
+  if (LOADS) NVFP4_ISSUE(ks + AH, bw, 1);
   NVFP4_DECODE(2, st.fa, st.ta, st.wsc, st.tsc, st.av0, st.bv0); NVFP4_MFMAS(st.av1, st.bv1); NVFP4_INTERLEAVE(NL);
-  if (LOADS) NVFP4_ISSUE(ks + 2, bw, 2);
+  if (LOADS) NVFP4_ISSUE(ks + AH, bw, 2);
   NVFP4_DECODE(3, st.fa, st.ta, st.wsc, st.tsc, st.av1, st.bv1); NVFP4_MFMAS(st.av0, st.bv0); NVFP4_INTERLEAVE(NL);
-  if (LOADS) NVFP4_ISSUE(ks + 2, bw, 3);
+  if (LOADS) NVFP4_ISSUE(ks + AH, bw, 3);
   NVFP4_DECODE(4, st.fb, st.tb, st.wsc, st.tsc, st.av0, st.bv0); NVFP4_MFMAS(st.av1, st.bv1); NVFP4_INTERLEAVE(NL);
-  // stage ks+1 must have landed; the loads of ks+2 issued so far may not have
-  if (LOADS) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");   // kLoadsBeforeBarrier
+  // stage ks+1 must have landed; the loads of ks+AH issued so far, and with
+  // AH 3 those of stage ks+2, may not have
+  if (AH == 2 && LOADS) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");   // kLoadsBeforeBarrier
+  else if (AH == 3 && LOADS) asm volatile("s_waitcnt vmcnt(20)" ::: "memory");  // 12 + 8
+  else if (AH == 3 && PEND) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
   else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   stage_barrier();
   if (more1) {
@@ -388,9 +418,9 @@ __device__ __forceinline__ void k_stage(KState<BN, BM, WN, WM, JV>& st, int ks, 
   // the reads go out here; their consumers stay in the last step (below),
   // so their latency hides behind steps 4-6 instead of stalling issue
   __builtin_amdgcn_sched_barrier(0);
-  if (LOADS) NVFP4_ISSUE(ks + 2, bw, 4);
+  if (LOADS) NVFP4_ISSUE(ks + AH, bw, 4);
   NVFP4_DECODE(5, st.fb, st.tb, st.wsc, st.tsc, st.av1, st.bv1); NVFP4_MFMAS(st.av0, st.bv0); NVFP4_INTERLEAVE(NL);
-  if (LOADS) NVFP4_ISSUE(ks + 2, bw, 5);
+  if (LOADS) NVFP4_ISSUE(ks + AH, bw, 5);
   NVFP4_DECODE(6, st.fb, st.tb, st.wsc, st.tsc, st.av0, st.bv0); NVFP4_MFMAS(st.av1, st.bv1); NVFP4_INTERLEAVE(NL);
   NVFP4_DECODE(7, st.fb, st.tb, st.wsc, st.tsc, st.av1, st.bv1); NVFP4_MFMAS(st.av0, st.bv0); NVFP4_INTERLEAVE(0);
   __builtin_amdgcn_sched_barrier(0);
@@ -615,8 +645,21 @@ __device__ __forceinline__ void tile_offsets(const Params& p, const Tile& t, int
     const int g = c * C::NW + wave;                // 16-row group
     const int r = 16 * g + (lane >> 2);
     const int q = chunk_pos(r, lane & 3);          // logical chunk stored at this lane's position
-    coff[c] = (c < C::CODE_LOADS_W) ? (uint32_t)(wrow(r) * ROW_BYTES + 16 * q)
-                                    : trow(r - BN) * kb + 16 * q;
+    if constexpr (C::SMALL) {
+      if (c < C::CODE_LOADS_W) {
+        coff[c] = (uint32_t)(wrow(r) * ROW_BYTES + 16 * q);
+      } else {
+        // 4 bytes per lane: token row i = 4 g' + lane / 16 (g' = the wave's
+        // token load number), byte 4 (lane % 16) of its LDS row, i.e. byte
+        // 4 (lane % 4) of the chunk at position (lane % 16) / 4
+        const int i = 4 * ((c - C::CODE_LOADS_W) * C::NW + wave) + (lane >> 4);
+        const int qs = chunk_pos(BN + i, (lane >> 2) & 3);
+        coff[c] = trow(i) * kb + 16 * qs + 4 * (lane & 3);
+      }
+    } else {
+      coff[c] = (c < C::CODE_LOADS_W) ? (uint32_t)(wrow(r) * ROW_BYTES + 16 * q)
+                                      : trow(r - BN) * kb + 16 * q;
+    }
   }
 #pragma unroll
   for (int c = 0; c < C::SF_LOADS_W; ++c) {      // 2 consecutive rows per lane
@@ -625,7 +668,7 @@ __device__ __forceinline__ void tile_offsets(const Params& p, const Tile& t, int
   }
 #pragma unroll
   for (int c = 0; c < C::SF_LOADS_T; ++c) {      // one 4-byte half row per lane
-    const int i = 32 * (c * C::NW + wave) + (lane >> 1);
+    const int i = C::SMALL ? (lane >> 1) : 32 * (c * C::NW + wave) + (lane >> 1);
     soff[C::SF_LOADS_W + c] = trow(i) * ksf + 4 * (lane & 1);
   }
 }
@@ -662,7 +705,7 @@ __device__ __forceinline__ bool run_tile(const Params& p, uint8_t* smem, const i
 #pragma unroll
       for (int r = 0; r < 16; ++r) st.acc[i][j][r] = 0.0f;
 
-  // three LDS stage buffers, stage ks in buffer ks % 3
+  // three LDS stage buffers, stage ks in buffer ks % 3 (four with AHEAD 3)
   const int nks = cur.nks;
   if constexpr (FMT == kFmtMx) {
     k_begin_mx(st, nks, smem);
@@ -682,6 +725,25 @@ __device__ __forceinline__ bool run_tile(const Params& p, uint8_t* smem, const i
                                         smem + buf1 * C::STAGE_BYTES, smem + buf2 * C::STAGE_BYTES);
       buf = buf1;
     }
+  } else if constexpr (C::AHEAD == 3) {
+    // four LDS stage buffers, stage ks in buffer ks % 4
+    constexpr int SB = C::STAGE_BYTES;
+    k_begin(st, nks, smem);
+    int ks = 0;
+    for (; ks + 3 < nks; ++ks)
+      k_stage<BN, BM, WN, WM, JV, 1, 1>(st, ks, nks, wave, coff, soff, wbase, wsbase, abase, asbase,
+                                        smem + (ks & 3) * SB, smem + ((ks + 1) & 3) * SB,
+                                        smem + ((ks + 3) & 3) * SB);
+    if (ks + 2 < nks) {
+      k_stage<BN, BM, WN, WM, JV, 0, 1>(st, ks, nks, wave, coff, soff, wbase, wsbase, abase, asbase,
+                                        smem + (ks & 3) * SB, smem + ((ks + 1) & 3) * SB,
+                                        smem + ((ks + 3) & 3) * SB);
+      ++ks;
+    }
+    for (; ks < nks; ++ks)
+      k_stage<BN, BM, WN, WM, JV, 0, 0>(st, ks, nks, wave, coff, soff, wbase, wsbase, abase, asbase,
+                                        smem + (ks & 3) * SB, smem + ((ks + 1) & 3) * SB,
+                                        smem + ((ks + 3) & 3) * SB);
   } else {
     k_begin(st, nks, smem);
     int buf = 0;
@@ -719,7 +781,8 @@ __device__ __forceinline__ bool run_tile(const Params& p, uint8_t* smem, const i
     if (tid == 0) claim = atomicAdd(sc.counters + sc.cx, 1);
     tile_offsets<BN, BM, WN, WM, EPI>(p, nxt, wave, lane, coff, soff);
     k_issue_first<BN, BM, WN, WM>(nxt.nks, wave, coff, soff, tile_wq<BN>(p, nxt), tile_wsf<BN>(p, nxt),
-                                  tile_aq(p, nxt), tile_asf(p, nxt), smem, smem + C::STAGE_BYTES);
+                                  tile_aq(p, nxt), tile_asf(p, nxt), smem, smem + C::STAGE_BYTES,
+                                  smem + 2 * C::STAGE_BYTES);
   }
 
   // ---- epilogue
@@ -830,6 +893,7 @@ __device__ __forceinline__ bool run_tile(const Params& p, uint8_t* smem, const i
 template <int BN, int BM, int WN, int WM, int EPI, int FMT>
 __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_gemm_kernel(Params p) {
   using C = Cfg<BN, BM, WN, WM>;
+  static_assert(!C::SMALL || FMT == kFmtNvfp4, "the MX stage assumes two stages ahead");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   int* tprefix = reinterpret_cast<int*>(smem + C::LDS_BYTES);   // [E + 1]
   __shared__ int s_scan[C::NT];
@@ -877,7 +941,8 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_gemm_kernel(Params p)
     tile_at<BN, BM>(p, tprefix, t0, cur);
     tile_offsets<BN, BM, WN, WM, EPI>(p, cur, wave, lane, coff, soff);
     k_issue_first<BN, BM, WN, WM>(cur.nks, wave, coff, soff, tile_wq<BN>(p, cur), tile_wsf<BN>(p, cur),
-                                  tile_aq(p, cur), tile_asf(p, cur), smem, smem + C::STAGE_BYTES);
+                                  tile_aq(p, cur), tile_asf(p, cur), smem, smem + C::STAGE_BYTES,
+                                  smem + 2 * C::STAGE_BYTES);
   }
   while (have) {
     Tile nxt;
@@ -953,12 +1018,13 @@ hipError_t device_cus(int& cus) {
   return hipSuccess;
 }
 
-constexpr int kBN = 512, kBM = 128;   // the tile every launch uses
+constexpr int kBN = 512, kBM = 128;   // the tile of every launch but small experts
+constexpr int kBMSmall = 32;          // experts of at most 32 rows on average
 
 // upper bound on the tile count: sum over experts of ceil(rows_e / BM)
 // <= (M + E * (BM - 1)) / BM m tiles, times the n tiles
-int64_t tile_bound(int64_t M, int64_t N, int E) {
-  return (M + (int64_t)E * (kBM - 1)) / kBM * ((N + kBN - 1) / kBN);
+int64_t tile_bound(int64_t M, int64_t N, int E, int bm = kBM) {
+  return (M + (int64_t)E * (bm - 1)) / bm * ((N + kBN - 1) / kBN);
 }
 
 // K ranges per tile: 1, unless a BF16-epilogue launch has at most half as
@@ -1003,7 +1069,8 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
     p.ksplit = splitk_factor(a.epilogue, a.M, a.N, a.K, a.E, cus);
     p.partial = splitk_partial(a.ws);
   }
-  const int64_t tiles = tile_bound(a.M, a.N, a.E) * p.ksplit;
+  if (a.E > C::MAX_E) return hipErrorInvalidValue;
+  const int64_t tiles = tile_bound(a.M, a.N, a.E, BM) * p.ksplit;
   int64_t grid = cus;                                     // one block per CU (LDS-limited)
   if (grid > tiles) grid = tiles;
   grid = (grid + 7) / 8 * 8;
@@ -1013,7 +1080,7 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
   if (!attr_set[dev].load(std::memory_order_relaxed)) {
     err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                               hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (int)(C::LDS_BYTES + sizeof(int) * 4097));
+                              (int)(C::LDS_BYTES + sizeof(int) * (C::MAX_E + 1)));
     if (err != hipSuccess) return err;
     attr_set[dev].store(true, std::memory_order_relaxed);
   }
@@ -1039,16 +1106,26 @@ size_t gemm_splitk_ws_bytes(int epilogue, int64_t M, int64_t N, int64_t K, int E
   return kGemmWorkspaceBytes + 255 + (size_t)f * (size_t)M * (size_t)N * sizeof(float);
 }
 
+// 32-token tiles for NVFP4 launches whose experts hold at most 32 rows on
+// average (decode-sized batches)
+bool small_experts(int fmt, int64_t M, int E) {
+  return fmt == kFmtNvfp4 && E <= Cfg<kBN, kBMSmall, 4, 1>::MAX_E && M <= (int64_t)kBMSmall * E;
+}
+
 template <int FMT>
 hipError_t launch_fmt(const GemmArgs& a, hipStream_t stream) {
+  constexpr int FS = FMT == kFmtNvfp4 ? kBMSmall : kBM;   // MX keeps the large tile
+  const bool small = small_experts(FMT, a.M, a.E);
   if (a.epilogue == NVFP4_EPI_SWIGLU_NVFP4)
-    return launch_cfg<kBN, kBM, 4, 1, NVFP4_EPI_SWIGLU_NVFP4, FMT>(a, stream);
+    return small ? launch_cfg<kBN, FS, 4, 1, NVFP4_EPI_SWIGLU_NVFP4, FMT>(a, stream)
+                 : launch_cfg<kBN, kBM, 4, 1, NVFP4_EPI_SWIGLU_NVFP4, FMT>(a, stream);
   // split K only when the caller's workspace holds the partials
   if (a.M > 0 && a.ws_bytes > kGemmWorkspaceBytes &&
       gemm_splitk_ws_bytes(a.epilogue, a.M, a.N, a.K, a.E) > kGemmWorkspaceBytes &&
       a.ws_bytes >= gemm_splitk_ws_bytes(a.epilogue, a.M, a.N, a.K, a.E))
     return launch_cfg<kBN, kBM, 4, 1, kEpiPartial, FMT>(a, stream);
-  return launch_cfg<kBN, kBM, 4, 1, NVFP4_EPI_BF16, FMT>(a, stream);
+  return small ? launch_cfg<kBN, FS, 4, 1, NVFP4_EPI_BF16, FMT>(a, stream)
+               : launch_cfg<kBN, kBM, 4, 1, NVFP4_EPI_BF16, FMT>(a, stream);
 }
 
 hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t stream) {
