@@ -157,3 +157,36 @@ def test_dense_linear_config2_sampled_rows(split):
     assert host(gs_a)[0] == gsa and host(gs_b)[0] == gsb[0]
     ref = bf16_values(O.dense_linear(Q.pack_codes(aq), asf, gsa, bq, bsf, gsb[0]))
     assert_close(bf16_values(host(c))[rows], ref, "dense linear (sampled rows)")
+
+
+# 315 rows over 16 experts (<= 32 per expert on average: the 32-token tile
+# configuration); experts of 0, 1, 31-33 and up to 70 rows
+SMALL_COUNTS = [0, 1, 31, 32, 33, 70, 5, 0, 2, 9, 17, 64, 3, 0, 8, 40]
+
+
+@pytest.mark.parametrize("K", [128, 256, 384, 512, 640, 1152])
+@pytest.mark.parametrize("epi", ["bf16", "swiglu"])
+def test_small_expert_tiles(epi, K):
+    """Launches whose experts average at most 32 rows run 32-token tiles
+    with loads three stages ahead: K of 1 to 9 stages covers every way the
+    last stages are peeled; experts above 32 rows span several tiles."""
+    if epi == "bf16":
+        res, (aq, asf, ga, bq, bsf, gb, off, rows) = _grouped_case(SMALL_COUNTS, 96, K, 31,
+                                                                   nv.EPI_BF16)
+        got = bf16_values(host(res))
+    else:
+        res, (aq, asf, ga, bq, bsf, gb, off, rows) = _grouped_case(SMALL_COUNTS, 128, K, 33,
+                                                                   nv.EPI_SWIGLU_NVFP4)
+        gq, gsf, gh = (host(t) for t in res)
+    for e in range(len(SMALL_COUNTS)):
+        lo, hi = off[e], off[e + 1]
+        if hi == lo:
+            continue
+        if epi == "bf16":
+            ref = bf16_values(O.round_to_bf16(
+                O.nvfp4_matmul(aq[rows[lo:hi]], asf[rows[lo:hi]], ga, bq[e], bsf[e], gb[e])))
+            assert_close(got[lo:hi], ref, f"expert {e}")
+        else:
+            ref_h = O.l1_swiglu(aq[rows[lo:hi]], asf[rows[lo:hi]], ga, bq[e], bsf[e], gb[e])
+            assert_close(gh[lo:hi], ref_h, f"h expert {e}")
+            assert_requant_matches(gq[lo:hi], gsf[lo:hi], ref_h, 64.0, f"requant expert {e}")
