@@ -389,7 +389,7 @@ def cpu_baseline(w, x, ids_h, tw_h, dev, budget_s=20.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="prefill", choices=sorted(I.WORKLOADS))
     ap.add_argument("--variant", default="nvfp4", choices=["nvfp4", "mx"],
