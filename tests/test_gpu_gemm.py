@@ -190,3 +190,27 @@ def test_small_expert_tiles(epi, K):
             ref_h = O.l1_swiglu(aq[rows[lo:hi]], asf[rows[lo:hi]], ga, bq[e], bsf[e], gb[e])
             assert_close(gh[lo:hi], ref_h, f"h expert {e}")
             assert_requant_matches(gq[lo:hi], gsf[lo:hi], ref_h, 64.0, f"requant expert {e}")
+
+
+@pytest.mark.parametrize("E,rows_per_expert", [
+    (1024, 32),     # the largest expert count of 32-token tiles, at its row limit
+    (1025, 4),      # one expert more: 128-token tiles
+    (4096, 33),     # the largest expert count of the API, 128-token tiles
+])
+def test_tile_configuration_limits(E, rows_per_expert):
+    """Expert counts at the edges of each tile configuration (the expert
+    prefix lives in LDS beside the stage buffers); sampled experts against
+    the oracle."""
+    rng = np.random.default_rng(E)
+    counts = rng.integers(0, 2 * rows_per_expert + 1, size=E)
+    counts[-1] = 0
+    counts[0] = rows_per_expert + 7
+    res, (aq, asf, ga, bq, bsf, gb, off, rows) = _grouped_case(list(counts), 32, 128, 41, nv.EPI_BF16)
+    got = bf16_values(host(res))
+    for e in sorted({0, 1, E // 2, E - 2, E - 1, *rng.integers(0, E, size=12).tolist()}):
+        lo, hi = off[e], off[e + 1]
+        if hi == lo:
+            continue
+        ref = bf16_values(O.round_to_bf16(
+            O.nvfp4_matmul(aq[rows[lo:hi]], asf[rows[lo:hi]], ga, bq[e], bsf[e], gb[e])))
+        assert_close(got[lo:hi], ref, f"expert {e}")
