@@ -6,7 +6,10 @@
 //   out[t][n] = bf16( sum_{j<k} w[t][j] * y[inv_perm[t*k+j]][n] ),
 // fp32 accumulation in slot order; rows d >= offsets[E] (invalid expert ids)
 // contribute nothing.  One block per token; each thread moves 16 bytes
-// (8 BF16) per row, so every wave reads 1 KiB contiguous spans.
+// (8 BF16) per row, so every wave reads 1 KiB contiguous spans.  y is read
+// once and out written once: both go through non-temporal accesses, which
+// keep them from displacing other lines in the caches (6% faster at
+// T=8192, H=7168, k=8 than plain accesses).
 #include "internal.hpp"
 #include "device.hpp"
 
@@ -14,6 +17,7 @@ namespace nvfp4 {
 
 namespace {
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 128;
 constexpr int kBatch = 8;                   // rows whose loads are in flight together
 
@@ -37,7 +41,12 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
         const int32_t d = j < k ? inv_perm[t * k + j] : n_valid;
         ok[b] = d < n_valid;          // slots past k and invalid expert ids add nothing
         w[b] = ok[b] ? topk_w[t * k + j] : 0.0f;
-        r[b] = ok[b] ? y[(int64_t)d * hv + v] : make_uint4(0, 0, 0, 0);
+        if (ok[b]) {
+          const u32x4 q = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(y + (int64_t)d * hv + v));
+          r[b] = make_uint4(q[0], q[1], q[2], q[3]);
+        } else {
+          r[b] = make_uint4(0, 0, 0, 0);
+        }
       }
 #pragma unroll
       for (int b = 0; b < kBatch; ++b) {
@@ -55,7 +64,8 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
     o.y = pack_bf16x2(acc[2], acc[3]);
     o.z = pack_bf16x2(acc[4], acc[5]);
     o.w = pack_bf16x2(acc[6], acc[7]);
-    out[t * hv + v] = o;
+    const u32x4 oq = {o.x, o.y, o.z, o.w};
+    __builtin_nontemporal_store(oq, reinterpret_cast<u32x4*>(out + t * hv + v));
   }
 }
 
