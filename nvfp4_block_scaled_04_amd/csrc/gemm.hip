@@ -36,6 +36,9 @@
 // 128 K go from HBM straight into LDS (global_load_lds), triple-buffered.  An
 // expert's rows are cut into ceil(rows/128) m tiles with its 32-row blocks
 // spread evenly over them; column blocks past a tile's rows are skipped.
+// Launches whose experts average at most 32 rows (decode-sized batches) use
+// 32-token tiles instead: smaller stages, four buffers, loads three stages
+// ahead, weights loaded with the non-temporal cache policy.
 //
 // MX mode.  The same tiles, loads and epilogues run on MXFP4 operands (E2M1
 // codes, one E8M0 scale per 32 elements stored once per 16-element block, as
@@ -373,7 +376,8 @@ __device__ __forceinline__ void k_begin(KState<BN, BM, WN, WM, JV>& st, int nks,
 //     so far may stay in flight), synchronise the block, read the half A
 //     fragments and scales of stage ks+1;
 //   steps 4-7: half B;
-//   the loads of stage ks+2 are spread over steps 0-5, two per step.
+//   the loads of stage ks+2 (ks+3 with four buffers) are spread over
+//   steps 0-5, two per step.
 // Every step runs its MFMAs on operands decoded during the previous step
 // while it decodes the next step's operands, so decode and MFMA overlap;
 // step 7 decodes step 0 of the next stage.  bw held stage ks-1, last read
@@ -678,10 +682,11 @@ __device__ __forceinline__ void tile_offsets(const Params& p, const Tile& t, int
 }
 
 // One tile: the K loop and the epilogue.  JV = number of 32-token column
-// blocks that hold rows (1..FM); the rest are skipped.  Stages 0 and 1 of
-// the tile were issued by the caller with the load offsets coff/soff; after
-// the K loop the stages 0 and 1 of the next tile (if any) are issued, with
-// coff/soff rewritten for it, so that their latency overlaps the epilogue.
+// blocks that hold rows (1..FM); the rest are skipped.  The tile's first
+// AHEAD stages (0 and 1; 0 to 2 for 32-token tiles) were issued by the caller
+// with the load offsets coff/soff; after the K loop those of the next tile
+// (if any) are issued, with coff/soff rewritten for it, so that their latency
+// overlaps the epilogue.
 template <int BN, int BM, int WN, int WM, int EPI, int FMT, int JV>
 __device__ __forceinline__ bool run_tile(const Params& p, uint8_t* smem, const int* tprefix,
                                          Sched& sc, const Tile& cur, uint32_t* coff,
