@@ -42,8 +42,8 @@ RIDGE = FP16_MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)   # flop per byte
 # each scaled by the ratio of known bytes to the counter's reading for a plain
 # 1 GiB device copy (--copy-calibration).  Reported only while the GEMM
 # sources hash to the value the counters were taken with; otherwise null.
-TRAFFIC = {("prefill", "l1", "nvfp4"): 6212200000, ("prefill", "l1", "mx"): 5691600000}
-TRAFFIC_SRC_SHA = "8b938b7b24fac494"
+TRAFFIC = {("prefill", "l1", "nvfp4"): 6209300000, ("prefill", "l1", "mx"): 5683300000}
+TRAFFIC_SRC_SHA = "8b7c0f15c97fcb86"
 
 
 def gemm_src_sha():
