@@ -19,7 +19,14 @@ float64 on exactly decoded operands.
 Pinning.  Every function here is pinned by ``tests/test_oracle_*.py`` against
 facts that do not come from this package: the pages' rules, the OCP FP8/FP4
 format definitions, closed forms, brute force and hand-worked fixtures under
-``tests/golden/``.  No function is "parity unpinned".
+``tests/golden/``.  The quantiser's open decisions are pinned by fixtures that
+tell the readings apart: the underflow test after the global scale (blocks
+whose raw amax and scaled amax fall on opposite sides of 6 * 2**-9, with
+gs = 4 and gs = 0.5), the correctly rounded a_s / 6 and gs / sd (values where
+a reciprocal multiply rounds differently and changes a byte), and a
+dequantise -> requantise round trip on blocks just above the threshold.  The
+near-tie certifier ``quantize.near_ties`` used by the GPU parity tests is
+pinned directly (values at, inside and outside the tolerance of a boundary).
 """
 
 from . import formats, quantize, route, layout, moe, mx  # noqa: F401

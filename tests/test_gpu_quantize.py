@@ -58,6 +58,27 @@ def test_quantize_zero_underflow_and_negative_zero_blocks():
     _check_quant(x.to(torch.bfloat16), what="special")
 
 
+def _golden_examples():
+    # the hand-worked fixtures of the oracle's pins (tests/golden)
+    import test_oracle_quantize as T
+    return T._load_examples()
+
+
+@pytest.mark.parametrize("ex", _golden_examples(), ids=lambda e: e["name"])
+def test_quantize_hand_worked_examples(ex):
+    """The device quantiser on the hand-worked fixtures: the expected bytes
+    were derived from the block rule, not by any quantiser program."""
+    x32 = ex["x"].astype(np.float32).reshape(1, -1)
+    bits = (x32.view(np.uint32) >> 16).astype(np.uint16)
+    x = _bits_to_dev(bits)
+    gs_in = None if ex["gs"] is None else torch.tensor([ex["gs"]], dtype=torch.float32, device=DEV)
+    print(f"[case] quantize worked example {ex['name']}", flush=True)
+    q, sf, gs = nv.quantize(x, gs_in=gs_in)
+    torch.cuda.synchronize()
+    assert host(sf).ravel().tolist() == ex["sf"].tolist()
+    assert host(q).ravel().tolist() == ex["q"].tolist()
+
+
 def test_quantize_all_zero_tensor():
     x = torch.zeros((8, 64), dtype=torch.bfloat16, device=DEV)
     q, sf, gs = nv.quantize(x)

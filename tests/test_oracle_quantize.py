@@ -232,3 +232,58 @@ def test_groups_have_independent_scales():
         qg, sfg, gsg = Q.quantize_nvfp4(xb[16 * g:16 * g + 16])
         assert gsg[0] == gs[g]
         assert np.array_equal(qg, q[16 * g:16 * g + 16])
+
+
+def test_dequant_requant_byte_identical_at_the_underflow_boundary():
+    # README "Correctness Bugs Fixed", bugs 2 and 4 together.  Weight-scale
+    # blocks (std 0.02, gs ~ 2.7e4) whose raw amax sits 0-7% above 6*2^-9: the
+    # E4M3 rounding of their scale can bring the dequantised amax below
+    # 6*2^-9, so a rule that tested the raw amax would zero them on the second
+    # pass.  With the test after the global scale (a_s ~ 300) nothing
+    # underflows and the round trip is exact.
+    rng = np.random.default_rng(12)
+    x = F.bf16_bits_to_f32(_randn_bf16((256, 512), 12, std=0.02)).copy()
+    thr = 6.0 * 2.0 ** -9
+    blocks = x.reshape(256, 32, 16)
+    picks = rng.choice(256 * 32, size=200, replace=False)
+    for p in picks:
+        r, b = divmod(int(p), 32)
+        blk = blocks[r, b]
+        blk *= np.float32(thr * (1.0 + rng.uniform(0.0, 0.07)) / np.abs(blk).max())
+    xb = (x.view(np.uint32) >> 16).astype(np.uint16)      # truncate to bf16
+    raw = F.bf16_bits_to_f32(xb).reshape(256, 32, 16)
+    near = np.abs(raw).max(-1)[np.unravel_index(picks, (256, 32))]
+    assert np.all(near >= np.float32(thr) * 0.999) and np.all(near <= thr * 1.07)
+    q, sf, gs = Q.quantize_nvfp4(xb)
+    assert np.all(sf != 0)                                 # nothing underflows at a_s ~ 300
+    xd = Q.dequantize(q, sf, gs[0])
+    # some dequantised blocks fall below the raw threshold: those are the
+    # blocks a raw-amax rule would zero on requantisation
+    assert np.sum(np.abs(xd).reshape(256, 32, 16).max(-1) < thr) > 0
+    q2, sf2, _ = Q.quantize_nvfp4(F.round_to_bf16(xd))
+    assert np.array_equal(q, q2) and np.array_equal(sf, sf2)
+    q3, sf3, _ = Q.quantize_nvfp4(xd.astype(np.float32), gs_in=gs)
+    assert np.array_equal(q, q3) and np.array_equal(sf, sf3)
+
+
+def test_near_ties_marks_exactly_the_values_near_a_boundary():
+    # near_ties certifies which requantisation differences the parity tests
+    # excuse; every expectation below follows from the block rule at gs = 1.
+    tau = 1e-3
+    row = np.zeros(64, np.float32)
+    # block 0: amax 6 -> t = 1 (an E4M3 value, far from its midpoints
+    # 0.96875 and 1.0625), r = 1, so v = |x|
+    row[0:8] = [6.0, 2.5, 2.5 * (1 + tau / 4), 2.5 * (1 + 8 * tau), 2.75, 0.1, 1.2501, 0.0]
+    elem_expect = [False, True, True, False, False, False, True, False]
+    # block 1: amax 6.375 -> t = 1.0625, the midpoint of E4M3 1 and 1.125
+    row[16:19] = [6.375, 1.0, 0.3]
+    # block 2: amax just above 6*2^-9: the underflow decision is a near tie
+    row[32] = np.float32(6.0 * 2.0 ** -9 * (1 + tau / 2))
+    # block 3: amax 3 -> t = 0.5 (an E4M3 value), r = 2; 1.0 -> v = 2, far
+    row[48:50] = [3.0, 1.0]
+    elem, block = Q.near_ties(row.reshape(1, 64), np.float32(1.0), tau)
+    assert block.ravel().tolist() == [False, True, True, False]
+    assert elem[0, 0:8].tolist() == elem_expect
+    assert np.all(elem[0, 16:48])                      # every element of a near-tie block
+    assert not elem[0, 48:64].any()
+    assert not elem[0, 8:16].any()                     # zeros: 0.25 is far from 0
