@@ -203,8 +203,13 @@ nvfp4_status nvfp4_quantize_scatter(const void* x_bf16, int64_t T, int64_t H, in
  *   (same block rule as nvfp4_quantize) into c_q uint8 [M][I/2] and
  *   c_sf uint8 [M][I/16]; c_debug_f32 (nullable) [M][I] receives h.
  * Rows d >= off[E] are not written.  Requires off[E] <= M (M = rows of C).
- * Shapes: E >= 1, M >= 0, K % 128 == 0, K >= 128, N % 32 == 0, N >= 32;
- *   SwiGLU: N % 32 == 0 (I % 16 == 0).
+ * Shapes: E >= 1, M >= 0, K % 128 == 0, 128 <= K < 2^24, N % 32 == 0,
+ *   32 <= N < 2^30; SwiGLU: N % 32 == 0 (I % 16 == 0).
+ * A rows are addressed with 32-bit byte offsets, so the A codes must span
+ *   less than 4 GiB: without a gather M*K/2 < 2^32 (checked, else
+ *   NVFP4_ERR_SHAPE); with a gather every a_row_src[d]/a_row_div must be a
+ *   row r of A with (r+1)*K/2 <= 2^32 (a precondition on device data, which
+ *   the host cannot read).
  * Unused output pointers of the other epilogue may be NULL.
  * Workspace: at least nvfp4_grouped_gemm_workspace_size() bytes, 4-byte
  *   aligned, caller-owned: the tile scheduler's counters.  Each call first
@@ -314,7 +319,9 @@ nvfp4_status nvfp4_moe_combine(const void* y_bf16, const int32_t* inv_perm,
  *   grouped GEMM L2 (BF16) -> combine.
  * taps (nullable): every non-NULL member receives that intermediate (the
  *   kernels write straight into it instead of the workspace).
- * Shapes: T >= 0, H % 128 == 0, I % 128 == 0, 1 <= k <= 64, 1 <= E <= 4096.
+ * Shapes: T >= 0, H % 128 == 0, I % 128 == 0, 1 <= k <= 64, 1 <= E <= 4096,
+ *   T*k < 2^31, H < 2^24, I < 2^23, and the quantised x and h below 4 GiB
+ *   each (T*H/2 < 2^32, T*k*I/2 < 2^32; else NVFP4_ERR_SHAPE).
  * Workspace: moe_expert_forward_workspace_size() bytes.
  * ---------------------------------------------------------------------- */
 typedef struct nvfp4_moe_taps {

@@ -96,7 +96,13 @@ nvfp4_status check_gemm(const nvfp4::GemmArgs& a) {
   if (a.M < 0 || a.M >= (int64_t(1) << 31)) return fail(NVFP4_ERR_SHAPE, "M must be in [0, 2^31)");
   if (a.K < 128 || a.K % 128) return fail(NVFP4_ERR_SHAPE, "K must be a positive multiple of 128 (got %lld)", (long long)a.K);
   if (a.N < 32 || a.N % 32) return fail(NVFP4_ERR_SHAPE, "N must be a positive multiple of 32 (got %lld)", (long long)a.N);
-  if (a.N >= (int64_t(1) << 30) || a.K >= (int64_t(1) << 30)) return fail(NVFP4_ERR_SHAPE, "N and K must be < 2^30");
+  if (a.N >= (int64_t(1) << 30)) return fail(NVFP4_ERR_SHAPE, "N must be < 2^30");
+  // the kernels address a K stage of a weight tile (512 rows x 64 bytes) and
+  // an A row (K/2 bytes) with 32-bit byte offsets
+  if (a.K >= (int64_t(1) << 24)) return fail(NVFP4_ERR_SHAPE, "K must be < 2^24");
+  if (!a.a_row_src && a.M * (a.K / 2) >= (int64_t(1) << 32))
+    return fail(NVFP4_ERR_SHAPE, "A codes must be below 4 GiB (M*K/2 = %lld bytes)",
+                (long long)(a.M * (a.K / 2)));
   if (a.a_row_src && a.a_row_div < 1) return fail(NVFP4_ERR_SHAPE, "a_row_div must be >= 1");
   // tile indices are 32-bit: (M/128 + E) m tiles times N/512 n tiles
   if (((a.M + 127) / 128 + a.E) * ((a.N + 511) / 512) >= (int64_t(1) << 31))
@@ -423,6 +429,11 @@ nvfp4_status forward_impl(int mx, const void* x_bf16, int64_t T, int64_t H, int6
   if (k < 1 || k > 64) return fail(NVFP4_ERR_SHAPE, "k must be in [1, 64] (got %d)", k);
   if (E < 1 || E > 4096) return fail(NVFP4_ERR_SHAPE, "E must be in [1, 4096] (got %d)", E);
   if (T * k >= (int64_t(1) << 31)) return fail(NVFP4_ERR_SHAPE, "T*k must be < 2^31");
+  // the GEMMs address their A rows with 32-bit byte offsets: the quantised x
+  // (L1, gathered) and h (L2) must each stay below 4 GiB of codes
+  if (T * (H / 2) >= (int64_t(1) << 32) || T * k * (I / 2) >= (int64_t(1) << 32))
+    return fail(NVFP4_ERR_SHAPE, "quantised x (T*H/2 bytes) and h (T*k*I/2 bytes) must be below 4 GiB");
+  if (H >= (int64_t(1) << 24) || I >= (int64_t(1) << 23)) return fail(NVFP4_ERR_SHAPE, "H must be < 2^24 and I < 2^23");
   if (T > 0 && (!x_bf16 || !topk_ids || !topk_w || !out_bf16))
     return fail(NVFP4_ERR_INVALID_ARG, "x, topk_ids, topk_w and out must be non-NULL");
   if (!w1_q || !w1_sf || !gs_w1 || !w2_q || !w2_sf || !gs_w2 || !gs_h)

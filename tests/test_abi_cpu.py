@@ -102,6 +102,11 @@ def test_gemm_rejects(L):
     assert _gemm(L, src=FAKE, div=0) == -2
     assert _gemm(L, off=None) == -1
     assert _gemm(L, M=1 << 30, N=1 << 29) == -2          # tile indices would overflow 32 bits
+    # A codes of 4 GiB or more would wrap the kernels' 32-bit row offsets
+    assert _gemm(L, M=1_200_000, N=2048, K=7168) == -2    # 4.3 GB without a gather
+    assert _gemm(L, M=300_000, N=256, K=28672) == -2
+    assert _gemm(L, M=1_198_373, N=256, K=7168) == -2     # the first M with M*K/2 >= 2^32
+    assert _gemm(L, K=1 << 24) == -2                      # K stage offsets of a weight tile
 
 
 def test_gemm_workspace(L):
@@ -141,6 +146,9 @@ def test_combine_and_forward_reject(L):
     assert f(gs_h=None) == -1
     assert f(wsb=16) == -3
     assert f(ws=FAKE + 16) == -3
+    # quantised x or h of 4 GiB or more would wrap the GEMMs' 32-bit row offsets
+    assert f(T=1_200_000, H=7168, I=128, k=1) == -2       # x codes 4.3 GB
+    assert f(T=524_288, H=1024, I=2048, k=8) == -2        # h codes 4.3 GB
     assert L.nvfp4_weight_layout(FAKE, 2, 4, 24, 1, FAKE, None) == -2
     assert L.nvfp4_weight_layout(FAKE, 2, 4, 32, 1, None, None) == -1
 
