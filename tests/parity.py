@@ -41,21 +41,46 @@ def cosine(a, b):
     return float(a @ b / (na * nb))
 
 
-def assert_close(gpu, ref, what):
-    """The floating-point parity bar; gpu/ref are float arrays."""
+# BF16 outputs (y, the combined output, the dense linear): both sides round
+# their own sum to BF16, the GPU from fp32 and the oracle from fp64; where the
+# two unrounded values straddle a rounding boundary the results differ by one
+# BF16 step, which exceeds MAXABS_RMS * RMS for elements above about 5 * RMS.
+# Such an element may differ by one step of its value; at most
+# MAX_BF16_STEP_FRACTION of the elements may exceed the plain bound.
+MAX_BF16_STEP_FRACTION = 1e-3
+
+
+def bf16_step(v):
+    """One BF16 step (unit in the last place) at each |v| (v nonzero)."""
+    _, e = np.frexp(np.abs(np.asarray(v, np.float64)))   # |v| = m * 2**e, 0.5 <= m < 1
+    return np.ldexp(1.0, e - 8)
+
+
+def assert_close(gpu, ref, what, log=True, bf16=False):
+    """The floating-point parity bar; gpu/ref are float arrays.  bf16=True for
+    BF16 outputs compared with the oracle's BF16 rounding (see above)."""
     gpu = np.asarray(gpu, np.float64)
     ref = np.asarray(ref, np.float64)
     assert gpu.shape == ref.shape, (what, gpu.shape, ref.shape)
     assert np.all(np.isfinite(gpu)), f"{what}: non-finite GPU values"
     rms = float(np.sqrt(np.mean(ref ** 2))) if ref.size else 0.0
-    err = float(np.max(np.abs(gpu - ref))) if ref.size else 0.0
+    d = np.abs(gpu - ref)
+    err = float(np.max(d)) if ref.size else 0.0
     cos = cosine(gpu, ref)
-    print(f"[parity] {what}: cos={cos:.7f} maxabs/rms={err / rms if rms else 0:.3e} n={ref.size}")
+    over = d > MAXABS_RMS * rms
+    if log or over.any():
+        print(f"[parity] {what}: cos={cos:.7f} maxabs/rms={err / rms if rms else 0:.3e} n={ref.size}"
+              + (f" ({int(over.sum())} elements one BF16 step apart above the bound)" if over.any() else ""))
     assert cos >= COS_MIN, f"{what}: cosine {cos} < {COS_MIN}"
-    assert err <= MAXABS_RMS * rms, f"{what}: max abs err {err} > {MAXABS_RMS} * rms {rms}"
+    if bf16 and over.any():
+        assert np.all(d[over] <= bf16_step(ref[over])), \
+            f"{what}: max abs err {err} > {MAXABS_RMS} * rms {rms} and beyond one BF16 step"
+        assert over.mean() <= MAX_BF16_STEP_FRACTION, f"{what}: {int(over.sum())} elements above the bound"
+    else:
+        assert err <= MAXABS_RMS * rms, f"{what}: max abs err {err} > {MAXABS_RMS} * rms {rms}"
 
 
-def assert_requant_matches(gpu_q, gpu_sf, ref_h, gs_h, what):
+def assert_requant_matches(gpu_q, gpu_sf, ref_h, gs_h, what, log=True):
     """GPU-requantised h vs the oracle's requantisation of its own h.
 
     Scale bytes must be equal except in blocks whose scale decision is a
@@ -80,7 +105,33 @@ def assert_requant_matches(gpu_q, gpu_sf, ref_h, gs_h, what):
           (((g_codes ^ ref_codes) & 8) == 0)
     assert np.all(adj[e_only]), f"{what}: a near-tie code moved by more than one grid step"
     frac = diff.sum() / max(1, diff.size)
-    print(f"[parity] {what}: requant codes differ at {int(diff.sum())} certified near-ties "
-          f"({frac:.2e}), {int((gpu_sf != ref_sf).sum())} scale bytes")
+    if log or diff.any():
+        print(f"[parity] {what}: requant codes differ at {int(diff.sum())} certified near-ties "
+              f"({frac:.2e}), {int((gpu_sf != ref_sf).sum())} scale bytes")
     assert frac <= MAX_TIE_FRACTION
     return diff.any(axis=1) | (gpu_sf != ref_sf).any(axis=1)
+
+
+def assert_mx_requant_matches(gpu_q, gpu_sc, ref_h, gs_h, what):
+    """GPU-requantised and MX re-encoded h vs the oracle's (NVFP4 requant of
+    its own h, then the MX re-encoding).  A 32-element MX block may differ
+    only where the NVFP4 requant holds a certified near-tie inside it (one
+    flipped code can move the block's E8M0 scale and so every code of the
+    block).  gpu_sc holds each E8M0 byte twice (the NVFP4 scale layout).
+    Returns the boolean mask of rows whose bytes differ from the oracle's."""
+    from oracle import mx as X
+    codes, sf = Q.quantize_blocks(ref_h, np.float32(gs_h))
+    ref_q, ref_sc = X.nvfp4_to_mx(Q.pack_codes(codes), sf)
+    elem, _ = Q.near_ties(ref_h, np.float32(gs_h), TAU)
+    R, C = ref_h.shape
+    tie32 = elem.reshape(R, C // 32, 32).any(axis=-1)
+    dq = (np.asarray(gpu_q) != ref_q).reshape(R, C // 32, 16).any(axis=-1)
+    ds = (np.asarray(gpu_sc).reshape(R, C // 32, 2) != ref_sc[..., None]).any(axis=-1)
+    diff = dq | ds
+    outside = diff & ~tie32
+    assert not outside.any(), (f"{what}: {int(outside.sum())} MX blocks differ outside certified "
+                               f"near-ties (first at {np.argwhere(outside)[:3].tolist()})")
+    if diff.any():
+        print(f"[parity] {what}: {int(diff.sum())} MX blocks differ at certified near-ties")
+    assert diff.mean() <= MAX_TIE_FRACTION * 32
+    return diff.any(axis=1)

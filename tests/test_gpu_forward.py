@@ -2,6 +2,7 @@
 oracle: full comparison on small workloads, sampled tokens at full size."""
 
 import concurrent.futures as cf
+import functools
 import multiprocessing as mp
 
 import numpy as np
@@ -13,7 +14,7 @@ from nvfp4_block_scaled_04_amd import inputs as I
 from oracle import moe as O
 from oracle import quantize as Q
 from oracle import route as R
-from parity import host, bf16_values, assert_close, assert_requant_matches, TAU
+from parity import host, bf16_values, assert_close, assert_requant_matches, assert_mx_requant_matches
 import oracle_pool
 
 pytestmark = pytest.mark.gpu
@@ -78,12 +79,12 @@ def _check_full(w, ids=None):
                                       ref["h"][:nv_rows], w.gs_h, f"{w.name} requant")
     clean = ~tie_rows
     assert_close(bf16_values(tp["y_bf16"][:nv_rows])[clean], bf16_values(ref["y"][:nv_rows])[clean],
-                 f"{w.name} y")
+                 f"{w.name} y", bf16=True)
     tok_clean = np.ones(w.T, bool)
     for d in np.nonzero(tie_rows)[0]:
         tok_clean[ref["perm"][d] // w.k] = False
     assert_close(bf16_values(host(out))[tok_clean], bf16_values(ref["out"])[tok_clean],
-                 f"{w.name} out")
+                 f"{w.name} out", bf16=True)
     assert tok_clean.mean() > 0.9
 
 
@@ -121,9 +122,11 @@ def test_forward_zero_tokens():
     assert out.shape == (0, 128)
 
 
-# ----------------------------------------------------------- full-size, sampled
+# ----------------------------------------------------------- full size
 
 _BIG = {}
+POOL = 16                                  # oracle worker processes (a GPU machine's CPU share)
+CHUNK_ROWS = 2048                          # rows of one expert per oracle job
 
 
 def _big_weights(w):
@@ -141,58 +144,208 @@ def _sample_tokens(name, ids):
     T = ids.shape[0]
     if name == "skewed":
         top = np.bincount(ids.ravel(), minlength=256).argmax()
-        return [int(np.nonzero((ids == top).any(axis=1))[0][0])]
-    return [0, T - 1] if name == "decode" else [T // 3]
+        return [int(np.nonzero((ids == top).any(axis=1))[0][0]), T // 2]
+    return [0, T - 1] if name == "decode" else [T // 3, T - 1]
 
 
+def _quantize_x(name, xb, chunk=2048):
+    """The oracle's quantisation of the whole x (per-call global scale)."""
+    gs_a = Q.global_scale(xb)
+    T, H = xb.shape
+    aq = np.empty((T, H // 2), np.uint8)
+    asf = np.empty((T, H // 16), np.uint8)
+    for r0 in range(0, T, chunk):
+        c, sc = Q.quantize_blocks(xb[r0:r0 + chunk], gs_a)
+        aq[r0:r0 + chunk] = Q.pack_codes(c)
+        asf[r0:r0 + chunk] = sc
+    return aq, asf, gs_a
+
+
+# experts by row count: m tiles of 1, 2, 3 and 4 32-row blocks, then 2, 3 and
+# more 128-row m tiles; plus the smallest and the largest expert
+_CATEGORIES = [(1, 32), (33, 64), (65, 96), (97, 128), (129, 256), (257, 384), (385, 1 << 30)]
+
+
+def _pick_experts(name, offsets):
+    counts = np.diff(offsets.astype(np.int64))
+    live = np.nonzero(counts)[0]
+    if name == "decode":
+        return [int(e) for e in live]                    # every routed row
+    picks = set()
+    for lo, hi in _CATEGORIES:
+        sel = live[(counts[live] >= lo) & (counts[live] <= hi)]
+        if sel.size:
+            picks.add(int(sel[0]))
+    picks.add(int(live[np.argmax(counts[live])]))
+    picks.add(int(live[np.argmin(counts[live])]))
+    return sorted(picks)
+
+
+def _oracle_rows(w, ew, jobs, worker, check_weights, a_rows):
+    """Run the oracle for (expert, rows) jobs in a process pool, a batch of
+    experts at a time (their BF16 weights are generated on the device and
+    copied to the host per batch), and yield (expert, rows, result).
+    check_weights(e, result) compares the expert's prepared weights once."""
+    ctx = mp.get_context("spawn")
+    by_e = {}
+    for e, rows in jobs:
+        by_e.setdefault(e, []).append(rows)
+    experts = sorted(by_e)
+    done = set()
+    with cf.ProcessPoolExecutor(max_workers=POOL, mp_context=ctx,
+                                initializer=oracle_pool.init_worker) as ex:
+        for b0 in range(0, len(experts), 2 * POOL):
+            batch = experts[b0:b0 + 2 * POOL]
+            futs = []
+            for e in batch:
+                w1, w2 = (host(t) for t in I.make_expert_weights(w, e, DEV))
+                for rows in by_e[e]:
+                    aq, asf = a_rows(rows)
+                    futs.append((e, rows, ex.submit(worker, w1, w2, aq, asf)))
+            for e, rows, f in futs:
+                r = f.result()
+                if e not in done:
+                    check_weights(e, r)
+                    done.add(e)
+                yield e, rows, r
+            print(f"[case] {w.name}: oracle done for {min(b0 + 2 * POOL, len(experts))} of "
+                  f"{len(experts)} experts", flush=True)
+
+
+def _jobs(offsets, experts, extra_rows):
+    """All rows of `experts` (cut into chunks) and the rows in extra_rows
+    (expert -> row list) of the others."""
+    jobs = []
+    for e in experts:
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        for c0 in range(lo, hi, CHUNK_ROWS):
+            jobs.append((e, np.arange(c0, min(hi, c0 + CHUNK_ROWS))))
+    for e, rows in extra_rows.items():
+        if e not in experts:
+            jobs.append((e, np.array(sorted(set(rows)))))
+    return jobs
+
+
+def _token_rows(ids, inv, k, toks):
+    extra = {}
+    for t in toks:
+        for j in range(k):
+            extra.setdefault(int(ids[t, j]), []).append(int(inv[t * k + j]))
+    return extra
+
+
+def _check_out(name, w, out_gpu, tw, inv, y_ref, same, toks, slots):
+    """out of every token whose `slots` rows were all checked with identical
+    quantised h: the oracle's combine of the oracle's y rows."""
+    got, ref = [], []
+    for t in toks:
+        ds = [int(inv[t * slots + j]) for j in range(slots)]
+        if not all(d in y_ref and same[d] for d in ds):
+            continue
+        acc = np.zeros(w.H)
+        for j, d in enumerate(ds):
+            wj = np.float64(tw[t, j]) if j < tw.shape[1] else 1.0
+            acc += wj * bf16_values(y_ref[d])
+        got.append(bf16_values(out_gpu[t]))
+        ref.append(bf16_values(O.round_to_bf16(acc)))
+    assert got, f"{name}: no token had all its rows checked"
+    assert_close(np.stack(got), np.stack(ref), f"{name} out ({len(got)} tokens)", bf16=True)
+    return len(got)
+
+
+def _check_rows_nvfp4(name, w, tp, e, rows, r, y_ref, same):
+    assert_close(tp["h_f32"][rows], r["h"], f"{name} h e={e}", log=False)
+    tie = assert_requant_matches(tp["h_q"][rows], tp["h_sf"][rows], r["h"], w.gs_h,
+                                 f"{name} requant e={e}", log=False)
+    # identical quantised operands: the GPU's h bytes equal the oracle's
+    ok = (tp["h_q"][rows] == r["h_q"]).all(axis=1) & (tp["h_sf"][rows] == r["h_sf"]).all(axis=1)
+    assert not (ok & tie).any()
+    if ok.any():
+        assert_close(bf16_values(tp["y_bf16"][rows][ok]), bf16_values(r["y"][ok]),
+                     f"{name} y e={e}", log=False, bf16=True)
+    for i, d in enumerate(rows):
+        y_ref[int(d)] = r["y"][i]
+        same[int(d)] = bool(ok[i])
+    return int(ok.sum())
+
+
+@pytest.mark.timeout(1500)
 @pytest.mark.parametrize("name", ["decode", "prefill", "skewed", "moe384"])
-def test_forward_full_size_sampled_tokens(name):
+def test_forward_full_size(name):
+    """A full-size workload: the whole quantised x and the routing bit-exact;
+    every row of experts chosen across the row-count categories (every
+    expert on the decode batch) through L1 + SwiGLU (f32 h, to the bar), the
+    requant (certified near-ties) and L2 (to the bar, wherever the GPU's
+    requantised h equals the oracle's byte for byte, i.e. identical operands);
+    the output of sampled tokens (all tokens on the decode batch)."""
     w = I.WORKLOADS[name]
     ew = _big_weights(w)
     x, ids, tw, out, tp = _run(w, ew)
-    # routing is cheap to check in full
     roff, rperm, rinv, _ = R.route(ids, w.E)
     assert np.array_equal(tp["expert_offsets"], roff)
     assert np.array_equal(tp["perm"], rperm) and np.array_equal(tp["inv_perm"], rinv)
-    xb = host(x)
-    gs_a = Q.global_scale(xb)
+    aq, asf, gs_a = _quantize_x(name, host(x))
     assert tp["gs_a"][0] == gs_a
-    toks = _sample_tokens(name, ids)
-    jobs = []
-    for t in toks:
-        aq, asf = Q.quantize_blocks(xb[t:t + 1], gs_a)
-        aq = Q.pack_codes(aq)
-        assert np.array_equal(tp["a_q"][t], aq[0]) and np.array_equal(tp["a_sf"][t], asf[0])
-        for j in range(w.k):
-            jobs.append((t, j, int(ids[t, j]), aq, asf))
-    experts = sorted({e for _, _, e, _, _ in jobs})
-    bf = {e: tuple(host(a) for a in I.make_expert_weights(w, e, DEV)) for e in experts}
-    print(f"[case] {name}: oracle for tokens {toks} over {len(experts)} experts", flush=True)
-    ctx = mp.get_context("spawn")
-    with cf.ProcessPoolExecutor(max_workers=min(8, len(jobs)), mp_context=ctx) as ex:
-        futs = [ex.submit(oracle_pool.expert_rows, bf[e][0], bf[e][1], aq, asf, gs_a,
-                          np.float32(w.gs_h)) for (_, _, e, aq, asf) in jobs]
-        res = [f.result() for f in futs]
-    for (t, j, e, _, _), r in zip(jobs, res):
+    assert np.array_equal(tp["a_q"], aq) and np.array_equal(tp["a_sf"], asf)
+    print(f"[rows] {name}: quantised x bit-exact on all {w.T} tokens "
+          f"({int((asf == 0).sum())} zero/underflow blocks)", flush=True)
+    experts = _pick_experts(name, roff)
+    toks = list(range(w.T)) if name == "decode" else _sample_tokens(name, ids)
+    jobs = _jobs(roff, experts, _token_rows(ids, rinv, w.k, toks))
+    counts = np.diff(roff)
+    print(f"[case] {name}: oracle for {len(jobs)} jobs, experts {experts[:12]} "
+          f"(rows {[int(counts[e]) for e in experts[:12]]})", flush=True)
+
+    rw = ew.rowmajor
+    gw1, gw2 = host(ew.gs_w1), host(ew.gs_w2)
+
+    def check_weights(e, r):
         for n in ("w1_q", "w1_sf", "w2_q", "w2_sf"):
-            assert np.array_equal(host(ew.rowmajor[n][e]), r[n]), (n, e)
-        assert host(ew.gs_w1)[e] == r["gs_w1"] and host(ew.gs_w2)[e] == r["gs_w2"]
-    for t in toks:
-        rows = [(j, r) for (tt, j, _, _, _), r in zip(jobs, res) if tt == t]
-        acc = np.zeros(w.H)
-        tie = False
-        for j, r in rows:
-            d = int(rinv[t * w.k + j])
-            assert_close(tp["h_f32"][d:d + 1], r["h"], f"{name} t={t} j={j} h")
-            tie |= bool(assert_requant_matches(tp["h_q"][d:d + 1], tp["h_sf"][d:d + 1], r["h"],
-                                               w.gs_h, f"{name} t={t} j={j} requant").any())
-            if not tie:
-                assert_close(bf16_values(tp["y_bf16"][d:d + 1]), bf16_values(r["y"]),
-                             f"{name} t={t} j={j} y")
-            acc += np.float64(tw[t, j]) * bf16_values(r["y"][0])
-        ref_out = bf16_values(O.round_to_bf16(acc))
-        if not tie:
-            assert_close(bf16_values(host(out)[t]), ref_out, f"{name} t={t} out")
+            assert np.array_equal(host(rw[n][e]), r[n]), (n, e)
+        assert gw1[e] == r["gs_w1"] and gw2[e] == r["gs_w2"]
+
+    def worker_args(rows):
+        tok = rperm[rows] // w.k
+        return aq[tok], asf[tok]
+
+    y_ref, same = {}, {}
+    n_h = n_y = 0
+    worker = functools.partial(oracle_pool.expert_rows, gs_a=gs_a, gs_h=np.float32(w.gs_h))
+    for e, rows, r in _oracle_rows(w, ew, jobs, worker, check_weights, worker_args):
+        n_h += rows.size
+        n_y += _check_rows_nvfp4(name, w, tp, e, rows, r, y_ref, same)
+    n_out = _check_out(name, w, host(out), tw, rinv, y_ref, same, toks, w.k)
+    print(f"[rows] {name}: h and requant on {n_h} rows, y on {n_y} rows "
+          f"({n_h - n_y} rows with a certified near-tie difference), out on {n_out} tokens",
+          flush=True)
+    assert n_h - n_y <= max(2, n_h // 100)
+
+
+@pytest.mark.timeout(600)
+def test_combine_full_size_prefill():
+    """The combine alone over the whole prefill output: seeded y rows, the
+    prefill routing, against the oracle's combine of the same y."""
+    w = I.WORKLOADS["prefill"]
+    T, k, H = w.T, w.k, w.H
+    ids, tw = I.make_routing(w)
+    g = torch.Generator(device=DEV).manual_seed(77)
+    y = torch.randn((T * k, H), generator=g, device=DEV).to(torch.bfloat16)
+    off, perm, inv, bad = nv.moe_route(torch.from_numpy(ids).to(DEV), w.E)
+    print("[case] combine full size prefill", flush=True)
+    out = nv.moe_combine(y, inv, torch.from_numpy(tw).to(DEV), off)
+    torch.cuda.synchronize()
+    roff, _, rinv, _ = R.route(ids, w.E)
+    assert np.array_equal(host(inv), rinv)
+    yb, ob = host(y), host(out)
+    n_valid = int(roff[-1])
+    for t0 in range(0, T, 1024):
+        sl = slice(t0, min(T, t0 + 1024))
+        d = rinv.reshape(T, k)[sl]
+        ref = O.combine(yb[d.ravel()], np.arange(d.size, dtype=np.int32), tw[sl], d.size)
+        assert_close(bf16_values(ob[sl]), bf16_values(ref), f"combine tokens {t0}..", log=t0 == 0, bf16=True)
+        # the fp32 sum in slot order rounds to the oracle's bf16 almost everywhere
+        assert (ob[sl] == ref).mean() > 0.999
+    print(f"[rows] combine: all {T} tokens x {H} columns to the bar ({n_valid} valid rows)", flush=True)
 
 
 # ----------------------------------------------------------- shared expert
@@ -232,14 +385,16 @@ def test_forward_with_shared_expert(name, invalid):
     # shared rows are the last T valid rows, in token order
     hs = host(taps["h_f32"])[off[w.E]:off[w.E + 1]]
     assert_close(hs, ref["h_shared"], "shared h")
-    assert_close(bf16_values(host(out)), bf16_values(ref["out"]), "out with shared expert")
+    assert_close(bf16_values(host(out)), bf16_values(ref["out"]), "out with shared expert", bf16=True)
 
 
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["prefill", "decode", "skewed"])
-def test_mx_forward_sampled_token(name):
-    """The MX variant at full size: one token's k expert rows and its output
-    against the MX oracle (weights re-encoded on both sides and compared
-    bit-exactly)."""
+def test_mx_forward_full_size(name):
+    """The MX variant at full size: the whole re-encoded x bit-exact; sampled
+    tokens' k expert rows (weights re-encoded on both sides and compared
+    bit-exactly) through h (to the bar), requant + re-encode (certified), y
+    (to the bar wherever the GPU's MX h equals the oracle's) and the output."""
     from oracle import mx as X
     w = I.WORKLOADS[name]
     ew_mx = nv.mx_expert_weights(_big_weights(w))
@@ -250,54 +405,66 @@ def test_mx_forward_sampled_token(name):
     z = lambda shape, dt: torch.zeros(shape, dtype=dt, device=DEV)
     taps = dict(a_q=z((T, H // 2), torch.uint8), a_sf=z((T, H // 16), torch.uint8),
                 gs_a=z((1,), torch.float32), inv_perm=z((M,), torch.int32),
-                h_f32=z((M, Iw), torch.float32), y_bf16=z((M, H), torch.bfloat16))
-    print(f"[case] mx forward {name} (sampled token)", flush=True)
+                h_f32=z((M, Iw), torch.float32), h_q=z((M, Iw // 2), torch.uint8),
+                h_sf=z((M, Iw // 16), torch.uint8), y_bf16=z((M, H), torch.bfloat16))
+    print(f"[case] mx forward {name} (full size)", flush=True)
     out = nv.moe_expert_forward(x, torch.from_numpy(ids).to(DEV), torch.from_numpy(tw).to(DEV),
                                 ew_mx, torch.tensor([w.gs_h], dtype=torch.float32, device=DEV),
                                 taps=taps)
     torch.cuda.synchronize()
     tp = {n: host(t) for n, t in taps.items()}
-    xb = host(x)
-    gs_a = Q.global_scale(xb)
+    aq, asf, gs_a = _quantize_x(name, host(x))
     assert tp["gs_a"][0] == gs_a
-    t = _sample_tokens(name, ids)[0] if name == "skewed" else T // 5
-    aq, asf = Q.quantize_blocks(xb[t:t + 1], gs_a)
-    amq, amsc = X.nvfp4_to_mx(Q.pack_codes(aq), asf)
-    assert np.array_equal(tp["a_q"][t], amq[0])
-    assert np.array_equal(tp["a_sf"][t], np.repeat(amsc[0], 2))
-    experts = [int(e) for e in ids[t]]
-    bf = {e: tuple(host(a) for a in I.make_expert_weights(w, e, DEV)) for e in experts}
-    ctx = mp.get_context("spawn")
-    with cf.ProcessPoolExecutor(max_workers=len(experts), mp_context=ctx) as ex:
-        res = list(ex.map(oracle_pool.expert_rows_mx, [bf[e][0] for e in experts],
-                          [bf[e][1] for e in experts], [amq] * k, [amsc] * k, [gs_a] * k,
-                          [np.float32(w.gs_h)] * k))
+    amq, amsc = X.nvfp4_to_mx(aq, asf)
+    assert np.array_equal(tp["a_q"], amq)
+    assert np.array_equal(tp["a_sf"], np.repeat(amsc, 2, axis=1))
+    print(f"[rows] mx {name}: re-encoded x bit-exact on all {T} tokens", flush=True)
+    _, rperm, rinv, _ = R.route(ids, w.E)
+    assert np.array_equal(tp["inv_perm"], rinv)
+    toks = _sample_tokens(name, ids)
     rw = ew_mx.rowmajor
-    acc = np.zeros(H)
-    tie = False
-    for j, (e, r) in enumerate(zip(experts, res)):
+    y_ref, same = {}, {}
+    n_h = n_y = 0
+    jobs = [(e, np.array(sorted(rows))) for e, rows in _token_rows(ids, rinv, k, toks).items()]
+
+    def check_weights(e, r):
         assert np.array_equal(host(rw["w1_q"][e]), r["w1_q"])
         assert np.array_equal(host(rw["w1_sf"][e]), np.repeat(r["w1_sc"], 2, axis=1))
-        d = int(tp["inv_perm"][t * k + j])
-        assert_close(tp["h_f32"][d:d + 1], r["h"], f"mx t={t} j={j} h")
-        # a requant decision within TAU of a rounding boundary may go either
-        # way; such rows are reported and kept out of the strict y/out bound
-        near = bool(Q.near_ties(r["h"], np.float32(w.gs_h), TAU)[0].any())
-        tie |= near
-        if not near:
-            assert_close(bf16_values(tp["y_bf16"][d:d + 1]), bf16_values(r["y"]), f"mx t={t} j={j} y")
-        acc += np.float64(tw[t, j]) * bf16_values(r["y"][0])
-    print(f"[case] mx {name} token {t}: near-tie rows present: {tie}", flush=True)
-    if not tie:
-        assert_close(bf16_values(host(out)[t]), bf16_values(O.round_to_bf16(acc)), f"mx t={t} out")
+        assert np.array_equal(host(rw["w2_q"][e]), r["w2_q"])
+
+    def worker_args(rows):
+        tok = rperm[rows] // k
+        return amq[tok], amsc[tok]
+
+    worker = functools.partial(oracle_pool.expert_rows_mx, gs_a=gs_a, gs_h=np.float32(w.gs_h))
+    for e, rows, r in _oracle_rows(w, ew_mx, jobs, worker, check_weights, worker_args):
+        n_h += rows.size
+        assert_close(tp["h_f32"][rows], r["h"], f"mx {name} h e={e}", log=False)
+        assert_mx_requant_matches(tp["h_q"][rows], tp["h_sf"][rows], r["h"], w.gs_h,
+                                  f"mx {name} requant e={e}")
+        ok = (tp["h_q"][rows] == r["h_q"]).all(axis=1) & \
+             (tp["h_sf"][rows] == np.repeat(r["h_sc"], 2, axis=1)).all(axis=1)
+        if ok.any():
+            assert_close(bf16_values(tp["y_bf16"][rows][ok]), bf16_values(r["y"][ok]),
+                         f"mx {name} y e={e}", log=False, bf16=True)
+        n_y += int(ok.sum())
+        for i, d in enumerate(rows):
+            y_ref[int(d)] = r["y"][i]
+            same[int(d)] = bool(ok[i])
+    n_out = _check_out(f"mx {name}", w, host(out), tw, rinv, y_ref, same, toks, k)
+    print(f"[rows] mx {name}: h on {n_h} rows, y on {n_y}, out on {n_out} tokens", flush=True)
+    assert n_h - n_y <= max(1, n_h // 100)
 
 
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["prefill", "skewed"])
-def test_shared_forward_sampled_token(name):
-    """The shared-expert forward at full size: one token's k routed rows plus
-    its shared-expert row, and its output, against the oracle."""
+def test_shared_forward_full_size(name):
+    """The shared-expert forward at full size: the shared expert's rows for
+    every 64th token and sampled tokens' routed rows, h / requant / y as in
+    the routed test, and the sampled tokens' outputs (k routed terms plus the
+    shared term)."""
     w = I.WORKLOADS[name]
-    print(f"[case] shared forward {name} (sampled token)", flush=True)
+    print(f"[case] shared forward {name} (full size)", flush=True)
     base = _big_weights(w)                                  # routed experts 0..E-1
     sw1, sw2 = I.make_expert_weights(w, w.E, DEV)          # the shared expert
     shared = nv.prepare_expert_weights([sw1[None]], [sw2[None]], DEV)
@@ -309,9 +476,12 @@ def test_shared_forward_sampled_token(name):
     x = I.make_x(w, DEV)
     ids, tw = I.make_routing(w)
     T, k, H, Iw = w.T, w.k, w.H, w.I
-    M = T * (k + 1)
+    K1 = k + 1
+    M = T * K1
     z = lambda shape, dt: torch.zeros(shape, dtype=dt, device=DEV)
-    taps = dict(inv_perm=z((M,), torch.int32), h_f32=z((M, Iw), torch.float32),
+    taps = dict(inv_perm=z((M,), torch.int32), perm=z((M,), torch.int32),
+                expert_offsets=z((w.E + 2,), torch.int32), h_f32=z((M, Iw), torch.float32),
+                h_q=z((M, Iw // 2), torch.uint8), h_sf=z((M, Iw // 16), torch.uint8),
                 y_bf16=z((M, H), torch.bfloat16))
     out = nv.moe_expert_forward_shared(x, torch.from_numpy(ids).to(DEV),
                                        torch.from_numpy(tw).to(DEV), both,
@@ -319,29 +489,34 @@ def test_shared_forward_sampled_token(name):
                                        taps=taps)
     torch.cuda.synchronize()
     tp = {n: host(t) for n, t in taps.items()}
-    xb = host(x)
-    gs_a = Q.global_scale(xb)
-    t = _sample_tokens(name, ids)[0] if name == "skewed" else T // 7
-    aq, asf = Q.quantize_blocks(xb[t:t + 1], gs_a)
-    aq = Q.pack_codes(aq)
-    experts = [int(e) for e in ids[t]] + [w.E]
-    bf = {e: tuple(host(a) for a in I.make_expert_weights(w, e, DEV)) for e in experts}
-    ctx = mp.get_context("spawn")
-    with cf.ProcessPoolExecutor(max_workers=len(experts), mp_context=ctx) as ex:
-        res = list(ex.map(oracle_pool.expert_rows, [bf[e][0] for e in experts],
-                          [bf[e][1] for e in experts], [aq] * (k + 1), [asf] * (k + 1),
-                          [gs_a] * (k + 1), [np.float32(w.gs_h)] * (k + 1)))
-    acc = np.zeros(H)
-    tie = False
-    for j, r in enumerate(res):
-        d = int(tp["inv_perm"][t * (k + 1) + j])
-        assert_close(tp["h_f32"][d:d + 1], r["h"], f"shared t={t} slot {j} h")
-        near = bool(Q.near_ties(r["h"], np.float32(w.gs_h), TAU)[0].any())
-        tie |= near
-        if not near:
-            assert_close(bf16_values(tp["y_bf16"][d:d + 1]), bf16_values(r["y"]), f"shared t={t} y {j}")
-        wj = np.float64(tw[t, j]) if j < k else 1.0
-        acc += wj * bf16_values(r["y"][0])
-    print(f"[case] shared {name} token {t}: near-tie rows present: {tie}", flush=True)
-    if not tie:
-        assert_close(bf16_values(host(out)[t]), bf16_values(O.round_to_bf16(acc)), f"shared t={t} out")
+    aq, asf, gs_a = _quantize_x(name, host(x))
+    # the routing with the shared slot appended: every token in expert E, last
+    ids2 = np.concatenate([ids, np.full((T, 1), w.E, np.int32)], axis=1)
+    roff, rperm, rinv, _ = R.route(ids2, w.E + 1)
+    assert np.array_equal(tp["expert_offsets"], roff)
+    assert np.array_equal(tp["perm"], rperm) and np.array_equal(tp["inv_perm"], rinv)
+    toks = _sample_tokens(name, ids)
+    extra = _token_rows(ids2, rinv, K1, toks)
+    extra.setdefault(w.E, []).extend(int(rinv[t * K1 + k]) for t in range(0, T, 64))
+    jobs = _jobs(roff, [], extra)
+
+    def check_weights(e, r):
+        src = rs if e == w.E else rw
+        ee = 0 if e == w.E else e
+        for n in ("w1_q", "w1_sf", "w2_q", "w2_sf"):
+            assert np.array_equal(host(src[n][ee]), r[n]), (n, e)
+
+    def worker_args(rows):
+        tok = rperm[rows] // K1
+        return aq[tok], asf[tok]
+
+    y_ref, same = {}, {}
+    n_h = n_y = 0
+    worker = functools.partial(oracle_pool.expert_rows, gs_a=gs_a, gs_h=np.float32(w.gs_h))
+    for e, rows, r in _oracle_rows(w, both, jobs, worker, check_weights, worker_args):
+        n_h += rows.size
+        n_y += _check_rows_nvfp4(f"shared {name}", w, tp, e, rows, r, y_ref, same)
+    twx = np.concatenate([tw, np.ones((T, 1), np.float32)], axis=1)
+    n_out = _check_out(f"shared {name}", w, host(out), twx, rinv, y_ref, same, toks, K1)
+    print(f"[rows] shared {name}: h on {n_h} rows, y on {n_y}, out on {n_out} tokens", flush=True)
+    assert n_h - n_y <= max(1, n_h // 100)

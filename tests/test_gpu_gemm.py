@@ -78,7 +78,7 @@ def test_grouped_bf16_epilogue(counts, N, K):
             continue
         ref = bf16_values(O.round_to_bf16(
             O.nvfp4_matmul(aq[rows[lo:hi]], asf[rows[lo:hi]], ga, bq[e], bsf[e], gb[e])))
-        assert_close(got[lo:hi], ref, f"expert {e}")
+        assert_close(got[lo:hi], ref, f"expert {e}", bf16=True)
 
 
 @pytest.mark.parametrize("counts,N,K", [
@@ -102,7 +102,7 @@ def test_grouped_bf16_split_k(counts, N, K):
             continue
         ref = bf16_values(O.round_to_bf16(
             O.nvfp4_matmul(aq[rows[lo:hi]], asf[rows[lo:hi]], ga, bq[e], bsf[e], gb[e])))
-        assert_close(got[lo:hi], ref, f"expert {e}")
+        assert_close(got[lo:hi], ref, f"expert {e}", bf16=True)
 
 
 @pytest.mark.parametrize("counts,N,K,gk,T", [
@@ -147,16 +147,22 @@ def test_dense_linear_config2_sampled_rows(split):
     torch.cuda.synchronize()
     ab, bb = host(a), host(b)
     gsa = Q.global_scale(ab)
-    rows = np.unique(np.concatenate([np.arange(0, M, 61), [M - 1]]))
-    aq, asf = Q.quantize_blocks(ab[rows], gsa)
+    # all of A and B bit-exact on the GPU
+    aq_all = np.empty((M, K // 2), np.uint8)
+    asf_all = np.empty((M, K // 16), np.uint8)
+    for r0 in range(0, M, 1024):
+        cq, cs = Q.quantize_blocks(ab[r0:r0 + 1024], gsa)
+        aq_all[r0:r0 + 1024], asf_all[r0:r0 + 1024] = Q.pack_codes(cq), cs
+    assert np.array_equal(host(a_q), aq_all) and np.array_equal(host(a_sf), asf_all)
     bq, bsf, gsb = Q.quantize_nvfp4(np.ascontiguousarray(bb.T))
-    # the sampled A rows and all of B are bit-exact on the GPU
-    assert np.array_equal(host(a_q)[rows], Q.pack_codes(aq))
-    assert np.array_equal(host(a_sf)[rows], asf)
     assert np.array_equal(host(b_q), bq) and np.array_equal(host(b_sf), bsf)
     assert host(gs_a)[0] == gsa and host(gs_b)[0] == gsb[0]
-    ref = bf16_values(O.dense_linear(Q.pack_codes(aq), asf, gsa, bq, bsf, gsb[0]))
-    assert_close(bf16_values(host(c))[rows], ref, "dense linear (sampled rows)")
+    # rows of every 128-row m tile (its first, last and a middle row) and
+    # every 61st row, all N columns (all n tiles)
+    mt = np.arange(0, M, 128)
+    rows = np.unique(np.concatenate([mt, mt + 127, mt + 53, np.arange(0, M, 61)]))
+    ref = bf16_values(O.dense_linear(aq_all[rows], asf_all[rows], gsa, bq, bsf, gsb[0]))
+    assert_close(bf16_values(host(c))[rows], ref, f"dense linear ({rows.size} rows, every m tile)", bf16=True)
 
 
 # 315 rows over 16 experts (<= 32 per expert on average: the 32-token tile
@@ -185,7 +191,7 @@ def test_small_expert_tiles(epi, K):
         if epi == "bf16":
             ref = bf16_values(O.round_to_bf16(
                 O.nvfp4_matmul(aq[rows[lo:hi]], asf[rows[lo:hi]], ga, bq[e], bsf[e], gb[e])))
-            assert_close(got[lo:hi], ref, f"expert {e}")
+            assert_close(got[lo:hi], ref, f"expert {e}", bf16=True)
         else:
             ref_h = O.l1_swiglu(aq[rows[lo:hi]], asf[rows[lo:hi]], ga, bq[e], bsf[e], gb[e])
             assert_close(gh[lo:hi], ref_h, f"h expert {e}")
@@ -213,4 +219,4 @@ def test_tile_configuration_limits(E, rows_per_expert):
             continue
         ref = bf16_values(O.round_to_bf16(
             O.nvfp4_matmul(aq[rows[lo:hi]], asf[rows[lo:hi]], ga, bq[e], bsf[e], gb[e])))
-        assert_close(got[lo:hi], ref, f"expert {e}")
+        assert_close(got[lo:hi], ref, f"expert {e}", bf16=True)

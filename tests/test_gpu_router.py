@@ -75,4 +75,4 @@ def test_router_feeds_the_forward():
     np.testing.assert_allclose(host(tw), rw, rtol=2e-6, atol=1e-7)
     ref = O.moe_forward(host(x), rid, rw.astype(np.float32), O.prepare_weights(host(w1), host(w2)),
                         np.float32(w.gs_h), w.E)
-    assert_close(bf16_values(host(out)), bf16_values(ref["out"]), "router -> forward out")
+    assert_close(bf16_values(host(out)), bf16_values(ref["out"]), "router -> forward out", bf16=True)

@@ -64,3 +64,27 @@ def test_floating_point_bar():
     bad[7] += 0.05 * np.sqrt(np.mean(ref ** 2))      # one element beyond 2e-2 * RMS
     with pytest.raises(AssertionError):
         assert_close(bad, ref, "one outlier")
+
+
+def test_bf16_step_allowance():
+    from parity import bf16_step
+    assert bf16_step(np.array([1.0, 1.5, 4.0, 7.9, 0.3]) ).tolist() == \
+        [2.0 ** -7, 2.0 ** -7, 2.0 ** -5, 2.0 ** -5, 2.0 ** -9]
+    ref = np.random.default_rng(5).standard_normal(4000)
+    ref[10] = 6.0                                     # above 5 * RMS: one step is 2^-5
+    gpu = ref.copy()
+    gpu[10] += 2.0 ** -5                              # one BF16 step apart
+    with pytest.raises(AssertionError):
+        assert_close(gpu, ref, "strict")
+    assert_close(gpu, ref, "one step", bf16=True)
+    gpu[10] += 2.0 ** -5                              # two steps: not excused
+    with pytest.raises(AssertionError):
+        assert_close(gpu, ref, "two steps", bf16=True)
+    many = np.random.default_rng(6).standard_normal(4000)
+    many[:20] = 6.0
+    shifted = many.copy()
+    shifted[:20] += 2.0 ** -5                         # 20 of 4000 one step apart (0.5%)
+    with pytest.raises(AssertionError, match="elements above the bound"):
+        assert_close(shifted, many, "many", bf16=True)
+    shifted[2:20] = many[2:20]                        # 2 of 4000 (0.05%): excused
+    assert_close(shifted, many, "few", bf16=True)
