@@ -380,6 +380,35 @@ nvfp4_status moe_expert_forward_mx(const void* x_bf16, int64_t T, int64_t H, int
                                    const float* gs_h, void* out_bf16, const nvfp4_moe_taps* taps,
                                    void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * The expert forward without a caller workspace.
+ * For callers that cannot allocate device memory: code under hipGraph
+ * capture, tight serving loops, harnesses that forbid allocation.
+ *
+ * Same arguments (without ws / ws_bytes), steps, taps, results and error
+ * behaviour as moe_expert_forward.  Its workspace is a static device array
+ * of NVFP4_NOALLOC_SCRATCH_BYTES that each GPU the library runs on holds
+ * until the process ends; the call allocates and frees nothing (its first
+ * call on a device looks up the array's address on that device).
+ * Requires moe_expert_forward_workspace_size(T, H, I, E, k) <=
+ *   NVFP4_NOALLOC_SCRATCH_BYTES (at H = 7168, I = 2048, k = 8 that is
+ *   T <= 524), else NVFP4_ERR_WORKSPACE and nothing is enqueued.
+ * All calls on one GPU share its array, which keeps the last call's
+ * contents (nothing in it needs to start at zero: every region is written
+ * before it is read, and the GEMMs' tile counters are cleared by a kernel on
+ * each launch).  Calls ordered on one stream are safe; calls that overlap on
+ * one GPU (unordered streams, several host threads) race on the array and
+ * give wrong results.
+ * ---------------------------------------------------------------------- */
+#define NVFP4_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+nvfp4_status moe_expert_forward_noalloc(const void* x_bf16, int64_t T, int64_t H, int64_t I, int E,
+                                        int k, const int32_t* topk_ids, const float* topk_w,
+                                        const uint8_t* w1_q, const uint8_t* w1_sf,
+                                        const float* gs_w1, const uint8_t* w2_q,
+                                        const uint8_t* w2_sf, const float* gs_w2,
+                                        const float* gs_h, void* out_bf16,
+                                        const nvfp4_moe_taps* taps, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

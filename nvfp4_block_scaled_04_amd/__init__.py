@@ -8,7 +8,7 @@ seeded synthetic workloads.
 
 from .binding import (  # noqa: F401
     EPI_BF16, EPI_SWIGLU_NVFP4, ExpertWeights, Nvfp4Error, PackedWeight, Taps, forward_workspace,
-    forward_shared_workspace, moe_expert_forward_shared,
+    forward_shared_workspace, moe_expert_forward_shared, moe_expert_forward_noalloc,
     gemm_splitk_workspace_bytes, gemm_workspace_bytes,
     grouped_gemm, lib, moe_combine, moe_expert_forward, moe_route, mx_expert_weights, pack_weights,
     prepare_expert_weights, quantize, quantize_scatter, router_topk, to_mx, weight_layout,

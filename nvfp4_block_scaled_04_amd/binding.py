@@ -63,6 +63,7 @@ SIGNATURES["nvfp4_mx_grouped_gemm"] = SIGNATURES["nvfp4_grouped_gemm"]
 SIGNATURES["moe_expert_forward_mx"] = SIGNATURES["moe_expert_forward"]
 SIGNATURES["moe_expert_forward_shared"] = SIGNATURES["moe_expert_forward"]
 SIGNATURES["moe_expert_forward_shared_workspace_size"] = SIGNATURES["moe_expert_forward_workspace_size"]
+SIGNATURES["moe_expert_forward_noalloc"] = (c_int, SIGNATURES["moe_expert_forward"][1][:17] + [c_void_p])
 
 
 class Taps(ctypes.Structure):
@@ -380,6 +381,33 @@ def moe_expert_forward(x, topk_ids, topk_w, w: ExpertWeights, gs_h, out=None, ta
               ctypes.byref(tp) if tp is not None else None, _ptr(ws), ws.numel(), _stream(dev)),
            "moe_expert_forward_mx" if w.mx else "moe_expert_forward")
     return o
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20      # NVFP4_NOALLOC_SCRATCH_BYTES
+
+
+def moe_expert_forward_noalloc(x, topk_ids, topk_w, w: ExpertWeights, gs_h, out, taps=None):
+    """The expert forward on the library's static scratch (no workspace and
+    no allocation: the caller passes the output)."""
+    _dev(x, torch.bfloat16, "x")
+    T, H = x.shape
+    E, I = w.E, w.I
+    k = topk_ids.shape[1]
+    _dev(topk_ids, torch.int32, "topk_ids", (T, k))
+    _dev(topk_w, torch.float32, "topk_w", (T, k))
+    if w.mx or w.H != H or w.w2.N != H or w.w2.K != I or w.w2.E != E:
+        raise ValueError("NVFP4 weights matching x expected")
+    _dev(w.gs_w1, torch.float32, "gs_w1", (E,))
+    _dev(w.gs_w2, torch.float32, "gs_w2", (E,))
+    _dev(gs_h, torch.float32, "gs_h", (1,))
+    _dev(out, torch.bfloat16, "out", (T, H))
+    tp = Taps(**{name: t.data_ptr() for name, t in taps.items()}) if taps else None
+    _check(lib().moe_expert_forward_noalloc(
+        _ptr(x), T, H, I, E, k, _ptr(topk_ids), _ptr(topk_w), _ptr(w.w1.q), _ptr(w.w1.sf),
+        _ptr(w.gs_w1), _ptr(w.w2.q), _ptr(w.w2.sf), _ptr(w.gs_w2), _ptr(gs_h), _ptr(out),
+        ctypes.byref(tp) if tp is not None else None, _stream(x.device)),
+        "moe_expert_forward_noalloc")
+    return out
 
 
 def forward_shared_workspace(T, H, I, E, k, device):

@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "nvfp4moe.h"
@@ -565,3 +566,67 @@ nvfp4_status moe_expert_forward_mx(const void* x_bf16, int64_t T, int64_t H, int
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------- without a workspace
+//
+// The forward's workspace for callers that cannot allocate device memory: a
+// file-scope device array, one copy per GPU, held until the process ends.  In
+// host code the name `scratch` stands for the host-side shadow of the symbol,
+// not a device address: every use goes through the address that
+// hipGetSymbolAddress returns on the device in question, cached per device.
+namespace {
+
+static __device__ __align__(256) uint8_t scratch[NVFP4_NOALLOC_SCRATCH_BYTES];
+
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// device address of this device's `scratch` (looked up once per device, with
+// that device current)
+nvfp4_status scratch_address(void** out) {
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return hip_fail(err, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(NVFP4_ERR_ARCH, "device index %d out of range", dev);
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+      err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (err != hipSuccess) return hip_fail(err, "hipGetSymbolAddress(scratch)");
+      if (p == nullptr || !aligned(p, 256))
+        return fail(NVFP4_ERR_HIP, "the scratch array has no 256-byte aligned device address");
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return NVFP4_OK;
+}
+
+}  // namespace
+
+extern "C" nvfp4_status moe_expert_forward_noalloc(
+    const void* x_bf16, int64_t T, int64_t H, int64_t I, int E, int k, const int32_t* topk_ids,
+    const float* topk_w, const uint8_t* w1_q, const uint8_t* w1_sf, const float* gs_w1,
+    const uint8_t* w2_q, const uint8_t* w2_sf, const float* gs_w2, const float* gs_h,
+    void* out_bf16, const nvfp4_moe_taps* taps, void* stream) {
+  const size_t need = moe_expert_forward_workspace_size(T, H, I, E, k);
+  if (need > NVFP4_NOALLOC_SCRATCH_BYTES)
+    return fail(NVFP4_ERR_WORKSPACE,
+                "moe_expert_forward_noalloc: this shape needs %zu workspace bytes, the static "
+                "scratch holds %zu; call moe_expert_forward with a workspace",
+                need, (size_t)NVFP4_NOALLOC_SCRATCH_BYTES);
+  // every argument check of the forward first, with a stand-in workspace
+  // address that is never dereferenced (nothing is enqueued)
+  void* const stand_in = reinterpret_cast<void*>(uintptr_t(256));
+  nvfp4_status st = forward_impl(0, x_bf16, T, H, I, E, k, topk_ids, topk_w, w1_q, w1_sf, gs_w1,
+                                 w2_q, w2_sf, gs_w2, gs_h, out_bf16, taps, stand_in,
+                                 NVFP4_NOALLOC_SCRATCH_BYTES, nullptr, /*check_only=*/true);
+  if (st != NVFP4_OK) return st;
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != NVFP4_OK) return st;
+  return forward_impl(0, x_bf16, T, H, I, E, k, topk_ids, topk_w, w1_q, w1_sf, gs_w1, w2_q, w2_sf,
+                      gs_w2, gs_h, out_bf16, taps, ws, NVFP4_NOALLOC_SCRATCH_BYTES, stream);
+}

@@ -211,3 +211,15 @@ def test_quantize_scatter_rejects(L):
     assert f(wsb=0) == -3
     assert L.nvfp4_quantize_scatter_workspace_size(0, 256) == 0
     assert L.nvfp4_quantize_scatter_workspace_size(8192, 7168) >= 4
+
+
+def test_noalloc_forward_rejects_before_touching_the_device(L):
+    f = lambda **kw: L.moe_expert_forward_noalloc(
+        FAKE, kw.get("T", 4), kw.get("H", 256), kw.get("I", 128), 4, kw.get("k", 2), FAKE, FAKE,
+        FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, kw.get("gs_h", FAKE), FAKE, None, None)
+    # a shape whose workspace exceeds the static scratch
+    assert L.moe_expert_forward_workspace_size(600, 7168, 2048, 4, 8) > (64 << 20)
+    assert f(T=600, H=7168, I=2048, k=8) == -3
+    assert b"static scratch" in L.nvfp4_last_error()
+    assert f(H=200) == -2
+    assert f(gs_h=None) == -1
