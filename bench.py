@@ -21,6 +21,7 @@ import argparse
 import json
 import os
 import sys
+import threading
 import time
 
 import numpy as np
@@ -98,6 +99,85 @@ class Events:
         return self.s.elapsed_time(self.e)
 
 
+PEAK_CLOCK_MHZ = 2400.0             # the clock the published peaks are quoted at
+
+
+class SmuSampler:
+    """GFX clock (MHz) and socket power (W) from the SMU metrics table (via
+    amdsmi), read every ~10 ms on a host thread while a measured region runs.
+    The chip runs its power-limited clock under these kernels, so a fraction
+    of the 2.4 GHz peak is reported together with the clock it ran at."""
+
+    def __init__(self):
+        self.h = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            handles = amdsmi.amdsmi_get_processor_handles()
+            self.amdsmi = amdsmi
+            if len(handles) == 1:
+                self.h = handles[0]
+            else:
+                bus = torch.cuda.get_device_properties(0).pci_bus_id
+                for h in handles:
+                    bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)
+                    if int(bdf.split(":")[1], 16) == bus:
+                        self.h = h
+        except Exception:
+            self.h = None
+        self.samples = []
+        self._stop = threading.Event()
+        self._thread = None
+
+    def power_cap_w(self):
+        try:
+            return self.amdsmi.amdsmi_get_power_cap_info(self.h)["power_cap"] / 1e6
+        except Exception:
+            return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                m = self.amdsmi.amdsmi_get_gpu_metrics_info(self.h)
+                clk, pw = m.get("current_gfxclk"), m.get("current_socket_power")
+                if isinstance(clk, (int, float)) and 0 < clk < 10000 and isinstance(pw, (int, float)):
+                    self.samples.append((float(clk), float(pw)))
+            except Exception:
+                pass
+            time.sleep(0.01)
+
+    def __enter__(self):
+        self.samples = []
+        if self.h is not None:
+            self._stop.clear()
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+        return self
+
+    def __exit__(self, *a):
+        if self._thread is not None:
+            self._stop.set()
+            self._thread.join()
+            self._thread = None
+
+    def summary(self):
+        if not self.samples:
+            return None
+        c = np.array(self.samples)
+        return {"gfxclk_mhz": round(float(c[:, 0].mean()), 1),
+                "socket_power_w": round(float(c[:, 1].mean()), 1), "samples": int(len(c))}
+
+
+SMU = None
+
+
+def smu():
+    global SMU
+    if SMU is None:
+        SMU = SmuSampler()
+    return SMU
+
+
 def nvfp4_bytes(rows, cols):
     """Codes + E4M3 scales of an NVFP4 (rows, cols) tensor."""
     return rows * cols * 0.5625
@@ -122,15 +202,23 @@ def timed_steps(fn, steps):
     return mean, pct
 
 
-def roofline(kernel, flops, nbytes, ms, traffic=None, peak=FP16_MFMA_PEAK_TFLOPS):
+def roofline(kernel, flops, nbytes, ms, traffic=None, peak=FP16_MFMA_PEAK_TFLOPS, clock=None):
     """Roofline object for one kernel: MFMA-bound (against the MFMA peak of
     its operand dtype) when its arithmetic intensity is above that ridge,
-    else HBM-bound."""
+    else HBM-bound.  clock: SMU summary of the kernel's timing loop; the
+    MFMA peak scales with the GFX clock, so the fraction of the peak at the
+    clock the chip sustained is reported beside the fraction of the 2.4 GHz
+    figure."""
     if flops / max(nbytes, 1.0) >= peak * 1e12 / (HBM_PEAK_GBS * 1e9):
         a = flops / (ms * 1e-3) / 1e12
-        return {"kernel": kernel, "bound": "mfma", "achieved": round(a, 2),
-                "peak": peak, "unit": "TFLOP/s",
-                "frac": round(a / peak, 4), "traffic": traffic}
+        r = {"kernel": kernel, "bound": "mfma", "achieved": round(a, 2),
+             "peak": peak, "unit": "TFLOP/s",
+             "frac": round(a / peak, 4), "traffic": traffic, "ms": round(ms, 4)}
+        if clock:
+            r.update(gfxclk_mhz=clock["gfxclk_mhz"], socket_power_w=clock["socket_power_w"],
+                     peak_at_clock=round(peak * clock["gfxclk_mhz"] / PEAK_CLOCK_MHZ, 1),
+                     frac_at_clock=round(a / (peak * clock["gfxclk_mhz"] / PEAK_CLOCK_MHZ), 4))
+        return r
     a = nbytes / (ms * 1e-3) / 1e9
     return {"kernel": kernel, "bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(a / HBM_PEAK_GBS, 4), "traffic": traffic}
@@ -143,6 +231,41 @@ def time_loop(fn, steps):
         for _ in range(steps):
             fn()
     return ev.ms() / steps
+
+
+def sustained(fn, secs=2.0, settle=0.8):
+    """Run fn back to back for `secs` seconds and return (ms per call over
+    the whole loop by HIP events, SMU summary over the part after `settle`
+    seconds).  The SMU metrics table lags the workload by a few hundred
+    milliseconds, so the clock and power of a kernel are read from a loop
+    of this length rather than from the short timed regions."""
+    torch.cuda.synchronize()
+    smp = smu()
+    samples0 = len(smp.samples)
+    with smp:
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(torch.cuda.current_stream())
+        n = 0
+        t_settle = None
+        while time.perf_counter() - t0 < secs:
+            fn()
+            n += 1
+            if n % 4 == 0:
+                torch.cuda.synchronize()
+                if t_settle is None and time.perf_counter() - t0 >= settle:
+                    t_settle = len(smp.samples)
+        e1.record(torch.cuda.current_stream())
+        e1.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    keep = smp.samples[t_settle:] if t_settle is not None else []
+    if not keep:
+        return ms, None
+    c = np.array(keep)
+    return ms, {"gfxclk_mhz": round(float(c[:, 0].mean()), 1),
+                "socket_power_w": round(float(c[:, 1].mean()), 1), "samples": int(len(c)),
+                "loop_ms": round(ms, 4), "loop_s": secs}
 
 
 def bench_shared(w, steps, warmup, dev):
@@ -186,6 +309,8 @@ def bench_moe(w, steps, warmup, dev, mx=False):
         step()
     ms_step, pct = timed_steps(step, steps)
     log(f"[bench] forward {ms_step:.3f} ms/step (p10/p50/p90 {pct['p10']}/{pct['p50']}/{pct['p90']})")
+    step_clk = sustained(step)[1]
+    log(f"[bench] forward sustained SMU reading: {step_clk}")
 
     # ---- each step alone, same kernels and arguments, events on the stream
     T, H, Iw, E, k = w.T, w.H, w.I, w.E, w.k
@@ -229,6 +354,9 @@ def bench_moe(w, steps, warmup, dev, mx=False):
     for name, fn in stages.items():
         fn()
         st_ms[name] = time_loop(fn, steps)
+    # sustained loops for the clock and power the two GEMMs run at
+    st_clk = {n: sustained(stages[n])[1] for n in ("l1_gemm_swiglu_requant", "l2_gemm")}
+    log(f"[bench] sustained SMU readings: {st_clk}")
     log("[bench] stages (ms): " + ", ".join(f"{n}={v:.4f}" for n, v in st_ms.items()))
     # the step before the path (not in the timed forward, which takes ids and
     # weights): router top-k + softmax on N(0,1) logits of this shape
@@ -253,13 +381,15 @@ def bench_moe(w, steps, warmup, dev, mx=False):
                     l1_flops, l1_bytes, st_ms["l1_gemm_swiglu_requant"],
                     TRAFFIC.get((w.name, "l1", "mx" if mx else "nvfp4"))
                     if TRAFFIC_SRC_SHA == gemm_src_sha() else None,
-                    peak=peak)
+                    peak=peak, clock=st_clk["l1_gemm_swiglu_requant"])
     extra = {
         "ms_percentiles": pct,
         "live_experts": n_live,
         "weight_stream_gbs": (w1_bytes + w2_bytes) / (ms_step * 1e-3) / 1e9,
         "l2_roofline": roofline("grouped_gemm_kernel<BF16 epilogue> (L2)" + (" MX" if mx else ""),
-                                l2_flops, l2_bytes, st_ms["l2_gemm"], peak=peak),
+                                l2_flops, l2_bytes, st_ms["l2_gemm"], peak=peak,
+                                clock=st_clk["l2_gemm"]),
+        "step_clock": step_clk,
         "tokens_per_s": T / (ms_step * 1e-3),
         "l2_gemm_tflops": l2_flops / (st_ms["l2_gemm"] * 1e-3) / 1e12,
         "quantize_gbs": (2 * T * H + 0.5625 * T * H) / (st_ms["quantize"] * 1e-3) / 1e9,
@@ -312,13 +442,14 @@ def bench_dense(w, steps, warmup, dev, mx=False):
         step()
     ms_step, pct = timed_steps(step, steps)
     st_ms = {"quantize": time_loop(quant, steps), "gemm": time_loop(gemm, steps)}
+    gemm_clk = sustained(gemm)[1]
     log(f"[bench] dense step {ms_step:.4f} ms; stages (ms): " +
         ", ".join(f"{n}={v:.4f}" for n, v in st_ms.items()))
     flops = 2.0 * M * N * K
     nbytes = nvfp4_bytes(M, K) + nvfp4_bytes(N, K) + 2.0 * M * N
     roof = roofline("grouped_gemm_kernel<BF16 epilogue> (dense)" + (" MX" if mx else ""), flops,
                     nbytes, st_ms["gemm"],
-                    peak=FP4_MFMA_PEAK_TFLOPS if mx else FP16_MFMA_PEAK_TFLOPS)
+                    peak=FP4_MFMA_PEAK_TFLOPS if mx else FP16_MFMA_PEAK_TFLOPS, clock=gemm_clk)
     extra = {"ms_percentiles": pct, "stages_ms": {n: round(v, 4) for n, v in st_ms.items()},
              "gemm_tflops": round(flops / (st_ms["gemm"] * 1e-3) / 1e12, 2),
              "split_k": gws.numel() > nv.gemm_workspace_bytes(),
@@ -466,6 +597,10 @@ def main():
         "ms_percentiles": extra["ms_percentiles"],
         "roofline": roof,
         "l2_roofline": extra["l2_roofline"],
+        "clock": dict(extra["step_clock"], power_cap_w=smu().power_cap_w(),
+                      source="SMU gpu_metrics (amdsmi) every 10 ms over a 2 s loop of the step, "
+                             "after 0.8 s")
+        if extra["step_clock"] else None,
         "stages_ms": extra["stages_ms"],
         "router_topk_ms": extra["router_topk_ms"],
         "l2_gemm_tflops": round(extra["l2_gemm_tflops"], 2),

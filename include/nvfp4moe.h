@@ -216,9 +216,13 @@ nvfp4_status nvfp4_quantize_scatter(const void* x_bf16, int64_t T, int64_t H, in
  *   zeroes them (a small kernel on `stream`), so the contents need no
  *   set-up; calls that share a workspace must be ordered on one stream.  May
  *   be NULL only when M == 0.
- * Split K (BF16 epilogue only): when the launch has too few tiles to occupy
- *   the device (at most half as many as it has CUs, e.g. a dense linear of
- *   a few thousand rows) and ws_bytes >= nvfp4_grouped_gemm_splitk_workspace_size
+ * Tiles: 512 weight rows x 128 token rows; 32-token tiles when the experts
+ *   average at most 32 rows (decode-sized batches); 64-token tiles for a
+ *   BF16-epilogue launch whose 128-token tiles would leave half the CUs idle
+ *   (a dense linear of a few thousand rows).
+ * Split K (BF16 epilogue only): when even 64-token tiles leave half the CUs
+ *   idle (e.g. a dense linear of about a thousand rows) and
+ *   ws_bytes >= nvfp4_grouped_gemm_splitk_workspace_size
  *   (same epilogue, M, N, K, E; current device), each tile's K range is cut
  *   into up to 4 parts whose fp32 partial sums (scaled by the global scales)
  *   go to the workspace; a second kernel on `stream` sums them in part order

@@ -170,6 +170,10 @@ struct Cfg {
   // (two loads fill a wave's 8 of the 32 rows), and its one token scale load
   // brings all 32 rows' scales (every wave writes the same 256 bytes)
   static constexpr bool SMALL = BM == 32;
+  // tiles of fewer than 32 token rows per wave (32- and 64-token tiles): every
+  // wave loads all of the tile's token scales, 32 rows per 4-byte load, and
+  // the waves write the same LDS bytes
+  static constexpr bool TSF_SHARED = BM < 32 * NW;
   static constexpr int MAX_E = SMALL ? 1024 : 4096;    // expert prefix kept in LDS
   static constexpr int NBUF = SMALL ? 4 : 3;           // LDS stage buffers
   static constexpr int AHEAD = NBUF - 1;               // stages loaded ahead of use
@@ -179,13 +183,14 @@ struct Cfg {
   static constexpr int CODE_LOADS_W = BN / 16 / NW;    // weight-row code loads
   static constexpr int CODE_LOADS = SMALL ? CODE_LOADS_W + 2 : ROWS / 16 / NW;
   static constexpr int SF_LOADS_W = BN / 128 / NW;
-  static constexpr int SF_LOADS_T = SMALL ? 1 : BM / 32 / NW;
+  static constexpr int SF_LOADS_T = TSF_SHARED ? BM / 32 : BM / 32 / NW;
   static constexpr int SF_LOADS = SF_LOADS_W + SF_LOADS_T;
   static constexpr int LOADS = CODE_LOADS + SF_LOADS;
   static_assert(TN % 32 == 0 && TM % 32 == 0, "wave tile must be a multiple of 32");
   static_assert(BN % (16 * NW) == 0 && (SMALL ? NW == 4 : ROWS % (16 * NW) == 0),
                 "code loads must divide evenly");
-  static_assert(BN % (128 * NW) == 0 && (SMALL || BM % (32 * NW) == 0), "scale loads must divide evenly");
+  static_assert(BN % (128 * NW) == 0 && (TSF_SHARED || BM % (32 * NW) == 0), "scale loads must divide evenly");
+  static_assert(CODE_LOADS + SF_LOADS_W + SF_LOADS_T == 12, "the vmcnt bookkeeping assumes 12 loads per stage");
   static_assert(BN == NVFP4_PACK_ROWS && BK == NVFP4_PACK_K, "tiles follow the packed weight layout");
   static_assert(WM == 1, "column-block skipping assumes one wave row");
 };
@@ -231,7 +236,7 @@ __device__ __forceinline__ void stage_barrier() {
 #define NVFP4_LOAD_CONSTS                                                                       \
   constexpr int kNW = C::NW, kCodeLoads = C::CODE_LOADS, kCodeLoadsW = C::CODE_LOADS_W;         \
   constexpr int kSfLoads = C::SF_LOADS, kSfLoadsW = C::SF_LOADS_W, kCodeBytes = C::CODE_BYTES;  \
-  constexpr bool kSmall = C::SMALL;                                                             \
+  constexpr bool kSmall = C::SMALL, kTsfShared = C::TSF_SHARED;                                \
   constexpr int kWPol = C::SMALL ? 2 : 0
 #define NVFP4_ISSUE(ks, dst, part)                                                              \
   do {                                                                                          \
@@ -255,9 +260,10 @@ __device__ __forceinline__ void stage_barrier() {
         if (c < kSfLoadsW)                                                                      \
           __builtin_amdgcn_global_load_lds(wsf + soff[c] + (uint32_t)(ks) * (BN * SF_BYTES),    \
                                            sbw + kCodeBytes + (c * kNW + wave) * 1024, 16, 0, kWPol); \
-        else if (kSmall)                                                                        \
+        else if (kTsfShared)                                                                    \
           __builtin_amdgcn_global_load_lds(asf + soff[c] + (uint32_t)(ks) * SF_BYTES,           \
-                                           sbw + kCodeBytes + BN * SF_BYTES, 4, 0, 0);          \
+                                           sbw + kCodeBytes + BN * SF_BYTES +                   \
+                                               (c - kSfLoadsW) * 256, 4, 0, 0);                 \
         else                                                                                    \
           __builtin_amdgcn_global_load_lds(asf + soff[c] + (uint32_t)(ks) * SF_BYTES,           \
                                            sbw + kCodeBytes + BN * SF_BYTES +                   \
@@ -531,6 +537,18 @@ struct Tile {
   int split, ks_lo, nks;   // K range [ks_lo, ks_lo + nks) in stages
 };
 
+// Wave-uniform read of a device array through the constant address space: a
+// scalar load, counted by lgkmcnt.  A vector load here would be counted by
+// vmcnt, which completes in order, so the compiler's wait for it would also
+// wait for every direct load issued before it (the next tile's first
+// stages).  Only for arrays the kernel never writes.
+__device__ __forceinline__ float uniform_load(const float* p, int i) {
+  return ((const __attribute__((address_space(4))) float*)p)[i];
+}
+__device__ __forceinline__ int uniform_load(const int32_t* p, int i) {
+  return ((const __attribute__((address_space(4))) int32_t*)p)[i];
+}
+
 // Tile number `logical` (< number of tiles) of the expert-ordered tile list
 // (per expert: n tiles, and inside each n tile the expert's m tiles of BM
 // rows, so the tiles that read one weight n tile are neighbours in the list
@@ -558,13 +576,14 @@ __device__ __forceinline__ void tile_at(const Params& p, const int* tprefix, int
   // BM/32 each, the larger shares first): with 9 blocks the tiles take 3, 3, 3
   // rather than 4, 4, 1, since a one-block tile decodes the whole weight
   // tile for a quarter of the MFMAs and is VALU-bound.
-  const int rows_e = p.offsets[t.e + 1] - p.offsets[t.e];
+  const int off_e = uniform_load(p.offsets, t.e), off_e1 = uniform_load(p.offsets, t.e + 1);
+  const int rows_e = off_e1 - off_e;
   const int nblk = (rows_e + 31) / 32;
   const int per = nblk / mcount, rem = nblk - per * mcount;
   const int blk0 = mt * per + min(mt, rem);
   const int nblk_t = per + (mt < rem ? 1 : 0);
-  t.row0 = __builtin_amdgcn_readfirstlane(p.offsets[t.e] + 32 * blk0);
-  t.nrows = __builtin_amdgcn_readfirstlane(min(32 * nblk_t, p.offsets[t.e + 1] - t.row0));
+  t.row0 = __builtin_amdgcn_readfirstlane(off_e + 32 * blk0);
+  t.nrows = __builtin_amdgcn_readfirstlane(min(32 * nblk_t, off_e1 - t.row0));
   t.n0 = (int64_t)__builtin_amdgcn_readfirstlane(nt) * BN;
   t.jv = (t.nrows + 31) / 32;
   t.split = __builtin_amdgcn_readfirstlane(split);
@@ -676,8 +695,58 @@ __device__ __forceinline__ void tile_offsets(const Params& p, const Tile& t, int
   }
 #pragma unroll
   for (int c = 0; c < C::SF_LOADS_T; ++c) {      // one 4-byte half row per lane
-    const int i = C::SMALL ? (lane >> 1) : 32 * (c * C::NW + wave) + (lane >> 1);
+    const int i = C::TSF_SHARED ? 32 * c + (lane >> 1) : 32 * (c * C::NW + wave) + (lane >> 1);
     soff[C::SF_LOADS_W + c] = trow(i) * ksf + 4 * (lane & 1);
+  }
+}
+
+// BF16 epilogue through LDS.  In the accumulator layout a lane holds one
+// token row (l32) and 16 of the wave's N columns in four 8-byte pieces, so a
+// direct store instruction writes 8-byte pieces of 32 different rows: 32
+// partially written cache lines per instruction, and the address unit's time
+// per line made these stores a tenth of the L2 GEMM.  Instead each 32-token
+// column block is scaled, converted and written to a wave-private LDS region
+// as 32 rows of the wave's TN columns, read back 16 bytes per lane along the
+// rows and stored as whole row segments (a store instruction covers 4 rows of
+// 2*TN contiguous bytes).  The region lies in the last stage buffer, which no
+// load of the next tile targets before that tile's first stage barrier, so
+// no block synchronisation is needed; rows past the tile's rows and columns
+// past N are written to LDS but never stored.
+constexpr int kEpiStride = 2 * 128 + 8;          // LDS bytes per staged row (TN = 128, 8 bytes pad)
+constexpr int kEpiWaveBytes = 32 * kEpiStride;   // one 32-token column block of a wave
+
+template <int TN, int FN, int FM, int JV>
+__device__ __forceinline__ void epilogue_bf16(const Params& p, float16v (&acc)[FN][FM],
+                                              float alpha, int row0, int nrows, int64_t nw0,
+                                              int lane, uint8_t* __restrict__ ep) {
+  static_assert(TN == 128 && FN == 4, "staging layout assumes a 128-column wave tile");
+  const int hf = lane >> 5, l32 = lane & 31;
+  const int64_t N = p.N;
+  const int rr = lane >> 4, ch = lane & 15;      // read-back: row (of 4) and 16-byte chunk
+  const bool col_ok = nw0 + 8 * ch < N;
+#pragma unroll
+  for (int j = 0; j < JV; ++j) {
+#pragma unroll
+    for (int i = 0; i < FN; ++i) {
+      // one 32 x 32 block at a time: the scheduler would otherwise copy all
+      // accumulators out of the AGPRs at once and spill
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        uint2 o;
+        o.x = pack_bf16x2(acc[i][j][4 * g + 0] * alpha, acc[i][j][4 * g + 1] * alpha);
+        o.y = pack_bf16x2(acc[i][j][4 * g + 2] * alpha, acc[i][j][4 * g + 3] * alpha);
+        *reinterpret_cast<uint2*>(ep + l32 * kEpiStride + 2 * (i * 32 + 8 * g + 4 * hf)) = o;
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int tok = j * 32 + 4 * it + rr;
+      const uint4 v = *reinterpret_cast<const uint4*>(ep + (4 * it + rr) * kEpiStride + 16 * ch);
+      if (tok < nrows && col_ok)
+        *reinterpret_cast<uint4*>(p.c_bf16 + (int64_t)(row0 + tok) * N + nw0 + 8 * ch) = v;
+    }
   }
 }
 
@@ -795,7 +864,8 @@ __device__ __forceinline__ bool run_tile(const Params& p, uint8_t* smem, const i
   }
 
   // ---- epilogue
-  const float alpha = 1.0f / (p.gs_a[0] * p.gs_b[e]);
+  const float alpha = 1.0f / (uniform_load(p.gs_a, 0) *
+                               uniform_load(p.gs_b, __builtin_amdgcn_readfirstlane(e)));
   if constexpr (EPI == kEpiPartial) {
     // fp32 partial sums of this K range: the lane's 4 contiguous columns of
     // each (i, g) as one 16-byte store; summed by splitk_reduce_kernel
@@ -816,33 +886,11 @@ __device__ __forceinline__ bool run_tile(const Params& p, uint8_t* smem, const i
       }
     }
   } else if constexpr (EPI == NVFP4_EPI_BF16) {
-    // Each lane holds, for token j*32 + l32, output columns 32i + 8g + 4hf
-    // .. +3 of the wave's TN: 8 contiguous bytes per (i, g).  The two lane
-    // halves write 16 contiguous bytes of a token row per store and the four
-    // g stores its 64 bytes of block i, which L2 merges before write-back.
-    // No LDS: buffers 0 and 1 may be receiving the next tile.
-    const int64_t nw0 = n0 + wn * TN;
-#pragma unroll
-    for (int j = 0; j < JV; ++j) {
-      const int tok = j * 32 + l32;
-      uint16_t* crow = p.c_bf16 + (int64_t)(row0 + tok) * N + nw0 + 4 * hf;
-#pragma unroll
-      for (int i = 0; i < FN; ++i) {
-        // one 32 x 32 block at a time: the scheduler would otherwise copy
-        // all accumulators out of the AGPRs at once and spill
-        __builtin_amdgcn_sched_barrier(0);
-        if (tok >= nrows || nw0 + i * 32 >= N) continue;   // N % 32 == 0
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          uint2 o;
-          o.x = pack_bf16x2(acc[i][j][4 * g + 0] * alpha, acc[i][j][4 * g + 1] * alpha);
-          o.y = pack_bf16x2(acc[i][j][4 * g + 2] * alpha, acc[i][j][4 * g + 3] * alpha);
-          *reinterpret_cast<uint2*>(crow + i * 32 + 8 * g) = o;
-        }
-      }
-    }
+    static_assert(C::NW * kEpiWaveBytes <= C::STAGE_BYTES, "staged epilogue must fit a stage buffer");
+    epilogue_bf16<C::TN, FN, FM, JV>(p, acc, alpha, row0, nrows, n0 + wn * TN, lane,
+                                 smem + (C::NBUF - 1) * C::STAGE_BYTES + wave * kEpiWaveBytes);
   } else {
-    const float gs_h = p.gs_out[0];
+    const float gs_h = uniform_load(p.gs_out, 0);
     const int64_t I = N / 2;
 #pragma unroll
     for (int i = 0; i < FN; ++i) {
@@ -1029,6 +1077,7 @@ hipError_t device_cus(int& cus) {
 
 constexpr int kBN = 512, kBM = 128;   // the tile of every launch but small experts
 constexpr int kBMSmall = 32;          // experts of at most 32 rows on average
+constexpr int kBMMid = 64;            // BF16 launches whose 128-token tiles leave CUs idle
 
 // upper bound on the tile count: sum over experts of ceil(rows_e / BM)
 // <= (M + E * (BM - 1)) / BM m tiles, times the n tiles
@@ -1041,6 +1090,9 @@ int64_t tile_bound(int64_t M, int64_t N, int E, int bm = kBM) {
 // most 4 and at least 4 K stages each
 int splitk_factor(int epilogue, int64_t M, int64_t N, int64_t K, int E, int cus) {
   if (epilogue != NVFP4_EPI_BF16 || M == 0 || cus <= 0) return 1;
+  // 64-token tiles come first: split only when even they leave half the
+  // device idle
+  if (2 * tile_bound(M, N, E, kBMMid) > cus) return 1;
   const int64_t tiles = tile_bound(M, N, E);
   if (2 * tiles > cus) return 1;
   int64_t f = cus / tiles;
@@ -1133,8 +1185,16 @@ hipError_t launch_fmt(const GemmArgs& a, hipStream_t stream) {
       gemm_splitk_ws_bytes(a.epilogue, a.M, a.N, a.K, a.E) > kGemmWorkspaceBytes &&
       a.ws_bytes >= gemm_splitk_ws_bytes(a.epilogue, a.M, a.N, a.K, a.E))
     return launch_cfg<kBN, kBM, 4, 1, kEpiPartial, FMT>(a, stream);
-  return small ? launch_cfg<kBN, FS, 4, 1, NVFP4_EPI_BF16, FMT>(a, stream)
-               : launch_cfg<kBN, kBM, 4, 1, NVFP4_EPI_BF16, FMT>(a, stream);
+  if (small) return launch_cfg<kBN, FS, 4, 1, NVFP4_EPI_BF16, FMT>(a, stream);
+  // 64-token tiles when the 128-token tile list would leave half the CUs idle
+  // (a dense linear of a few thousand rows: 4096 x 2048 gives 128 tiles of
+  // 128 x 512, 256 of 64 x 512)
+  int cus = 0;
+  const hipError_t err = device_cus(cus);
+  if (err != hipSuccess) return err;
+  if (a.M > 0 && 2 * tile_bound(a.M, a.N, a.E, kBM) <= cus)
+    return launch_cfg<kBN, kBMMid, 4, 1, NVFP4_EPI_BF16, FMT>(a, stream);
+  return launch_cfg<kBN, kBM, 4, 1, NVFP4_EPI_BF16, FMT>(a, stream);
 }
 
 hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t stream) {

@@ -35,5 +35,7 @@ def test_bench_line_contract_tiny():
     assert roof["bound"] in ("hbm", "mfma")
     assert roof["unit"] == ("GB/s" if roof["bound"] == "hbm" else "TFLOP/s")
     assert abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-3
+    if d.get("clock"):                        # SMU reading of a sustained loop of the step
+        assert 0 < d["clock"]["gfxclk_mhz"] < 5000 and d["clock"]["socket_power_w"] > 0
     cpu = d["cpu_baseline"]
     assert cpu["kind"] == "oracle" and cpu["value"] > 0 and cpu["cores"] >= 1 and cpu["sample"]

@@ -86,6 +86,7 @@ def test_grouped_bf16_epilogue(counts, N, K):
     ([5, 0, 130, 1, 64, 200], 96, 1152),      # 9 stages: parts of 4 and 5
     ([300], 512, 2048),                       # 16 stages: 4 parts
     ([0, 1], 32, 512),                        # one row, 4 stages: no split
+    ([1024], 2048, 7168),                     # a dense linear of 1024 rows: 64 tiles of 64 x 512
 ])
 def test_grouped_bf16_split_k(counts, N, K):
     """Launches with few tiles split K when the workspace allows it; each
@@ -139,7 +140,10 @@ def test_dense_linear_config2_sampled_rows(split):
     if split:
         nbytes = nv.gemm_splitk_workspace_bytes(nv.EPI_BF16, M, N, K, 1)
         print(f"[case] dense split-K workspace {nbytes} bytes", flush=True)
-        assert nbytes > nv.gemm_workspace_bytes(), "128 tiles on 256 CUs are expected to split K"
+        # 64-token tiles (256 of them) cover 256 CUs: K is not split even
+        # when the workspace would allow it
+        assert nbytes == nv.gemm_workspace_bytes(), "the dense shape runs unsplit 64-token tiles"
+        nbytes = nv.gemm_splitk_workspace_bytes(nv.EPI_BF16, 1024, N, K, 1)
         ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
     c = nv.grouped_gemm(nv.EPI_BF16, a_q, a_sf, gs_a, off,
                         nv.pack_weights(b_q.view(1, N, K // 2), b_sf.view(1, N, K // 16)), gs_b, M,
