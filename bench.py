@@ -43,8 +43,8 @@ RIDGE = FP16_MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)   # flop per byte
 # each scaled by the ratio of known bytes to the counter's reading for a plain
 # 1 GiB device copy (--copy-calibration).  Reported only while the GEMM
 # sources hash to the value the counters were taken with; otherwise null.
-TRAFFIC = {("prefill", "l1", "nvfp4"): 6209300000, ("prefill", "l1", "mx"): 5683300000}
-TRAFFIC_SRC_SHA = "8b7c0f15c97fcb86"
+TRAFFIC = {("prefill", "l1", "nvfp4"): 6184157490, ("prefill", "l2", "nvfp4"): 3532244603}
+TRAFFIC_SRC_SHA = "a7edf429f7ed4e69"
 
 
 def gemm_src_sha():
@@ -233,15 +233,19 @@ def time_loop(fn, steps):
     return ev.ms() / steps
 
 
+CLOCK_LOOPS = True
+
+
 def sustained(fn, secs=2.0, settle=0.8):
     """Run fn back to back for `secs` seconds and return (ms per call over
     the whole loop by HIP events, SMU summary over the part after `settle`
     seconds).  The SMU metrics table lags the workload by a few hundred
     milliseconds, so the clock and power of a kernel are read from a loop
     of this length rather than from the short timed regions."""
+    if not CLOCK_LOOPS:
+        return None, None
     torch.cuda.synchronize()
     smp = smu()
-    samples0 = len(smp.samples)
     with smp:
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
@@ -387,8 +391,10 @@ def bench_moe(w, steps, warmup, dev, mx=False):
         "live_experts": n_live,
         "weight_stream_gbs": (w1_bytes + w2_bytes) / (ms_step * 1e-3) / 1e9,
         "l2_roofline": roofline("grouped_gemm_kernel<BF16 epilogue> (L2)" + (" MX" if mx else ""),
-                                l2_flops, l2_bytes, st_ms["l2_gemm"], peak=peak,
-                                clock=st_clk["l2_gemm"]),
+                                l2_flops, l2_bytes, st_ms["l2_gemm"],
+                                TRAFFIC.get((w.name, "l2", "mx" if mx else "nvfp4"))
+                                if TRAFFIC_SRC_SHA == gemm_src_sha() else None,
+                                peak=peak, clock=st_clk["l2_gemm"]),
         "step_clock": step_clk,
         "tokens_per_s": T / (ms_step * 1e-3),
         "l2_gemm_tflops": l2_flops / (st_ms["l2_gemm"] * 1e-3) / 1e12,
@@ -529,10 +535,14 @@ def main():
     ap.add_argument("--shared", action="store_true",
                     help="add one shared expert (every token, weight 1) to the MoE forward")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip the 2 s loops that read the SMU clock and power (for profiler runs)")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy 1 GiB device-to-device 3 times (counter calibration)")
     args = ap.parse_args()
+    global CLOCK_LOOPS
+    CLOCK_LOOPS = not args.no_clock
     if args.copy_calibration:
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
         dst = torch.empty_like(src)
