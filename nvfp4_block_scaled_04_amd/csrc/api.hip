@@ -154,7 +154,7 @@ FwdLayout fwd_layout(int64_t T, int64_t H, int64_t I, int E, int k) {
   L.inv = take(sizeof(int32_t) * (size_t)M);
   L.bad = take(sizeof(int32_t));
   L.rws = take(nvfp4::route_ws_bytes(T, k, E));
-  L.gws = take(nvfp4::kGemmWorkspaceBytes);
+  L.gws = take(2 * nvfp4::kGemmWorkspaceBytes);   // L1's scheduler counters, then L2's
   L.h_q = take((size_t)(M * I / 2));
   L.h_sf = take((size_t)(M * I / 16));
   L.y = take((size_t)(M * H * 2));
@@ -469,23 +469,29 @@ nvfp4_status forward_impl(int mx, const void* x_bf16, int64_t T, int64_t H, int6
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t M = T * k;
   hipError_t err = hipSuccess;
+  uint8_t* gws1 = base + L.gws;
+  uint8_t* gws2 = gws1 + nvfp4::kGemmWorkspaceBytes;
   if (T > 0) {
-    err = nvfp4::launch_quantize(x_bf16, 1, T, H, nullptr, a_q, a_sf, gs_a,
-                                 reinterpret_cast<float*>(base + L.qws), s);
-    if (err != hipSuccess) return hip_fail(err, "moe_expert_forward quantize");
+    // quantize x + route in three launches; the first also zeroes both
+    // GEMMs' scheduler counters (both 256-byte slots)
+    err = nvfp4::launch_forward_prologue(x_bf16, T, H, topk_ids, k, E, a_q, a_sf, gs_a,
+                                         reinterpret_cast<float*>(base + L.qws), base + L.rws, off,
+                                         perm, inv, bad, reinterpret_cast<int*>(gws1),
+                                         (int)(2 * nvfp4::kGemmWorkspaceBytes / sizeof(int)), s);
+    if (err != hipSuccess) return hip_fail(err, "moe_expert_forward quantize + route");
     if (mx) {
       err = nvfp4::launch_mx_reencode(a_q, a_sf, T, H, a_q, a_sf, s);
       if (err != hipSuccess) return hip_fail(err, "moe_expert_forward_mx re-encode x");
     }
   } else {
     nvfp4::fill_f32(gs_a, 1.0f, 1, s);
+    err = nvfp4::launch_route(topk_ids, T, k, E, off, perm, inv, bad, base + L.rws, s);
+    if (err != hipSuccess) return hip_fail(err, "moe_expert_forward route");
   }
-  err = nvfp4::launch_route(topk_ids, T, k, E, off, perm, inv, bad, base + L.rws, s);
-  if (err != hipSuccess) return hip_fail(err, "moe_expert_forward route");
   if (M > 0) {
     nvfp4::GemmArgs l1{NVFP4_EPI_SWIGLU_NVFP4, a_q, a_sf, gs_a, perm, k, off, E, M, 2 * I, H,
-                       w1_q, w1_sf, gs_w1, gs_h, nullptr, h_q, h_sf, tp.h_f32, base + L.gws,
-                       nvfp4::kGemmWorkspaceBytes, mx};
+                       w1_q, w1_sf, gs_w1, gs_h, nullptr, h_q, h_sf, tp.h_f32, gws1,
+                       nvfp4::kGemmWorkspaceBytes, mx, /*clear_sched=*/false};
     err = nvfp4::launch_grouped_gemm(l1, s);
     if (err != hipSuccess) return hip_fail(err, "moe_expert_forward L1");
     if (mx) {
@@ -493,8 +499,8 @@ nvfp4_status forward_impl(int mx, const void* x_bf16, int64_t T, int64_t H, int6
       if (err != hipSuccess) return hip_fail(err, "moe_expert_forward_mx re-encode h");
     }
     nvfp4::GemmArgs l2{NVFP4_EPI_BF16, h_q, h_sf, gs_h, nullptr, 1, off, E, M, H, I,
-                       w2_q, w2_sf, gs_w2, nullptr, y, nullptr, nullptr, nullptr, base + L.gws,
-                       nvfp4::kGemmWorkspaceBytes, mx};
+                       w2_q, w2_sf, gs_w2, nullptr, y, nullptr, nullptr, nullptr, gws2,
+                       nvfp4::kGemmWorkspaceBytes, mx, /*clear_sched=*/false};
     err = nvfp4::launch_grouped_gemm(l2, s);
     if (err != hipSuccess) return hip_fail(err, "moe_expert_forward L2");
   }

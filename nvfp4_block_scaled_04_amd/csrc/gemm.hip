@@ -1145,7 +1145,8 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
     if (err != hipSuccess) return err;
     attr_set[dev].store(true, std::memory_order_relaxed);
   }
-  zero_ints_kernel<<<1, 64, 0, stream>>>(p.sched, 8);   // a kernel, not a memset: graph-safe
+  if (a.clear_sched)
+    zero_ints_kernel<<<1, 64, 0, stream>>>(p.sched, 8);   // a kernel, not a memset: graph-safe
   kern<<<(unsigned)grid, C::NT, lds, stream>>>(p);
   if (EPI == kEpiPartial) {
     const int64_t vecs = a.M * a.N / 8;

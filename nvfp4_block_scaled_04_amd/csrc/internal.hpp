@@ -30,10 +30,26 @@ hipError_t launch_quantize_scatter(const void* x, int64_t T, int64_t H, int k,
 
 // route.hip
 int64_t route_chunks(int64_t T, int k);
+int64_t route_chunk(int64_t M);   // entries per chunk for M routed pairs
 size_t route_ws_bytes(int64_t T, int k, int E);
 hipError_t launch_route(const int32_t* topk_ids, int64_t T, int k, int E, int32_t* offsets,
                         int32_t* perm, int32_t* inv_perm, int32_t* invalid_count, void* ws,
                         hipStream_t stream);
+// the last routing launch alone: ws holds the scanned histogram and the
+// bucket totals (route_ws_bytes layout); M > 0
+hipError_t launch_route_scatter(const int32_t* topk_ids, int64_t M, int E, void* ws,
+                                int32_t* offsets, int32_t* perm, int32_t* inv_perm,
+                                int32_t* invalid_count, hipStream_t stream);
+
+// prologue.hip: quantize x (one group, per-call global scale) and route,
+// in the same bytes as launch_quantize + launch_route, and clear sched_ints
+// ints at sched (the GEMMs' scheduler counters); T > 0, qws and rws sized
+// as for launch_quantize and launch_route
+hipError_t launch_forward_prologue(const void* x, int64_t T, int64_t H, const int32_t* topk_ids,
+                                   int k, int E, uint8_t* a_q, uint8_t* a_sf, float* gs_a,
+                                   float* qws, void* rws, int32_t* offsets, int32_t* perm,
+                                   int32_t* inv_perm, int32_t* invalid_count, int* sched,
+                                   int sched_ints, hipStream_t stream);
 
 // slot k of every token -> expert E with weight 1 (ids [T][k+1], w [T][k+1])
 hipError_t launch_route_add_shared(const int32_t* ids, const float* w, int64_t T, int k, int E,
@@ -69,6 +85,7 @@ struct GemmArgs {
                     // room for split-K partials if ws_bytes allows
   size_t ws_bytes;
   int mx = 0;       // operands are MXFP4 (nvfp4 -> mx re-encoding), not NVFP4
+  bool clear_sched = true;   // false: an earlier launch on the stream zeroed the counters
 };
 constexpr size_t kGemmWorkspaceBytes = 256;
 // workspace with which a launch of this shape splits K (kGemmWorkspaceBytes

@@ -6,64 +6,50 @@
 // blocks are zeroed; CURRENT_BUG.md "What Works": the activation global scale
 // is recomputed per call.
 //
-// Three launches for the per-call global scale, one with a given scale:
-//   amax_partial   grid (P, groups): chunk maxima of |x| -> ws[g][P]
-//   gs_finalize    grid (groups):    gs[g] = 2688 / max(ws[g][:]) (1 if 0)
-//   quantize       one thread per 16-element block: 32 B in, 9 B out.
-// Max is exact, so the partial split cannot change the result.
+// Launches for a per-call global scale: one group (the forward's tokens, a
+// dense A operand) takes two,
+//   amax_partial   grid (P, 1):    chunk maxima of |x| -> ws[P]
+//   quantize_gs    capped grid:    every block reduces ws to the global scale
+//                                  2688 / max (1 if 0) and quantises 16-element
+//                                  blocks grid-stride (32 B in, 9 B out each);
+// several groups (weight preparation) three: amax_partial over (P, groups),
+// gs_finalize per group, then quantize with the per-group scales.  With a
+// given scale only quantize runs.  Max is exact, so the partial split cannot
+// change the result.
 #include "internal.hpp"
-#include "device.hpp"
+#include "steps.hpp"
 
 namespace nvfp4 {
 
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = kStepThreads;
 
 __global__ __launch_bounds__(kThreads) void amax_partial_kernel(
     const uint4* __restrict__ x, int64_t vec_per_group, int parts, float* __restrict__ partial) {
   const int g = blockIdx.y;
   const int p = blockIdx.x;
-  const uint4* xg = x + (int64_t)g * vec_per_group;
   const int64_t per = (vec_per_group + parts - 1) / parts;
   const int64_t lo = (int64_t)p * per;
   const int64_t hi = lo + per < vec_per_group ? lo + per : vec_per_group;
-  float m = 0.0f;
-  for (int64_t i = lo + threadIdx.x; i < hi; i += kThreads) {
-    const uint4 v = xg[i];
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      m = fmaxf(m, fabsf(bf16_to_f32(w[j] & 0xFFFFu)));
-      m = fmaxf(m, fabsf(bf16_to_f32(w[j] >> 16)));
-    }
-  }
-  // wave reduction, then across the 4 waves
-  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
   __shared__ float red[kThreads / 64];
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    float r = red[0];
-    for (int i = 1; i < kThreads / 64; ++i) r = fmaxf(r, red[i]);
-    partial[(int64_t)g * parts + p] = r;
-  }
+  const float m = block_max(thread_amax(x + (int64_t)g * vec_per_group, lo, hi), red);
+  if (threadIdx.x == 0) partial[(int64_t)g * parts + p] = m;
 }
 
 __global__ __launch_bounds__(kThreads) void gs_finalize_kernel(const float* __restrict__ partial,
                                                                int parts, float* __restrict__ gs_out) {
   const int g = blockIdx.x;
-  float m = 0.0f;
-  for (int i = threadIdx.x; i < parts; i += kThreads) m = fmaxf(m, partial[(int64_t)g * parts + i]);
-  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
   __shared__ float red[kThreads / 64];
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    float r = red[0];
-    for (int i = 1; i < kThreads / 64; ++i) r = fmaxf(r, red[i]);
-    gs_out[g] = (r == 0.0f) ? 1.0f : kGsNumerator / r;
-  }
+  const float gs = gs_from_partials(partial + (int64_t)g * parts, parts, red);
+  if (threadIdx.x == 0) gs_out[g] = gs;
+}
+
+__global__ __launch_bounds__(kThreads) void quantize_gs_kernel(
+    const uint4* __restrict__ x, int64_t nblocks, const float* __restrict__ partial, int parts,
+    float* __restrict__ gs_out, uint2* __restrict__ q, uint8_t* __restrict__ sf) {
+  __shared__ float red[kThreads / 64];
+  quantize_gs_body(x, nblocks, partial, parts, gs_out, q, sf, blockIdx.x, gridDim.x, red);
 }
 
 // One thread per 16-element block.  blocks_per_group = rows_per_group*cols/16.
@@ -74,47 +60,43 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
   const int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (gs_copy_dst != nullptr && b < groups) gs_copy_dst[b] = gs_copy_src[b];
   if (b >= nblocks) return;
-  const float g = gs[b / blocks_per_group];
-  const uint4 v0 = x[2 * b], v1 = x[2 * b + 1];
-  const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-  float xs[16];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    xs[2 * j] = bf16_to_f32(w[j] & 0xFFFFu);
-    xs[2 * j + 1] = bf16_to_f32(w[j] >> 16);
-  }
-  uint32_t lo, hi, s;
-  quantize_block16(xs, g, lo, hi, s);
-  q[b] = make_uint2(lo, hi);
-  sf[b] = (uint8_t)s;
+  quantize_at(x, b, gs[b / blocks_per_group], q, sf);
 }
 
-// Quantise-and-scatter: one thread per 16-element block of a token row; the
-// block is quantised once (same rule as quantize_kernel) and written to the
-// k expert-order rows of that token (rows past offsets[E] skipped).
+// Quantise-and-scatter: every block reduces the chunk maxima to the global
+// scale (block 0 stores it), then takes 16-element blocks of token rows
+// grid-stride; a block is quantised once (same rule as quantize_kernel) and
+// written to the k expert-order rows of its token (rows past offsets[E]
+// skipped).
 __global__ __launch_bounds__(kThreads) void quantize_scatter_kernel(
     const uint4* __restrict__ x, int64_t T, int64_t blocks_per_row, int k,
     const int32_t* __restrict__ inv_perm, const int32_t* __restrict__ offsets, int E,
-    const float* __restrict__ gs, uint2* __restrict__ q, uint8_t* __restrict__ sf) {
-  const int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (b >= T * blocks_per_row) return;
-  const int64_t t = b / blocks_per_row, blk = b - t * blocks_per_row;
-  const uint4 v0 = x[2 * b], v1 = x[2 * b + 1];
-  const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-  float xs[16];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    xs[2 * j] = bf16_to_f32(w[j] & 0xFFFFu);
-    xs[2 * j + 1] = bf16_to_f32(w[j] >> 16);
-  }
-  uint32_t lo, hi, s;
-  quantize_block16(xs, gs[0], lo, hi, s);
+    const float* __restrict__ partial, int parts, float* __restrict__ gs_out,
+    uint2* __restrict__ q, uint8_t* __restrict__ sf) {
+  __shared__ float red[kThreads / 64];
+  const float g = gs_from_partials(partial, parts, red);
+  if (blockIdx.x == 0 && threadIdx.x == 0) gs_out[0] = g;
   const int32_t n_valid = offsets[E];
-  for (int j = 0; j < k; ++j) {
-    const int32_t d = inv_perm[t * k + j];
-    if (d >= n_valid) continue;
-    q[(int64_t)d * blocks_per_row + blk] = make_uint2(lo, hi);
-    sf[(int64_t)d * blocks_per_row + blk] = (uint8_t)s;
+  const int64_t nblocks = T * blocks_per_row;
+  for (int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x; b < nblocks;
+       b += (int64_t)gridDim.x * kThreads) {
+    const int64_t t = b / blocks_per_row, blk = b - t * blocks_per_row;
+    const uint4 v0 = x[2 * b], v1 = x[2 * b + 1];
+    const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    float xs[16];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      xs[2 * j] = bf16_to_f32(w[j] & 0xFFFFu);
+      xs[2 * j + 1] = bf16_to_f32(w[j] >> 16);
+    }
+    uint32_t lo, hi, s;
+    quantize_block16(xs, g, lo, hi, s);
+    for (int j = 0; j < k; ++j) {
+      const int32_t d = inv_perm[t * k + j];
+      if (d >= n_valid) continue;
+      q[(int64_t)d * blocks_per_row + blk] = make_uint2(lo, hi);
+      sf[(int64_t)d * blocks_per_row + blk] = (uint8_t)s;
+    }
   }
 }
 
@@ -131,10 +113,9 @@ hipError_t launch_quantize_scatter(const void* x, int64_t T, int64_t H, int k,
   const int parts = quantize_parts(1, T, H);
   amax_partial_kernel<<<dim3(parts, 1), kThreads, 0, stream>>>(static_cast<const uint4*>(x),
                                                                 T * H / 8, parts, ws);
-  gs_finalize_kernel<<<1, kThreads, 0, stream>>>(ws, parts, gs_out);
   const int64_t nblocks = T * (H / 16);
-  quantize_scatter_kernel<<<(unsigned)((nblocks + kThreads - 1) / kThreads), kThreads, 0, stream>>>(
-      static_cast<const uint4*>(x), T, H / 16, k, inv_perm, offsets, E, gs_out,
+  quantize_scatter_kernel<<<(unsigned)quant_grid(nblocks), kThreads, 0, stream>>>(
+      static_cast<const uint4*>(x), T, H / 16, k, inv_perm, offsets, E, ws, parts, gs_out,
       reinterpret_cast<uint2*>(q), sf);
   return hipGetLastError();
 }
@@ -158,9 +139,17 @@ hipError_t launch_quantize(const void* x, int64_t groups, int64_t rows_per_group
   const int64_t rows = groups * rows_per_group;
   const int64_t nblocks = rows * (cols / 16);
   if (groups == 0) return hipSuccess;
+  const int parts = quantize_parts(groups, rows_per_group, cols);
+  if (gs_in == nullptr && groups == 1 && parts > 0) {
+    // one group: the quantising blocks reduce the chunk maxima themselves
+    amax_partial_kernel<<<dim3(parts, 1), kThreads, 0, stream>>>(static_cast<const uint4*>(x),
+                                                                  rows * cols / 8, parts, ws);
+    quantize_gs_kernel<<<(unsigned)quant_grid(nblocks), kThreads, 0, stream>>>(
+        static_cast<const uint4*>(x), nblocks, ws, parts, gs_out, reinterpret_cast<uint2*>(q), sf);
+    return hipGetLastError();
+  }
   const float* gs = gs_in;
   if (gs_in == nullptr) {
-    const int parts = quantize_parts(groups, rows_per_group, cols);
     if (parts > 0) {
       amax_partial_kernel<<<dim3(parts, (unsigned)groups), kThreads, 0, stream>>>(
           static_cast<const uint4*>(x), rows_per_group * cols / 8, parts, ws);

@@ -14,18 +14,22 @@
 //                           (the bucket bases; block 0 writes them as the
 //                           expert offsets), then walks its chunk in order,
 //                           64 entries at a time; a lane's rank among equal
-//                           buckets of the batch comes from a ballot, so every
+//                           buckets of the batch comes from ballots, so every
 //                           bucket keeps increasing f (a stable counting sort).
-// All integer; integer atomics only in LDS, where order cannot matter.
+// The forward runs the histogram and the scan inside its fused prologue
+// (prologue.hip) and then the same scatter.  All integer; integer atomics
+// only in LDS, where order cannot matter.
 #include "internal.hpp"
+#include "steps.hpp"
 
 namespace nvfp4 {
 
 namespace {
 
-constexpr int kHistThreads = 256;
+constexpr int kHistThreads = kStepThreads;
 constexpr int64_t kMinChunk = 256;
 constexpr int64_t kMaxChunks = 1024;
+constexpr int kScatterBatches = 4;   // 64-entry batches whose ids a lane loads at once
 
 int64_t chunk_size(int64_t M) {
   int64_t ch = kMinChunk;
@@ -33,49 +37,30 @@ int64_t chunk_size(int64_t M) {
   return ch;
 }
 
-__device__ __forceinline__ int bucket_of(int32_t id, int E) {
-  return (id >= 0 && id < E) ? id : E;
-}
-
 __global__ __launch_bounds__(kHistThreads) void route_hist_kernel(
     const int32_t* __restrict__ ids, int64_t M, int64_t chunk, int64_t C, int E,
     int32_t* __restrict__ hist) {
   extern __shared__ int32_t cnt[];
-  const int nb = E + 1;
-  for (int b = threadIdx.x; b < nb; b += kHistThreads) cnt[b] = 0;
-  __syncthreads();
   const int64_t lo = (int64_t)blockIdx.x * chunk;
   const int64_t hi = lo + chunk < M ? lo + chunk : M;
-  for (int64_t f = lo + threadIdx.x; f < hi; f += kHistThreads) {
-    atomicAdd(&cnt[bucket_of(ids[f], E)], 1);
-  }
-  __syncthreads();
-  for (int b = threadIdx.x; b < nb; b += kHistThreads) hist[(int64_t)b * C + blockIdx.x] = cnt[b];
-}
-
-// inclusive prefix sum over the 64 lanes of a wave
-__device__ __forceinline__ int32_t wave_incl_scan(int32_t v, int lane) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int32_t u = __shfl_up(v, off, 64);
-    if (lane >= off) v += u;
-  }
-  return v;
+  chunk_hist(ids, lo, hi, E, cnt, hist, C, blockIdx.x);
 }
 
 __global__ __launch_bounds__(64) void route_scan_kernel(int32_t* __restrict__ hist, int64_t C,
                                                         int32_t* __restrict__ total) {
-  const int lane = threadIdx.x;
-  int32_t* h = hist + (int64_t)blockIdx.x * C;
-  int32_t run = 0;
-  for (int64_t c0 = 0; c0 < C; c0 += 64) {
-    const int64_t c = c0 + lane;
-    const int32_t v = c < C ? h[c] : 0;
-    const int32_t incl = wave_incl_scan(v, lane);
-    if (c < C) h[c] = run + incl - v;
-    run += __shfl(incl, 63, 64);
+  scan_bucket(hist + (int64_t)blockIdx.x * C, C, total + blockIdx.x, threadIdx.x);
+}
+
+// Lanes of the wave whose bucket equals this lane's, among the lanes in
+// `active`: one ballot per bit of the bucket index (nbits bits cover 0..E).
+__device__ __forceinline__ uint64_t same_bucket_lanes(int e, bool active, int nbits) {
+  uint64_t m = __ballot(active);
+  for (int bit = 0; bit < nbits; ++bit) {
+    const bool set = (e >> bit) & 1;
+    const uint64_t ones = __ballot(active && set);
+    m &= set ? ones : ~ones;
   }
-  if (lane == 0) total[blockIdx.x] = run;
+  return m;
 }
 
 __global__ __launch_bounds__(64) void route_scatter_kernel(
@@ -86,6 +71,15 @@ __global__ __launch_bounds__(64) void route_scatter_kernel(
   extern __shared__ int32_t cur[];
   const int nb = E + 1;
   const int lane = threadIdx.x;
+  const int64_t lo = (int64_t)blockIdx.x * chunk;
+  const int64_t hi = lo + chunk < M ? lo + chunk : M;
+  // the first batches' ids, loaded while the bucket bases are computed
+  int32_t pre[kScatterBatches];
+#pragma unroll
+  for (int i = 0; i < kScatterBatches; ++i) {
+    const int64_t f = lo + 64 * i + lane;
+    pre[i] = f < hi ? ids[f] : 0;
+  }
   // bucket bases: each lane sums a contiguous segment of total[], then an
   // exclusive scan of the segment sums across the wave
   const int seg = (nb + 63) / 64;
@@ -107,28 +101,25 @@ __global__ __launch_bounds__(64) void route_scatter_kernel(
     invalid_count[0] = total[E];
   }
   __syncthreads();
-  const int64_t lo = (int64_t)blockIdx.x * chunk;
-  const int64_t hi = lo + chunk < M ? lo + chunk : M;
+  const int nbits = 32 - __builtin_clz((unsigned)E);   // bits of the largest bucket, E
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int64_t base = lo; base < hi; base += 64) {
+  for (int64_t base = lo, i = 0; base < hi; base += 64, ++i) {
     const int64_t f = base + lane;
     const bool active = f < hi;
-    const int e = active ? bucket_of(ids[f], E) : -1;
-    uint64_t pending = __ballot(active);
-    int rank = 0, cnt = 0;
-    while (pending) {
-      const int leader = __ffsll((unsigned long long)pending) - 1;
-      const int e0 = __builtin_amdgcn_readlane(e, leader);
-      const uint64_t m = __ballot(active && e == e0);
-      if (active && e == e0) {
-        rank = __popcll(m & below);
-        cnt = __popcll(m);
-      }
-      pending &= ~m;
+    int32_t id;
+    if (i < kScatterBatches) {
+      id = pre[0];
+#pragma unroll
+      for (int j = 1; j < kScatterBatches; ++j)
+        if (i == j) id = pre[j];
+    } else {
+      id = active ? ids[f] : 0;
     }
-    int32_t pos = 0;
+    const int e = bucket_of(id, E);
+    const uint64_t m = same_bucket_lanes(e, active, nbits);
+    const int rank = __popcll(m & below), cnt = __popcll(m);
     if (active) {
-      pos = cur[e] + rank;
+      const int32_t pos = cur[e] + rank;
       perm[pos] = (int32_t)f;
       inv_perm[f] = pos;
     }
@@ -184,6 +175,20 @@ size_t route_ws_bytes(int64_t T, int k, int E) {
   return (size_t)n * sizeof(int32_t);
 }
 
+int64_t route_chunk(int64_t M) { return chunk_size(M); }
+
+hipError_t launch_route_scatter(const int32_t* topk_ids, int64_t M, int E, void* ws,
+                                int32_t* offsets, int32_t* perm, int32_t* inv_perm,
+                                int32_t* invalid_count, hipStream_t stream) {
+  const int64_t ch = chunk_size(M);
+  const int64_t C = (M + ch - 1) / ch;
+  const int32_t* hist = static_cast<const int32_t*>(ws);
+  const int32_t* total = hist + C * (int64_t)(E + 1);
+  route_scatter_kernel<<<(unsigned)C, 64, (size_t)(E + 1) * sizeof(int32_t), stream>>>(
+      topk_ids, M, ch, C, E, hist, total, offsets, invalid_count, perm, inv_perm);
+  return hipGetLastError();
+}
+
 hipError_t launch_route(const int32_t* topk_ids, int64_t T, int k, int E, int32_t* offsets,
                         int32_t* perm, int32_t* inv_perm, int32_t* invalid_count, void* ws,
                         hipStream_t stream) {
@@ -200,10 +205,7 @@ hipError_t launch_route(const int32_t* topk_ids, int64_t T, int k, int E, int32_
   const size_t lds_hist = (size_t)(E + 1) * sizeof(int32_t);
   route_hist_kernel<<<(unsigned)C, kHistThreads, lds_hist, stream>>>(topk_ids, M, ch, C, E, hist);
   route_scan_kernel<<<(unsigned)(E + 1), 64, 0, stream>>>(hist, C, total);
-  route_scatter_kernel<<<(unsigned)C, 64, lds_hist, stream>>>(topk_ids, M, ch, C, E, hist, total,
-                                                              offsets, invalid_count, perm,
-                                                              inv_perm);
-  return hipGetLastError();
+  return launch_route_scatter(topk_ids, M, E, ws, offsets, perm, inv_perm, invalid_count, stream);
 }
 
 }  // namespace nvfp4
