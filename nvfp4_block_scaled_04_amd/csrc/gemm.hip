@@ -596,9 +596,13 @@ __device__ __forceinline__ void tile_at(const Params& p, const int* tprefix, int
 // expert's tiles share one L2; its blocks claim tiles dynamically from
 // counter x.  The XCDs do not run at one clock, so a block whose range is
 // exhausted steals from the other XCDs' counters.  Thread 0 of a block
-// claims the tile after its next one right before it issues the next tile's
-// loads; the claim is published through LDS at the following post-K-loop
-// barrier, when every earlier load has completed.
+// claims its next tile when the current tile enters its last two K stages
+// (after the tile's last load is issued, so the claim only makes the
+// remaining vmcnt waits stricter); the claim is published through LDS at the
+// post-K-loop barrier, when every load has completed.  A tile therefore
+// starts within about two stages and an epilogue of its claim, and the m
+// tiles of one weight n tile, claimed one after another, stream that n tile
+// nearly in step and share it through L2.
 struct Sched {
   int64_t total;    // tiles in the list
   int* counters;    // eight per-XCD claim counters, zero at launch
@@ -796,6 +800,7 @@ __device__ __forceinline__ bool run_tile(const Params& p, uint8_t* smem, const i
                                         smem + buf1 * C::STAGE_BYTES, smem + buf2 * C::STAGE_BYTES);
       buf = buf1;
     }
+    if (tid == 0) claim = atomicAdd(sc.counters + sc.cx, 1);
     for (; ks < nks; ++ks) {
       const int buf1 = buf == 2 ? 0 : buf + 1, buf2 = buf == 0 ? 2 : buf - 1;
       k_stage_mx<BN, BM, WN, WM, JV, 0>(st, ks, nks, wave, coff, soff, wbase, wsbase, abase,
@@ -818,6 +823,7 @@ __device__ __forceinline__ bool run_tile(const Params& p, uint8_t* smem, const i
                                         smem + ((ks + 3) & 3) * SB);
       ++ks;
     }
+    if (tid == 0) claim = atomicAdd(sc.counters + sc.cx, 1);
     for (; ks < nks; ++ks)
       k_stage<BN, BM, WN, WM, JV, 0, 0>(st, ks, nks, wave, coff, soff, wbase, wsbase, abase, asbase,
                                         smem + (ks & 3) * SB, smem + ((ks + 1) & 3) * SB,
@@ -833,6 +839,7 @@ __device__ __forceinline__ bool run_tile(const Params& p, uint8_t* smem, const i
                                      smem + buf2 * C::STAGE_BYTES);
       buf = buf1;
     }
+    if (tid == 0) claim = atomicAdd(sc.counters + sc.cx, 1);
     for (; ks < nks; ++ks) {
       const int buf1 = buf == 2 ? 0 : buf + 1, buf2 = buf == 0 ? 2 : buf - 1;
       k_stage<BN, BM, WN, WM, JV, 0>(st, ks, nks, wave, coff, soff, wbase, wsbase, abase, asbase,
@@ -856,7 +863,6 @@ __device__ __forceinline__ bool run_tile(const Params& p, uint8_t* smem, const i
   {
   const int lane = lane_x, hf = lane_x >> 5, l32 = lane_x & 31;
   if (has_next) {
-    if (tid == 0) claim = atomicAdd(sc.counters + sc.cx, 1);
     tile_offsets<BN, BM, WN, WM, EPI>(p, nxt, wave, lane, coff, soff);
     k_issue_first<BN, BM, WN, WM>(nxt.nks, wave, coff, soff, tile_wq<BN>(p, nxt), tile_wsf<BN>(p, nxt),
                                   tile_aq(p, nxt), tile_asf(p, nxt), smem, smem + C::STAGE_BYTES,
@@ -991,7 +997,6 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_gemm_kernel(Params p)
   const int t0 = resolve_claim(sc, __builtin_amdgcn_readfirstlane(s_claim[0]));
   bool have = t0 >= 0;
   int claim = 0;                           // pending claim, meaningful in thread 0 only
-  if (have && tid == 0) claim = atomicAdd(sc.counters + sc.cx, 1);
   Tile cur;
   uint32_t coff[C::CODE_LOADS], soff[C::SF_LOADS];
   if (have) {
