@@ -78,8 +78,10 @@ nvfp4_status nvfp4_weight_layout(const void* src_bf16, int64_t groups, int64_t r
  * zeroed, scale 0 (bug 4); CURRENT_BUG.md "What Works": the activation global
  * scale is recomputed per call.
  *
- * x: BF16 [groups*rows_per_group][cols]; every group is quantised along its
- * rows (the contiguous axis) with its own global scale:
+ * x: BF16 [groups*rows_per_group][cols], row r at x + r*ld_x elements
+ * (ld_x >= cols, a multiple of 8 so that rows stay 16-byte aligned; ld_x ==
+ * cols for a contiguous tensor); every group is quantised along its rows
+ * (the contiguous axis) with its own global scale:
  *   gs_in == NULL: gs[g] = fl32(2688 / amax(group g)), or 1 for an all-zero
  *                  group, computed on the device and written to gs_out[g];
  *   gs_in != NULL: device float[groups] used as given and copied to gs_out.
@@ -89,13 +91,14 @@ nvfp4_status nvfp4_weight_layout(const void* src_bf16, int64_t groups, int64_t r
  *   code = signbit(x) << 3 | E2M1(min(|x*r|, 6)).
  * Outputs: q uint8 [groups*rows][cols/2], sf uint8 [groups*rows][cols/16],
  *   gs_out float [groups] (all device).
- * Shapes: groups >= 0, rows_per_group >= 0, cols >= 16, cols % 16 == 0.
+ * Shapes: groups >= 0, rows_per_group >= 0, cols >= 16, cols % 16 == 0,
+ *   ld_x >= cols, ld_x % 8 == 0 (else NVFP4_ERR_SHAPE).
  * Workspace: nvfp4_quantize_workspace_size() bytes (0 allowed with NULL).
  * ---------------------------------------------------------------------- */
 size_t nvfp4_quantize_workspace_size(int64_t groups, int64_t rows_per_group, int64_t cols);
 nvfp4_status nvfp4_quantize(const void* x_bf16, int64_t groups, int64_t rows_per_group,
-                            int64_t cols, const float* gs_in, uint8_t* q, uint8_t* sf,
-                            float* gs_out, void* ws, size_t ws_bytes, void* stream);
+                            int64_t cols, int64_t ld_x, const float* gs_in, uint8_t* q,
+                            uint8_t* sf, float* gs_out, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * Weight packing for the grouped GEMM (untimed preparation).

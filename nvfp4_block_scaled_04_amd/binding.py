@@ -34,8 +34,8 @@ SIGNATURES = {
     "nvfp4_pack_weights": (c_int, [c_void_p, c_void_p, c_int64, c_int64, c_int64, c_void_p, c_void_p,
                                    c_void_p]),
     "nvfp4_quantize_workspace_size": (c_size_t, [c_int64, c_int64, c_int64]),
-    "nvfp4_quantize": (c_int, [c_void_p, c_int64, c_int64, c_int64, c_void_p, c_void_p, c_void_p,
-                               c_void_p, c_void_p, c_size_t, c_void_p]),
+    "nvfp4_quantize": (c_int, [c_void_p, c_int64, c_int64, c_int64, c_int64, c_void_p, c_void_p,
+                               c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     "nvfp4_moe_route_workspace_size": (c_size_t, [c_int64, c_int, c_int]),
     "nvfp4_moe_route": (c_int, [c_void_p, c_int64, c_int, c_int, c_void_p, c_void_p, c_void_p,
                                 c_void_p, c_void_p, c_size_t, c_void_p]),
@@ -109,14 +109,19 @@ def _stream(device):
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def _dev(t, dtype, name, shape=None):
+def _dev(t, dtype, name, shape=None, rows=False):
+    """Check a device tensor; rows=True accepts a 2-D tensor whose rows are
+    contiguous but spaced apart (a row stride), as the row-strided calls do."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.device.type != "cuda":
         raise ValueError(f"{name} must be a device tensor")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
-    if not t.is_contiguous():
+    if rows:
+        if t.dim() != 2 or t.stride(1) != 1 or (t.shape[0] > 1 and t.stride(0) < t.shape[1]):
+            raise ValueError(f"{name} must be 2-D with contiguous rows")
+    elif not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if shape is not None and tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
@@ -204,8 +209,9 @@ def to_mx(q, sf, out=None):
 
 
 def quantize(x, groups=1, gs_in=None, out=None):
-    """x (R, C) bf16 -> (q (R, C/2) u8, sf (R, C/16) u8, gs (groups,) f32)."""
-    _dev(x, torch.bfloat16, "x")
+    """x (R, C) bf16 -> (q (R, C/2) u8, sf (R, C/16) u8, gs (groups,) f32).
+    x's rows may be spaced apart (x.stride(0) >= C, e.g. a column slice)."""
+    _dev(x, torch.bfloat16, "x", rows=True)
     R, C = x.shape
     if groups < 1 or R % groups:
         raise ValueError("rows must divide evenly into groups")
@@ -221,8 +227,9 @@ def quantize(x, groups=1, gs_in=None, out=None):
     L = lib()
     nbytes = L.nvfp4_quantize_workspace_size(groups, R // groups, C) if gs_in is None else 0
     ws = _workspace(nbytes, dev)
-    _check(L.nvfp4_quantize(_ptr(x), groups, R // groups, C, _ptr(gs_in), _ptr(q), _ptr(sf),
-                            _ptr(gs), _ptr(ws), nbytes, _stream(dev)), "nvfp4_quantize")
+    ld_x = x.stride(0) if R > 1 else C      # a one-row tensor's row stride is arbitrary
+    _check(L.nvfp4_quantize(_ptr(x), groups, R // groups, C, ld_x, _ptr(gs_in), _ptr(q),
+                            _ptr(sf), _ptr(gs), _ptr(ws), nbytes, _stream(dev)), "nvfp4_quantize")
     return q, sf, gs
 
 

@@ -65,17 +65,20 @@ size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
 
 // ---------------------------------------------------------------- checks
 
-nvfp4_status check_quantize(const void* x, int64_t groups, int64_t rpg, int64_t cols, uint8_t* q,
-                            uint8_t* sf, float* gs_out) {
+nvfp4_status check_quantize(const void* x, int64_t groups, int64_t rpg, int64_t cols, int64_t ld_x,
+                            uint8_t* q, uint8_t* sf, float* gs_out) {
   if (groups < 0 || rpg < 0) return fail(NVFP4_ERR_SHAPE, "groups and rows_per_group must be >= 0");
   if (groups > 65535) return fail(NVFP4_ERR_SHAPE, "groups must be <= 65535");
   if (cols < 16 || cols % 16) return fail(NVFP4_ERR_SHAPE, "cols must be a positive multiple of 16 (got %lld)", (long long)cols);
+  if (ld_x < cols || ld_x % 8)
+    return fail(NVFP4_ERR_SHAPE, "ld_x must be >= cols and a multiple of 8 (got %lld)", (long long)ld_x);
   if (groups == 0) return NVFP4_OK;
   if (!gs_out) return fail(NVFP4_ERR_INVALID_ARG, "gs_out is NULL");
   if (rpg == 0) return NVFP4_OK;
   if (!x || !q || !sf) return fail(NVFP4_ERR_INVALID_ARG, "x, q and sf must be non-NULL");
   if (!aligned(x, 16) || !aligned(q, 8)) return fail(NVFP4_ERR_INVALID_ARG, "x must be 16-byte and q 8-byte aligned");
-  if ((groups * rpg * cols / 16) >= (int64_t(1) << 40)) return fail(NVFP4_ERR_SHAPE, "tensor too large");
+  if ((groups * rpg * cols / 16) >= (int64_t(1) << 40) || groups * rpg * (ld_x / 8) >= (int64_t(1) << 40))
+    return fail(NVFP4_ERR_SHAPE, "tensor too large");
   return NVFP4_OK;
 }
 
@@ -228,9 +231,9 @@ size_t nvfp4_quantize_workspace_size(int64_t groups, int64_t rows_per_group, int
 }
 
 nvfp4_status nvfp4_quantize(const void* x, int64_t groups, int64_t rows_per_group, int64_t cols,
-                            const float* gs_in, uint8_t* q, uint8_t* sf, float* gs_out, void* ws,
-                            size_t ws_bytes, void* stream) {
-  nvfp4_status st = check_quantize(x, groups, rows_per_group, cols, q, sf, gs_out);
+                            int64_t ld_x, const float* gs_in, uint8_t* q, uint8_t* sf,
+                            float* gs_out, void* ws, size_t ws_bytes, void* stream) {
+  nvfp4_status st = check_quantize(x, groups, rows_per_group, cols, ld_x, q, sf, gs_out);
   if (st != NVFP4_OK) return st;
   if (gs_in == nullptr) {
     const size_t need = nvfp4_quantize_workspace_size(groups, rows_per_group, cols);
@@ -241,7 +244,7 @@ nvfp4_status nvfp4_quantize(const void* x, int64_t groups, int64_t rows_per_grou
   if (groups == 0) return NVFP4_OK;
   st = check_arch();
   if (st != NVFP4_OK) return st;
-  return finish(nvfp4::launch_quantize(x, groups, rows_per_group, cols, gs_in, q, sf, gs_out,
+  return finish(nvfp4::launch_quantize(x, groups, rows_per_group, cols, ld_x, gs_in, q, sf, gs_out,
                                        static_cast<float*>(ws), static_cast<hipStream_t>(stream)),
                 "nvfp4_quantize launch");
 }

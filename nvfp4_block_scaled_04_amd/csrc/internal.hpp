@@ -17,9 +17,10 @@ void fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t stream);
 
 // quantize.hip
 int quantize_parts(int64_t groups, int64_t rows_per_group, int64_t cols);
+// x rows are ld_x bf16 elements apart (ld_x >= cols, ld_x % 8 == 0)
 hipError_t launch_quantize(const void* x, int64_t groups, int64_t rows_per_group, int64_t cols,
-                           const float* gs_in, uint8_t* q, uint8_t* sf, float* gs_out, float* ws,
-                           hipStream_t stream);
+                           int64_t ld_x, const float* gs_in, uint8_t* q, uint8_t* sf,
+                           float* gs_out, float* ws, hipStream_t stream);
 
 // x (T, H) -> NVFP4 with a per-call global scale, each token row written to
 // its k expert-order rows (inv_perm), rows >= offsets[E] skipped

@@ -44,22 +44,22 @@ __global__ __launch_bounds__(kStepThreads) void prologue_a_kernel(
     const int64_t per = (vecs + parts - 1) / parts;
     const int64_t lo = p * per;
     const int64_t hi = lo + per < vecs ? lo + per : vecs;
-    const float m = block_max(thread_amax(x, lo, hi), red);
+    const float m = block_max(thread_amax(x, Rows{vecs, vecs}, lo, hi), red);
     if (threadIdx.x == 0) partial[p] = m;
   }
 }
 
 __global__ __launch_bounds__(kStepThreads) void prologue_b_kernel(
     int32_t* __restrict__ hist, int64_t C, int32_t* __restrict__ total, int E, int64_t scan_blocks,
-    const uint4* __restrict__ x, int64_t nblocks, const float* __restrict__ partial, int parts,
-    float* __restrict__ gs_out, uint2* __restrict__ q, uint8_t* __restrict__ sf) {
+    const uint4* __restrict__ x, Rows rows, int64_t nblocks, const float* __restrict__ partial,
+    int parts, float* __restrict__ gs_out, uint2* __restrict__ q, uint8_t* __restrict__ sf) {
   __shared__ float red[kStepThreads / 64];
   const int64_t b = blockIdx.x;
   if (b < scan_blocks) {
     const int64_t bucket = b * (kStepThreads / 64) + (threadIdx.x >> 6);
     if (bucket <= E) scan_bucket(hist + bucket * C, C, total + bucket, threadIdx.x & 63);
   } else {
-    quantize_gs_body(x, nblocks, partial, parts, gs_out, q, sf, b - scan_blocks,
+    quantize_gs_body(x, rows, nblocks, partial, parts, gs_out, q, sf, b - scan_blocks,
                      (int64_t)gridDim.x - scan_blocks, red);
   }
 }
@@ -85,8 +85,8 @@ hipError_t launch_forward_prologue(const void* x, int64_t T, int64_t H, const in
   const int64_t nblocks = T * (H / 16);
   const int64_t scan_blocks = (E + 1 + kStepThreads / 64 - 1) / (kStepThreads / 64);
   prologue_b_kernel<<<(unsigned)(scan_blocks + quant_grid(nblocks)), kStepThreads, 0, stream>>>(
-      hist, C, total, E, scan_blocks, static_cast<const uint4*>(x), nblocks, qws, parts, gs_a,
-      reinterpret_cast<uint2*>(a_q), a_sf);
+      hist, C, total, E, scan_blocks, static_cast<const uint4*>(x), Rows{H / 8, H / 8}, nblocks,
+      qws, parts, gs_a, reinterpret_cast<uint2*>(a_q), a_sf);
   return launch_route_scatter(topk_ids, M, E, rws, offsets, perm, inv_perm, invalid_count, stream);
 }
 

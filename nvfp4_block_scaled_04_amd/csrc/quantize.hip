@@ -25,15 +25,18 @@ namespace {
 
 constexpr int kThreads = kStepThreads;
 
+// vec_per_group data vectors per group; group g starts rows_per_group rows
+// (rows.ld vectors each) after group g - 1
 __global__ __launch_bounds__(kThreads) void amax_partial_kernel(
-    const uint4* __restrict__ x, int64_t vec_per_group, int parts, float* __restrict__ partial) {
+    const uint4* __restrict__ x, Rows rows, int64_t rows_per_group, int64_t vec_per_group,
+    int parts, float* __restrict__ partial) {
   const int g = blockIdx.y;
   const int p = blockIdx.x;
   const int64_t per = (vec_per_group + parts - 1) / parts;
   const int64_t lo = (int64_t)p * per;
   const int64_t hi = lo + per < vec_per_group ? lo + per : vec_per_group;
   __shared__ float red[kThreads / 64];
-  const float m = block_max(thread_amax(x + (int64_t)g * vec_per_group, lo, hi), red);
+  const float m = block_max(thread_amax(x + (int64_t)g * rows_per_group * rows.ld, rows, lo, hi), red);
   if (threadIdx.x == 0) partial[(int64_t)g * parts + p] = m;
 }
 
@@ -46,21 +49,21 @@ __global__ __launch_bounds__(kThreads) void gs_finalize_kernel(const float* __re
 }
 
 __global__ __launch_bounds__(kThreads) void quantize_gs_kernel(
-    const uint4* __restrict__ x, int64_t nblocks, const float* __restrict__ partial, int parts,
-    float* __restrict__ gs_out, uint2* __restrict__ q, uint8_t* __restrict__ sf) {
+    const uint4* __restrict__ x, Rows rows, int64_t nblocks, const float* __restrict__ partial,
+    int parts, float* __restrict__ gs_out, uint2* __restrict__ q, uint8_t* __restrict__ sf) {
   __shared__ float red[kThreads / 64];
-  quantize_gs_body(x, nblocks, partial, parts, gs_out, q, sf, blockIdx.x, gridDim.x, red);
+  quantize_gs_body(x, rows, nblocks, partial, parts, gs_out, q, sf, blockIdx.x, gridDim.x, red);
 }
 
 // One thread per 16-element block.  blocks_per_group = rows_per_group*cols/16.
 __global__ __launch_bounds__(kThreads) void quantize_kernel(
-    const uint4* __restrict__ x, int64_t nblocks, int64_t blocks_per_group,
+    const uint4* __restrict__ x, Rows rows, int64_t nblocks, int64_t blocks_per_group,
     const float* __restrict__ gs, const float* __restrict__ gs_copy_src, int groups,
     float* __restrict__ gs_copy_dst, uint2* __restrict__ q, uint8_t* __restrict__ sf) {
   const int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (gs_copy_dst != nullptr && b < groups) gs_copy_dst[b] = gs_copy_src[b];
   if (b >= nblocks) return;
-  quantize_at(x, b, gs[b / blocks_per_group], q, sf);
+  quantize_at(x, rows, b, gs[b / blocks_per_group], q, sf);
 }
 
 // Quantise-and-scatter: every block reduces the chunk maxima to the global
@@ -111,8 +114,8 @@ hipError_t launch_quantize_scatter(const void* x, int64_t T, int64_t H, int k,
     return hipGetLastError();
   }
   const int parts = quantize_parts(1, T, H);
-  amax_partial_kernel<<<dim3(parts, 1), kThreads, 0, stream>>>(static_cast<const uint4*>(x),
-                                                                T * H / 8, parts, ws);
+  amax_partial_kernel<<<dim3(parts, 1), kThreads, 0, stream>>>(
+      static_cast<const uint4*>(x), Rows{H / 8, H / 8}, T, T * H / 8, parts, ws);
   const int64_t nblocks = T * (H / 16);
   quantize_scatter_kernel<<<(unsigned)quant_grid(nblocks), kThreads, 0, stream>>>(
       static_cast<const uint4*>(x), T, H / 16, k, inv_perm, offsets, E, ws, parts, gs_out,
@@ -134,25 +137,27 @@ int quantize_parts(int64_t groups, int64_t rows_per_group, int64_t cols) {
 }
 
 hipError_t launch_quantize(const void* x, int64_t groups, int64_t rows_per_group, int64_t cols,
-                           const float* gs_in, uint8_t* q, uint8_t* sf, float* gs_out, float* ws,
-                           hipStream_t stream) {
+                           int64_t ld_x, const float* gs_in, uint8_t* q, uint8_t* sf,
+                           float* gs_out, float* ws, hipStream_t stream) {
   const int64_t rows = groups * rows_per_group;
   const int64_t nblocks = rows * (cols / 16);
+  const uint4* xv = static_cast<const uint4*>(x);
+  const Rows rv{cols / 8, ld_x / 8};
   if (groups == 0) return hipSuccess;
   const int parts = quantize_parts(groups, rows_per_group, cols);
   if (gs_in == nullptr && groups == 1 && parts > 0) {
     // one group: the quantising blocks reduce the chunk maxima themselves
-    amax_partial_kernel<<<dim3(parts, 1), kThreads, 0, stream>>>(static_cast<const uint4*>(x),
-                                                                  rows * cols / 8, parts, ws);
+    amax_partial_kernel<<<dim3(parts, 1), kThreads, 0, stream>>>(xv, rv, rows, rows * cols / 8,
+                                                                  parts, ws);
     quantize_gs_kernel<<<(unsigned)quant_grid(nblocks), kThreads, 0, stream>>>(
-        static_cast<const uint4*>(x), nblocks, ws, parts, gs_out, reinterpret_cast<uint2*>(q), sf);
+        xv, rv, nblocks, ws, parts, gs_out, reinterpret_cast<uint2*>(q), sf);
     return hipGetLastError();
   }
   const float* gs = gs_in;
   if (gs_in == nullptr) {
     if (parts > 0) {
       amax_partial_kernel<<<dim3(parts, (unsigned)groups), kThreads, 0, stream>>>(
-          static_cast<const uint4*>(x), rows_per_group * cols / 8, parts, ws);
+          xv, rv, rows_per_group, rows_per_group * cols / 8, parts, ws);
       gs_finalize_kernel<<<(unsigned)groups, kThreads, 0, stream>>>(ws, parts, gs_out);
     } else {
       // empty groups: global scale 1
@@ -165,7 +170,7 @@ hipError_t launch_quantize(const void* x, int64_t groups, int64_t rows_per_group
   const unsigned grid = (unsigned)((need + kThreads - 1) / kThreads);
   const bool copy = gs_in != nullptr && gs_out != gs_in;
   quantize_kernel<<<grid, kThreads, 0, stream>>>(
-      static_cast<const uint4*>(x), nblocks, rows_per_group * (cols / 16) > 0 ? rows_per_group * (cols / 16) : 1,
+      xv, rv, nblocks, rows_per_group * (cols / 16) > 0 ? rows_per_group * (cols / 16) : 1,
       gs, gs_in, (int)groups, copy ? gs_out : nullptr, reinterpret_cast<uint2*>(q), sf);
   return hipGetLastError();
 }

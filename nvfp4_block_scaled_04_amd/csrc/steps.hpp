@@ -25,13 +25,26 @@ __device__ __forceinline__ float block_max(float m, float* red) {
   return r;
 }
 
-// This thread's max |x| over the bf16 vectors [lo, hi) (8 values each),
+// Rows of a bf16 tensor in 16-byte vectors: rv vectors of data per row, rows
+// ld vectors apart (ld == rv: contiguous).  at(i) is the position of data
+// vector i (row-major).
+struct Rows {
+  int64_t rv, ld;
+  __device__ __forceinline__ int64_t at(int64_t i) const {
+    if (ld == rv) return i;
+    const int64_t row = i / rv;
+    return row * ld + (i - row * rv);
+  }
+};
+
+// This thread's max |x| over the data vectors [lo, hi) (8 values each),
 // block-strided.  Max is exact, so any split of the range gives the same
 // global result.
-__device__ __forceinline__ float thread_amax(const uint4* __restrict__ x, int64_t lo, int64_t hi) {
+__device__ __forceinline__ float thread_amax(const uint4* __restrict__ x, Rows rows, int64_t lo,
+                                             int64_t hi) {
   float m = 0.0f;
   for (int64_t i = lo + threadIdx.x; i < hi; i += kStepThreads) {
-    const uint4 v = x[i];
+    const uint4 v = x[rows.at(i)];
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -53,11 +66,13 @@ __device__ __forceinline__ float gs_from_partials(const float* __restrict__ part
   return (r == 0.0f) ? 1.0f : kGsNumerator / r;
 }
 
-// 16-element block b of x (two 16-byte vectors) -> 8 bytes of codes and a
-// scale byte, with global scale g
-__device__ __forceinline__ void quantize_at(const uint4* __restrict__ x, int64_t b, float g,
-                                            uint2* __restrict__ q, uint8_t* __restrict__ sf) {
-  const uint4 v0 = x[2 * b], v1 = x[2 * b + 1];
+// 16-element block b of x (data vectors 2b and 2b + 1, one row) -> 8 bytes
+// of codes and a scale byte, with global scale g
+__device__ __forceinline__ void quantize_at(const uint4* __restrict__ x, Rows rows, int64_t b,
+                                            float g, uint2* __restrict__ q,
+                                            uint8_t* __restrict__ sf) {
+  const int64_t v = rows.at(2 * b);
+  const uint4 v0 = x[v], v1 = x[v + 1];
   const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
   float xs[16];
 #pragma unroll
@@ -84,15 +99,15 @@ inline int64_t quant_grid(int64_t nblocks) {
 // Quantisation of one group of nblocks 16-element blocks whose global scale
 // follows from the chunk maxima: block `blk` of `nblk` reduces them, block 0
 // stores the scale, and the 16-element blocks are taken grid-stride.
-__device__ __forceinline__ void quantize_gs_body(const uint4* __restrict__ x, int64_t nblocks,
-                                                 const float* __restrict__ partial, int parts,
-                                                 float* __restrict__ gs_out, uint2* __restrict__ q,
-                                                 uint8_t* __restrict__ sf, int64_t blk,
-                                                 int64_t nblk, float* red) {
+__device__ __forceinline__ void quantize_gs_body(const uint4* __restrict__ x, Rows rows,
+                                                 int64_t nblocks, const float* __restrict__ partial,
+                                                 int parts, float* __restrict__ gs_out,
+                                                 uint2* __restrict__ q, uint8_t* __restrict__ sf,
+                                                 int64_t blk, int64_t nblk, float* red) {
   const float g = gs_from_partials(partial, parts, red);
   if (blk == 0 && threadIdx.x == 0) gs_out[0] = g;
   for (int64_t b = blk * kStepThreads + threadIdx.x; b < nblocks; b += nblk * kStepThreads)
-    quantize_at(x, b, g, q, sf);
+    quantize_at(x, rows, b, g, q, sf);
 }
 
 // routing bucket of an expert id: ids outside [0, E) share bucket E

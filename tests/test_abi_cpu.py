@@ -62,11 +62,13 @@ FAKE = 0x1000  # never dereferenced: every call below fails validation first
 
 
 @pytest.mark.parametrize("args,status", [
-    ((FAKE, 1, 4, 15, None, FAKE, FAKE, FAKE, FAKE, 1 << 20, None), -2),   # cols % 16
-    ((FAKE, -1, 4, 16, None, FAKE, FAKE, FAKE, FAKE, 1 << 20, None), -2),
-    ((None, 1, 4, 16, None, FAKE, FAKE, FAKE, FAKE, 1 << 20, None), -1),   # null x
-    ((FAKE, 1, 4, 16, None, FAKE, FAKE, FAKE, None, 0, None), -3),         # no workspace
-    ((FAKE + 8, 1, 4, 16, None, FAKE, FAKE, FAKE, FAKE, 1 << 20, None), -1),  # misaligned x
+    ((FAKE, 1, 4, 15, 16, None, FAKE, FAKE, FAKE, FAKE, 1 << 20, None), -2),   # cols % 16
+    ((FAKE, -1, 4, 16, 16, None, FAKE, FAKE, FAKE, FAKE, 1 << 20, None), -2),
+    ((FAKE, 1, 4, 32, 16, None, FAKE, FAKE, FAKE, FAKE, 1 << 20, None), -2),   # ld_x < cols
+    ((FAKE, 1, 4, 32, 36, None, FAKE, FAKE, FAKE, FAKE, 1 << 20, None), -2),   # ld_x % 8
+    ((None, 1, 4, 16, 16, None, FAKE, FAKE, FAKE, FAKE, 1 << 20, None), -1),   # null x
+    ((FAKE, 1, 4, 16, 16, None, FAKE, FAKE, FAKE, None, 0, None), -3),         # no workspace
+    ((FAKE + 8, 1, 4, 16, 16, None, FAKE, FAKE, FAKE, FAKE, 1 << 20, None), -1),  # misaligned x
 ])
 def test_quantize_rejects(L, args, status):
     assert L.nvfp4_quantize(*args) == status

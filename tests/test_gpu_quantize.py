@@ -47,6 +47,20 @@ def test_quantize_ragged_shapes(shape):
     _check_quant(x, what=str(shape))
 
 
+@pytest.mark.parametrize("R,C,ld,col0,groups,given", [
+    (37, 272, 280, 0, 1, False), (64, 256, 1024, 8, 4, False), (130, 1040, 1048, 8, 2, True),
+    (1000, 7168, 7176, 0, 1, False)])
+def test_quantize_row_stride(R, C, ld, col0, groups, given):
+    """Rows ld_x elements apart (a column slice of a wider tensor): the same
+    bytes as the oracle's quantisation of the slice."""
+    g = torch.Generator(device=DEV).manual_seed(R + C + ld)
+    wide = torch.randn((R, ld), generator=g, device=DEV).to(torch.bfloat16)
+    x = wide[:, col0:col0 + C]
+    assert x.stride(0) == ld and not x.is_contiguous()
+    gs_in = torch.tensor([0.5, 3.0][:groups], dtype=torch.float32, device=DEV) if given else None
+    _check_quant(x, groups=groups, gs_in=gs_in, what=f"ld_x={ld} col0={col0}")
+
+
 def test_quantize_zero_underflow_and_negative_zero_blocks():
     g = torch.Generator(device=DEV).manual_seed(3)
     x = torch.randn((64, 256), generator=g, device=DEV)
