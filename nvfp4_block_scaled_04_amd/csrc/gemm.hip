@@ -60,7 +60,7 @@
 // owns a contiguous eighth of it, so the tiles that share a weight n tile run
 // side by side in one L2, and its blocks claim tiles from a per-XCD counter,
 // stealing from other XCDs' ranges at the end.  A block finds a tile's expert
-// by binary search of a per-expert m-tile prefix kept in LDS.
+// by a two-round 64-way search of a per-expert m-tile prefix kept in LDS.
 #include <atomic>
 
 #include "internal.hpp"
@@ -563,10 +563,15 @@ __device__ __forceinline__ void tile_at(const Params& p, const int* tprefix, int
   // the largest e with tprefix[e] <= tix / n_tiles (fixed steps, no loop:
   // tprefix is non-decreasing and tprefix[0] = 0)
   const int mg = tix / p.n_tiles;
-  int e = 0;
-#pragma unroll
-  for (int step = 2048; step > 0; step >>= 1)
-    if (e + step < p.E && tprefix[e + step] <= mg) e += step;
+  // two wave-wide rounds of 64 tests (E <= 4096): lane l tests expert l*S
+  // (S = ceil(E / 64)), then expert e0 + l; the lanes that pass form a prefix
+  // (tprefix is non-decreasing), and lane 0 always passes
+  const int lane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  const int S = (p.E + 63) >> 6;
+  int c = lane * S;
+  const int e0 = (__popcll(__ballot(c < p.E && tprefix[c] <= mg)) - 1) * S;
+  c = e0 + lane;
+  const int e = e0 + __popcll(__ballot(lane < S && c < p.E && tprefix[c] <= mg)) - 1;
   t.e = __builtin_amdgcn_readfirstlane(e);
   const int mcount = tprefix[t.e + 1] - tprefix[t.e];
   const int local = tix - tprefix[t.e] * p.n_tiles;
@@ -757,9 +762,12 @@ __device__ __forceinline__ void epilogue_bf16(const Params& p, float16v (&acc)[F
 // One tile: the K loop and the epilogue.  JV = number of 32-token column
 // blocks that hold rows (1..FM); the rest are skipped.  The tile's first
 // AHEAD stages (0 and 1; 0 to 2 for 32-token tiles) were issued by the caller
-// with the load offsets coff/soff; after the K loop those of the next tile
-// (if any) are issued, with coff/soff rewritten for it, so that their latency
-// overlaps the epilogue.
+// with the load offsets coff/soff; after the epilogue those of the next tile
+// (if any) are issued, with coff/soff rewritten for it.  Issuing them before
+// the epilogue would overlap their latency with it, but keeps the offsets
+// and the next tile's bases live through the epilogue, whose spill reloads
+// (vector loads, completing in order) then wait for those loads anyway; the
+// later issue measured faster (prefill L1 -1.8%).
 template <int BN, int BM, int WN, int WM, int EPI, int FMT, int JV>
 __device__ __forceinline__ bool run_tile(const Params& p, uint8_t* smem, const int* tprefix,
                                          Sched& sc, const Tile& cur, uint32_t* coff,
@@ -862,12 +870,6 @@ __device__ __forceinline__ bool run_tile(const Params& p, uint8_t* smem, const i
   if (has_next) tile_at<BN, BM>(p, tprefix, t_next, nxt);
   {
   const int lane = lane_x, hf = lane_x >> 5, l32 = lane_x & 31;
-  if (has_next) {
-    tile_offsets<BN, BM, WN, WM, EPI>(p, nxt, wave, lane, coff, soff);
-    k_issue_first<BN, BM, WN, WM>(nxt.nks, wave, coff, soff, tile_wq<BN>(p, nxt), tile_wsf<BN>(p, nxt),
-                                  tile_aq(p, nxt), tile_asf(p, nxt), smem, smem + C::STAGE_BYTES,
-                                  smem + 2 * C::STAGE_BYTES);
-  }
 
   // ---- epilogue
   const float alpha = 1.0f / (uniform_load(p.gs_a, 0) *
@@ -948,6 +950,12 @@ __device__ __forceinline__ bool run_tile(const Params& p, uint8_t* smem, const i
         }
       }
     }
+  }
+  if (has_next) {
+    tile_offsets<BN, BM, WN, WM, EPI>(p, nxt, wave, lane, coff, soff);
+    k_issue_first<BN, BM, WN, WM>(nxt.nks, wave, coff, soff, tile_wq<BN>(p, nxt), tile_wsf<BN>(p, nxt),
+                                  tile_aq(p, nxt), tile_asf(p, nxt), smem, smem + C::STAGE_BYTES,
+                                  smem + 2 * C::STAGE_BYTES);
   }
   }
   return has_next;
