@@ -97,6 +97,9 @@ def test_forward_tiny_workload():
     I.custom("ragged", T=77, H=384, I=256, E=6, k=3, seed=2),
     I.custom("skewed_small", T=200, H=256, I=128, E=16, k=4, routing="zipf", special="blocks", seed=3),
     I.custom("many_experts", T=50, H=128, I=128, E=64, k=8, seed=4),
+    # more experts than the 32-token tiles take (E > 1024), mostly empty, and
+    # two routing chunks in the forward's fused histogram and scan
+    I.custom("wide_E", T=64, H=128, I=128, E=1500, k=6, seed=7),
 ], ids=lambda w: w.name)
 def test_forward_small_edge_workloads(w):
     _check_full(w)
