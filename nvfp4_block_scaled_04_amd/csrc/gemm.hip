@@ -33,7 +33,7 @@
 // Tiling.  A block is 4 waves stacked along N (wave tile 128 N x 128 tokens,
 // 4x4 MFMA blocks, 256 fp32 accumulators per lane); decoding is done per wave
 // from packed codes in LDS, so each decoded element feeds 4 MFMAs.  Stages of
-// 128 K go from HBM straight into LDS (global_load_lds), triple-buffered.  An
+// 128 K go from HBM straight into LDS (buffer loads with the lds flag), triple-buffered.  An
 // expert's rows are cut into ceil(rows/128) m tiles with its 32-row blocks
 // spread evenly over them; column blocks past a tile's rows are skipped.
 // Launches whose experts average at most 32 rows (decode-sized batches) use
@@ -238,36 +238,55 @@ __device__ __forceinline__ void stage_barrier() {
   constexpr int kSfLoads = C::SF_LOADS, kSfLoadsW = C::SF_LOADS_W, kCodeBytes = C::CODE_BYTES;  \
   constexpr bool kSmall = C::SMALL, kTsfShared = C::TSF_SHARED;                                \
   constexpr int kWPol = C::SMALL ? 2 : 0
+// A direct load of `size` bytes per lane from base + voff (per lane, 32 bits)
+// + soff (uniform) into LDS at dst, through a raw buffer resource: the base
+// stays in scalar registers and the per-lane offset in one VGPR, so no
+// 64-bit per-lane address is formed or kept per load.  The resource spans
+// the whole 32-bit offset range (the offsets are validated on the host).
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const uint8_t* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, -1, 0x00020000);
+}
+// LDS pointer from a generic pointer into LDS by its low 32 bits (the LDS
+// offset in the shared aperture): a plain address-space cast of a pointer
+// selected among the stage buffers makes the compiler emit an aperture check
+// it then rejects
+__device__ __forceinline__ lds_ptr_t lds_addr(const uint8_t* p) {
+  return (lds_ptr_t)(uint32_t)(uintptr_t)p;
+}
+#define NVFP4_BLOAD(rs, voff, soff, dst, size, pol)                                             \
+  __builtin_amdgcn_raw_ptr_buffer_load_lds((rs), lds_addr(dst), (size), (int)(voff),          \
+                                           (int)(soff), 0, (pol))
 #define NVFP4_ISSUE(ks, dst, part)                                                              \
   do {                                                                                          \
     uint8_t* sbw = (dst);                                                                       \
+    const __amdgpu_buffer_rsrc_t rw_ = raw_rsrc(wq), rws_ = raw_rsrc(wsf);                      \
+    const __amdgpu_buffer_rsrc_t ra_ = raw_rsrc(aq), ras_ = raw_rsrc(asf);                      \
     _Pragma("unroll") for (int c = 0; c < kCodeLoads; ++c) {                                    \
       if ((part) < 0 || load_step(c) == (part)) {                                               \
         if (c < kCodeLoadsW)                                                                    \
-          __builtin_amdgcn_global_load_lds(wq + coff[c] + (uint32_t)(ks) * (BN * ROW_BYTES),    \
-                                           sbw + (c * kNW + wave) * 1024, 16, 0, kWPol);        \
+          NVFP4_BLOAD(rw_, coff[c], (uint32_t)(ks) * (BN * ROW_BYTES),                          \
+                      sbw + (c * kNW + wave) * 1024, 16, kWPol);                                \
         else if (kSmall)                                                                        \
-          __builtin_amdgcn_global_load_lds(aq + coff[c] + (uint32_t)(ks) * ROW_BYTES,           \
-                                           sbw + BN * ROW_BYTES +                               \
-                                               ((c - kCodeLoadsW) * kNW + wave) * 256, 4, 0, 0); \
+          NVFP4_BLOAD(ra_, coff[c], (uint32_t)(ks) * ROW_BYTES,                                 \
+                      sbw + BN * ROW_BYTES + ((c - kCodeLoadsW) * kNW + wave) * 256, 4, 0);     \
         else                                                                                    \
-          __builtin_amdgcn_global_load_lds(aq + coff[c] + (uint32_t)(ks) * ROW_BYTES,           \
-                                           sbw + (c * kNW + wave) * 1024, 16, 0, 0);            \
+          NVFP4_BLOAD(ra_, coff[c], (uint32_t)(ks) * ROW_BYTES, sbw + (c * kNW + wave) * 1024,  \
+                      16, 0);                                                                   \
       }                                                                                         \
     }                                                                                           \
     _Pragma("unroll") for (int c = 0; c < kSfLoads; ++c) {                                      \
       if ((part) < 0 || load_step(kCodeLoads + c) == (part)) {                                  \
         if (c < kSfLoadsW)                                                                      \
-          __builtin_amdgcn_global_load_lds(wsf + soff[c] + (uint32_t)(ks) * (BN * SF_BYTES),    \
-                                           sbw + kCodeBytes + (c * kNW + wave) * 1024, 16, 0, kWPol); \
+          NVFP4_BLOAD(rws_, soff[c], (uint32_t)(ks) * (BN * SF_BYTES),                          \
+                      sbw + kCodeBytes + (c * kNW + wave) * 1024, 16, kWPol);                   \
         else if (kTsfShared)                                                                    \
-          __builtin_amdgcn_global_load_lds(asf + soff[c] + (uint32_t)(ks) * SF_BYTES,           \
-                                           sbw + kCodeBytes + BN * SF_BYTES +                   \
-                                               (c - kSfLoadsW) * 256, 4, 0, 0);                 \
+          NVFP4_BLOAD(ras_, soff[c], (uint32_t)(ks) * SF_BYTES,                                 \
+                      sbw + kCodeBytes + BN * SF_BYTES + (c - kSfLoadsW) * 256, 4, 0);          \
         else                                                                                    \
-          __builtin_amdgcn_global_load_lds(asf + soff[c] + (uint32_t)(ks) * SF_BYTES,           \
-                                           sbw + kCodeBytes + BN * SF_BYTES +                   \
-                                               ((c - kSfLoadsW) * kNW + wave) * 256, 4, 0, 0);  \
+          NVFP4_BLOAD(ras_, soff[c], (uint32_t)(ks) * SF_BYTES,                                 \
+                      sbw + kCodeBytes + BN * SF_BYTES + ((c - kSfLoadsW) * kNW + wave) * 256, \
+                      4, 0);                                                                    \
       }                                                                                         \
     }                                                                                           \
   } while (0)
