@@ -321,9 +321,10 @@ nvfp4_status nvfp4_moe_combine(const void* y_bf16, const int32_t* inv_perm,
  *   [E][H][I/16]); gs_w2 [E];
  * gs_h float[1]: global scale of the requantised L2 input (pre-computed);
  * out BF16 [T][H].
- * Steps on `stream`: nvfp4_quantize(x, per-call gs) -> nvfp4_moe_route ->
- *   grouped GEMM L1 (SwiGLU + NVFP4 epilogue, A rows gathered by perm/k) ->
- *   grouped GEMM L2 (BF16) -> combine.
+ * Steps on `stream`: quantize x with a per-call gs and route (the bytes of
+ *   nvfp4_quantize + nvfp4_moe_route, in three launches that also clear the
+ *   GEMMs' tile counters) -> grouped GEMM L1 (SwiGLU + NVFP4 epilogue, A rows
+ *   gathered by perm/k) -> grouped GEMM L2 (BF16) -> combine.
  * taps (nullable): every non-NULL member receives that intermediate (the
  *   kernels write straight into it instead of the workspace).
  * Shapes: T >= 0, H % 128 == 0, I % 128 == 0, 1 <= k <= 64, 1 <= E <= 4096,
@@ -402,8 +403,8 @@ nvfp4_status moe_expert_forward_mx(const void* x_bf16, int64_t T, int64_t H, int
  *   T <= 524), else NVFP4_ERR_WORKSPACE and nothing is enqueued.
  * All calls on one GPU share its array, which keeps the last call's
  * contents (nothing in it needs to start at zero: every region is written
- * before it is read, and the GEMMs' tile counters are cleared by a kernel on
- * each launch).  Calls ordered on one stream are safe; calls that overlap on
+ * before it is read, and the GEMMs' tile counters are cleared by the first
+ * kernel of each call).  Calls ordered on one stream are safe; calls that overlap on
  * one GPU (unordered streams, several host threads) race on the array and
  * give wrong results.
  * ---------------------------------------------------------------------- */
