@@ -349,7 +349,8 @@ __device__ __forceinline__ lds_ptr_t lds_addr(const uint8_t* p) {
 // pointer parameters are __restrict__ here and in k_stage: LDS reads of one
 // buffer are then known not to alias direct loads into another, so the
 // compiler adds no wait on loads in flight; every wait those reads need is
-// an explicit s_waitcnt + barrier.
+// an explicit s_waitcnt + barrier.  (That holds within one function: k_begin
+// below cannot tell its reads of b0 from these loads into b1 and b2.)
 template <int BN, int BM, int WN, int WM>
 __device__ __forceinline__ void k_issue_first(int nks, int wave, const uint32_t* coff,
                                               const uint32_t* soff,
@@ -368,13 +369,32 @@ __device__ __forceinline__ void k_issue_first(int nks, int wave, const uint32_t*
 
 // Waits for stage 0 (in b0; the tile's first stages are the last loads
 // issued, later vector memory operations are stores), synchronises the
-// block and decodes step 0.
+// block and decodes step 0.  32-token tiles issue their first AHEAD stages
+// here, from the same __restrict__ parameters as the reads: with the loads
+// issued in k_issue_first the compiler cannot tell the reads of b0 from the
+// loads into b1 and b2 and waits for all three stages before the first
+// read.  Decode-sized launches run many short tiles and lost that time at
+// every tile start (decode L1 -5.7%, L2 -3.4%, A/B).  Larger tiles keep the
+// issue in k_issue_first, after the epilogue: issuing there from k_begin
+// made the SwiGLU epilogue spill, and prefill L1 ran 1% slower.
 template <int BN, int BM, int WN, int WM, int JV>
-__device__ __forceinline__ void k_begin(KState<BN, BM, WN, WM, JV>& st, int nks,
-                                        const uint8_t* __restrict__ b0) {
+__device__ __forceinline__ void k_begin(KState<BN, BM, WN, WM, JV>& st, int nks, int wave,
+                                        const uint32_t* coff, const uint32_t* soff,
+                                        const uint8_t* __restrict__ wq,
+                                        const uint8_t* __restrict__ wsf,
+                                        const uint8_t* __restrict__ aq,
+                                        const uint8_t* __restrict__ asf,
+                                        uint8_t* __restrict__ b0, uint8_t* __restrict__ b1,
+                                        uint8_t* __restrict__ b2) {
   using C = Cfg<BN, BM, WN, WM>;
   constexpr int FN = C::FN, TN = C::TN, TM = C::TM;
   static_assert(C::LOADS == 12 && kLoadsBeforeBarrier == 8, "vmcnt immediates assume 12 loads per stage");
+  NVFP4_LOAD_CONSTS;
+  if constexpr (C::SMALL) {
+    NVFP4_ISSUE(0, b0, -1);
+    if (nks > 1) NVFP4_ISSUE(1, b1, -1);
+    if (nks > 2) NVFP4_ISSUE(2, b2, -1);
+  }
   if (C::AHEAD > 2 && nks > 2) asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
   else if (nks > 1) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
   else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -780,13 +800,14 @@ __device__ __forceinline__ void epilogue_bf16(const Params& p, float16v (&acc)[F
 
 // One tile: the K loop and the epilogue.  JV = number of 32-token column
 // blocks that hold rows (1..FM); the rest are skipped.  The tile's first
-// AHEAD stages (0 and 1; 0 to 2 for 32-token tiles) were issued by the caller
-// with the load offsets coff/soff; after the epilogue those of the next tile
-// (if any) are issued, with coff/soff rewritten for it.  Issuing them before
-// the epilogue would overlap their latency with it, but keeps the offsets
-// and the next tile's bases live through the epilogue, whose spill reloads
-// (vector loads, completing in order) then wait for those loads anyway; the
-// later issue measured faster (prefill L1 -1.8%).
+// AHEAD stages (0 and 1) were issued by the caller with the load offsets
+// coff/soff; after the epilogue those of the next tile (if any) are issued,
+// with coff/soff rewritten for it.  Issuing them before the epilogue would
+// overlap their latency with it, but keeps the offsets and the next tile's
+// bases live through the epilogue, whose spill reloads (vector loads,
+// completing in order) then wait for those loads anyway; the later issue
+// measured faster (prefill L1 -1.8%).  32-token tiles compute coff/soff and
+// issue their first three stages at the start of the tile, in k_begin.
 template <int BN, int BM, int WN, int WM, int EPI, int FMT, int JV>
 __device__ __forceinline__ bool run_tile(const Params& p, uint8_t* smem, const int* tprefix,
                                          Sched& sc, const Tile& cur, uint32_t* coff,
@@ -804,6 +825,7 @@ __device__ __forceinline__ bool run_tile(const Params& p, uint8_t* smem, const i
   const uint8_t* wsbase = tile_wsf<BN>(p, cur);
   const uint8_t* abase = tile_aq(p, cur);
   const uint8_t* asbase = tile_asf(p, cur);
+  if constexpr (C::SMALL) tile_offsets<BN, BM, WN, WM, EPI>(p, cur, wave, lane, coff, soff);
 
   KState<BN, BM, WN, WM, JV> st;
   st.wn = wn; st.wm = wm; st.hf = hf; st.l32 = l32;
@@ -838,7 +860,7 @@ __device__ __forceinline__ bool run_tile(const Params& p, uint8_t* smem, const i
   } else if constexpr (C::AHEAD == 3) {
     // four LDS stage buffers, stage ks in buffer ks % 4
     constexpr int SB = C::STAGE_BYTES;
-    k_begin(st, nks, smem);
+    k_begin(st, nks, wave, coff, soff, wbase, wsbase, abase, asbase, smem, smem + SB, smem + 2 * SB);
     int ks = 0;
     for (; ks + 3 < nks; ++ks)
       k_stage<BN, BM, WN, WM, JV, 1, 1>(st, ks, nks, wave, coff, soff, wbase, wsbase, abase, asbase,
@@ -856,7 +878,8 @@ __device__ __forceinline__ bool run_tile(const Params& p, uint8_t* smem, const i
                                         smem + (ks & 3) * SB, smem + ((ks + 1) & 3) * SB,
                                         smem + ((ks + 3) & 3) * SB);
   } else {
-    k_begin(st, nks, smem);
+    k_begin(st, nks, wave, coff, soff, wbase, wsbase, abase, asbase, smem,
+            smem + C::STAGE_BYTES, smem + 2 * C::STAGE_BYTES);
     int buf = 0;
     int ks = 0;
     for (; ks + 2 < nks; ++ks) {
@@ -970,7 +993,7 @@ __device__ __forceinline__ bool run_tile(const Params& p, uint8_t* smem, const i
       }
     }
   }
-  if (has_next) {
+  if (!C::SMALL && has_next) {
     tile_offsets<BN, BM, WN, WM, EPI>(p, nxt, wave, lane, coff, soff);
     k_issue_first<BN, BM, WN, WM>(nxt.nks, wave, coff, soff, tile_wq<BN>(p, nxt), tile_wsf<BN>(p, nxt),
                                   tile_aq(p, nxt), tile_asf(p, nxt), smem, smem + C::STAGE_BYTES,
@@ -1028,6 +1051,8 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_gemm_kernel(Params p)
   uint32_t coff[C::CODE_LOADS], soff[C::SF_LOADS];
   if (have) {
     tile_at<BN, BM>(p, tprefix, t0, cur);
+  }
+  if (!C::SMALL && have) {
     tile_offsets<BN, BM, WN, WM, EPI>(p, cur, wave, lane, coff, soff);
     k_issue_first<BN, BM, WN, WM>(cur.nks, wave, coff, soff, tile_wq<BN>(p, cur), tile_wsf<BN>(p, cur),
                                   tile_aq(p, cur), tile_asf(p, cur), smem, smem + C::STAGE_BYTES,
