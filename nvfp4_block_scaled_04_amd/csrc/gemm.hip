@@ -658,20 +658,37 @@ __device__ __forceinline__ int range_lo(int64_t total, int c) { return (int)((to
 
 // Tile index of claim k made on counter sc.cx, or -1 when every range is
 // exhausted.  Every thread calls it with the same k; when sc.cx's range is
-// exhausted thread 0 claims from the other counters in turn and the result
+// exhausted wave 0 looks for another range with tiles left and the result
 // is broadcast through LDS (one extra barrier, only at the end of a range).
+// Lanes 1-7 read the other counters at once (agent-scope atomic loads; a
+// counter only grows, so a stale value that shows its range exhausted is
+// right), and thread 0 then claims, in order, only from ranges that looked
+// open.  Claiming on every counter in turn took seven dependent atomics,
+// about 15 us, at the end of every block's work (12% of a dense linear).
 __device__ __forceinline__ int resolve_claim(Sched& sc, int k) {
   if (range_lo(sc.total, sc.cx) + k < range_lo(sc.total, sc.cx + 1))
     return range_lo(sc.total, sc.cx) + k;
-  if (threadIdx.x == 0) {
-    int t = -1, c = sc.cx;
-    for (int d = 1; d < 8 && t < 0; ++d) {
-      c = (c + 1) & 7;
-      const int kk = atomicAdd(sc.counters + c, 1);
-      if (range_lo(sc.total, c) + kk < range_lo(sc.total, c + 1)) t = range_lo(sc.total, c) + kk;
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const int c = (sc.cx + lane) & 7;
+    bool open = false;
+    if (lane >= 1 && lane < 8) {
+      const int cnt = __hip_atomic_load(sc.counters + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      open = range_lo(sc.total, c) + cnt < range_lo(sc.total, c + 1);
     }
-    sc.s_claim[2] = t;
-    sc.s_claim[3] = c;
+    uint64_t cand = __ballot(open);
+    if (lane == 0) {
+      int t = -1, cc = sc.cx;
+      while (cand != 0 && t < 0) {
+        const int d = __builtin_ctzll(cand);   // next open range, in order from sc.cx
+        cand &= cand - 1;
+        cc = (sc.cx + d) & 7;
+        const int kk = atomicAdd(sc.counters + cc, 1);
+        if (range_lo(sc.total, cc) + kk < range_lo(sc.total, cc + 1)) t = range_lo(sc.total, cc) + kk;
+      }
+      sc.s_claim[2] = t;
+      sc.s_claim[3] = cc;
+    }
   }
   __syncthreads();
   sc.cx = __builtin_amdgcn_readfirstlane(sc.s_claim[3]);
