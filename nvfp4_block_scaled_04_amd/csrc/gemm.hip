@@ -375,8 +375,8 @@ __device__ __forceinline__ void k_issue_first(int nks, int wave, const uint32_t*
 // loads into b1 and b2 and waits for all three stages before the first
 // read.  Decode-sized launches run many short tiles and lost that time at
 // every tile start (decode L2 -1.2%, forward -0.7%, A/B).  Larger tiles keep
-// the issue in k_issue_first, after the epilogue: moving it into k_begin
-// made their SwiGLU epilogue spill, and prefill L1 ran 1% slower.
+// the issue in k_issue_first, after the epilogue: issuing there from
+// k_begin made the SwiGLU epilogue spill, and prefill L1 ran 1% slower.
 template <int BN, int BM, int WN, int WM, int JV>
 __device__ __forceinline__ void k_begin(KState<BN, BM, WN, WM, JV>& st, int nks, int wave,
                                         const uint32_t* coff, const uint32_t* soff,
