@@ -35,19 +35,19 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // Subnormal range: t = k * 2^-9 with k = rint(t * 512) in 1..8 (k = 8 is the
 // smallest normal, byte 0x08, so the two ranges meet without a seam).
 __device__ __forceinline__ uint32_t e4m3_encode(float t) {
-  if (t < 0.015625f) {
-    return (uint32_t)__builtin_rintf(t * 512.0f);
-  }
+  const uint32_t sub = (uint32_t)__builtin_rintf(t * 512.0f);
   uint32_t u = __float_as_uint(t);
   u += 0x7FFFFu + ((u >> 20) & 1u);
-  return (u >> 20) - (120u << 3);
+  const uint32_t nrm = (u >> 20) - (120u << 3);
+  return t < 0.015625f ? sub : nrm;   // both computed: a select, not a branch
 }
 
 // value of an E4M3 byte with sign bit clear (never the NaN byte here)
 __device__ __forceinline__ float e4m3_decode(uint32_t b) {
   uint32_t e = (b >> 3) & 15u, m = b & 7u;
-  if (e == 0) return (float)m * 0.001953125f;   // m * 2^-9, exact
-  return __uint_as_float(((e + 120u) << 23) | (m << 20));
+  const float sub = (float)m * 0.001953125f;   // m * 2^-9, exact
+  const float nrm = __uint_as_float(((e + 120u) << 23) | (m << 20));
+  return e == 0 ? sub : nrm;
 }
 
 // Eight fp32 values -> eight E2M1 codes (value i in bits 4i..4i+3):

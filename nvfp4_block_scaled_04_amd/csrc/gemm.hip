@@ -375,8 +375,8 @@ __device__ __forceinline__ void k_issue_first(int nks, int wave, const uint32_t*
 // loads into b1 and b2 and waits for all three stages before the first
 // read.  Decode-sized launches run many short tiles and lost that time at
 // every tile start (decode L2 -1.2%, forward -0.7%, A/B).  Larger tiles keep
-// the issue in k_issue_first, after the epilogue: issuing there from
-// k_begin made the SwiGLU epilogue spill, and prefill L1 ran 1% slower.
+// the issue in k_issue_first, after the epilogue: moving it into k_begin
+// made their SwiGLU epilogue spill, and prefill L1 ran 1% slower.
 template <int BN, int BM, int WN, int WM, int JV>
 __device__ __forceinline__ void k_begin(KState<BN, BM, WN, WM, JV>& st, int nks, int wave,
                                         const uint32_t* coff, const uint32_t* soff,
@@ -985,21 +985,24 @@ __device__ __forceinline__ bool run_tile(const Params& p, uint8_t* smem, const i
         const auto swp = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m),
                                                           false, false);
         const float amax = fmaxf(__uint_as_float(swp[0]), __uint_as_float(swp[1]));
-        if (tok >= nrows || nb >= N) continue;
-        const int64_t d = row0 + tok;
-        uint32_t codes = 0, sfb = 0;
+        uint32_t codes, sfb;
         {
 #pragma clang fp contract(off)
           const float a_s = amax * gs_h;
-          if (!(amax == 0.0f || a_s < kUnderflow)) {
-            const float t = fminf(a_s / 6.0f, kE4m3Max);
-            sfb = e4m3_encode(t);
-            const float r = gs_h / e4m3_decode(sfb);
-            // sign | E2M1(min(|h*r|, 6)); r > 0, so h*r has the sign of h
-            codes = e2m1_pack8(h[0] * r, h[1] * r, h[2] * r, h[3] * r, h[4] * r, h[5] * r,
-                               h[6] * r, h[7] * r);
-          }
+          const bool zero = amax == 0.0f || a_s < kUnderflow;
+          // every lane encodes (a zeroed block gives r = inf and is replaced):
+          // no branch inside the block's chain
+          const float t = fminf(a_s / 6.0f, kE4m3Max);
+          const uint32_t sb = e4m3_encode(t);
+          const float r = gs_h / e4m3_decode(sb);
+          // sign | E2M1(min(|h*r|, 6)); r > 0, so h*r has the sign of h
+          const uint32_t c = e2m1_pack8(h[0] * r, h[1] * r, h[2] * r, h[3] * r, h[4] * r,
+                                        h[5] * r, h[6] * r, h[7] * r);
+          codes = zero ? 0u : c;
+          sfb = zero ? 0u : sb;
         }
+        if (tok >= nrows || nb >= N) continue;
+        const int64_t d = row0 + tok;
         *reinterpret_cast<uint32_t*>(p.c_q + d * (I / 2) + hb * 8 + hf * 4) = codes;
         if (hf == 0) p.c_sf[d * (I / 16) + hb] = (uint8_t)sfb;
         if (p.c_debug != nullptr) {
