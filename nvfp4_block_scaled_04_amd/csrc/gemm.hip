@@ -576,6 +576,15 @@ struct Tile {
   int split, ks_lo, nks;   // K range [ks_lo, ks_lo + nks) in stages
 };
 
+// Lane index within the wave (0..63), recomputed wherever it is called: an
+// asm statement with side effects is not hoisted out of a loop or merged
+// with another call.
+__device__ __forceinline__ int lane_index() {
+  int lane;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
+  return lane;
+}
+
 // Wave-uniform read of a device array through the constant address space: a
 // scalar load, counted by lgkmcnt.  A vector load here would be counted by
 // vmcnt, which completes in order, so the compiler's wait for it would also
@@ -594,7 +603,7 @@ __device__ __forceinline__ int uniform_load(const int32_t* p, int i) {
 // and run side by side; split-K parts innermost).  tprefix: per-expert
 // m-tile prefix (E <= 4096).  The fields are wave-uniform: readfirstlane
 // keeps them in scalar registers.
-template <int BN, int BM>
+template <int BN, int BM, bool LANE_ASM = false>
 __device__ __forceinline__ void tile_at(const Params& p, const int* tprefix, int logical, Tile& t) {
   const int tix = logical / p.ksplit;
   const int split = logical - tix * p.ksplit;
@@ -605,7 +614,8 @@ __device__ __forceinline__ void tile_at(const Params& p, const int* tprefix, int
   // two wave-wide rounds of 64 tests (E <= 4096): lane l tests expert l*S
   // (S = ceil(E / 64)), then expert e0 + l; the lanes that pass form a prefix
   // (tprefix is non-decreasing), and lane 0 always passes
-  const int lane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  int lane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  if constexpr (LANE_ASM) lane = lane_index();   // see run_tile
   const int S = (p.E + 63) >> 6;
   int c = lane * S;
   const int e0 = (__popcll(__ballot(c < p.E && tprefix[c] <= mg)) - 1) * S;
@@ -832,7 +842,15 @@ __device__ __forceinline__ bool run_tile(const Params& p, uint8_t* smem, const i
   using C = Cfg<BN, BM, WN, WM>;
   constexpr int FN = C::FN, FM = C::FM, TN = C::TN, TM = C::TM;
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // The BF16 128-token tiles take the lane index from an asm statement the
+  // compiler cannot hoist out of the tile loop.  Derived from threadIdx.x,
+  // it and the lane's LDS fragment addresses are computed once before the
+  // loop, kept across every epilogue, spilled there and reloaded behind its
+  // stores (L2 GEMM: 41 -> 8 scratch instructions, prefill L2 -1.2%).  The
+  // SwiGLU tiles keep the plain index: there the change measured no gain.
+  int lane = tid & 63;
+  if constexpr (EPI == NVFP4_EPI_BF16 && BM == 128) lane = lane_index();
   const int wn = wave % WN, wm = wave / WN;
   const int hf = lane >> 5, l32 = lane & 31;
   const int64_t N = p.N, K = p.K;
@@ -926,7 +944,7 @@ __device__ __forceinline__ bool run_tile(const Params& p, uint8_t* smem, const i
   asm volatile("" : "+v"(lane_x));
   const int t_next = resolve_claim(sc, __builtin_amdgcn_readfirstlane(*sc.s_claim));
   const bool has_next = t_next >= 0;
-  if (has_next) tile_at<BN, BM>(p, tprefix, t_next, nxt);
+  if (has_next) tile_at<BN, BM, EPI == NVFP4_EPI_BF16 && BM == 128>(p, tprefix, t_next, nxt);
   {
   const int lane = lane_x, hf = lane_x >> 5, l32 = lane_x & 31;
 
