@@ -62,6 +62,19 @@ __device__ __forceinline__ uint32_t e2m1_pack8(float v0, float v1, float v2, flo
   return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, v6, v7, 1.0f, 3);
 }
 
+// x / 6 rounded to nearest even, equal to the IEEE division for every fp32
+// x >= 2^-125 (checked exhaustively against it; below, where the quotient is
+// subnormal, the two can differ in the last place): the product with
+// RN(1/6), then one FMA correction by the remainder, which the FMA computes
+// exactly.  Callers use it where x >= 6 * 2^-9, or where the result is
+// discarded.
+__device__ __forceinline__ float div6_rn(float x) {
+  const float c = 0.16666667f;                 // RN(1/6), 0x3E2AAAAB
+  const float q0 = x * c;
+  const float r = __builtin_fmaf(-q0, 6.0f, x);
+  return __builtin_fmaf(r, c, q0);
+}
+
 // One 16-element block -> (8 bytes of packed codes, scale byte).
 // x[i] are the fp32 values, gs the global scale.  Operation order:
 // a_s = amax*gs; zero/underflow (amax == 0 or a_s < 6*2^-9) -> all zero;

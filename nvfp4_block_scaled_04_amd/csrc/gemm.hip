@@ -837,6 +837,7 @@ __device__ __forceinline__ void epilogue_bf16(const Params& p, float16v (&acc)[F
 // issue their first three stages at the start of the tile, in k_begin.
 template <int BN, int BM, int WN, int WM, int EPI, int FMT, int JV>
 __device__ __forceinline__ bool run_tile(const Params& p, uint8_t* smem, const int* tprefix,
+                                         const float* rtab,
                                          Sched& sc, const Tile& cur, uint32_t* coff,
                                          uint32_t* soff, int& claim, Tile& nxt) {
   using C = Cfg<BN, BM, WN, WM>;
@@ -1010,9 +1011,9 @@ __device__ __forceinline__ bool run_tile(const Params& p, uint8_t* smem, const i
           const bool zero = amax == 0.0f || a_s < kUnderflow;
           // every lane encodes (a zeroed block gives r = inf and is replaced):
           // no branch inside the block's chain
-          const float t = fminf(a_s / 6.0f, kE4m3Max);
+          const float t = fminf(div6_rn(a_s), kE4m3Max);   // a_s < 6 * 2^-9 is zeroed below
           const uint32_t sb = e4m3_encode(t);
-          const float r = gs_h / e4m3_decode(sb);
+          const float r = rtab[sb];                       // gs_h / e4m3_decode(sb)
           // sign | E2M1(min(|h*r|, 6)); r > 0, so h*r has the sign of h
           const uint32_t c = e2m1_pack8(h[0] * r, h[1] * r, h[2] * r, h[3] * r, h[4] * r,
                                         h[5] * r, h[6] * r, h[7] * r);
@@ -1074,6 +1075,13 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_gemm_kernel(Params p)
     __syncthreads();
   }
   __shared__ int s_claim[4];
+  // SwiGLU epilogue: gs_h / E4M3 value of every scale byte the requant can
+  // produce (0..0x7E; 0 gives inf, selected away), one IEEE division each per
+  // block instead of one per 16-column block and lane
+  __shared__ float rtab[EPI == NVFP4_EPI_SWIGLU_NVFP4 ? 128 : 1];
+  if constexpr (EPI == NVFP4_EPI_SWIGLU_NVFP4) {
+    if (tid < 128) rtab[tid] = uniform_load(p.gs_out, 0) / e4m3_decode((uint32_t)tid);
+  }
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   Sched sc;
   sc.total = (int64_t)tprefix[p.E] * p.n_tiles * p.ksplit;
@@ -1100,12 +1108,12 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_gemm_kernel(Params p)
     Tile nxt;
     bool more = false;
     if (cur.jv >= C::FM) {
-      more = run_tile<BN, BM, WN, WM, EPI, FMT, C::FM>(p, smem, tprefix, sc, cur, coff, soff, claim, nxt);
+      more = run_tile<BN, BM, WN, WM, EPI, FMT, C::FM>(p, smem, tprefix, rtab, sc, cur, coff, soff, claim, nxt);
     } else if constexpr (C::FM > 1) {
-      if (cur.jv == 1) more = run_tile<BN, BM, WN, WM, EPI, FMT, 1>(p, smem, tprefix, sc, cur, coff, soff, claim, nxt);
+      if (cur.jv == 1) more = run_tile<BN, BM, WN, WM, EPI, FMT, 1>(p, smem, tprefix, rtab, sc, cur, coff, soff, claim, nxt);
       else if constexpr (C::FM > 2) {
-        if (cur.jv == 2) more = run_tile<BN, BM, WN, WM, EPI, FMT, 2>(p, smem, tprefix, sc, cur, coff, soff, claim, nxt);
-        else if constexpr (C::FM > 3) more = run_tile<BN, BM, WN, WM, EPI, FMT, 3>(p, smem, tprefix, sc, cur, coff, soff, claim, nxt);
+        if (cur.jv == 2) more = run_tile<BN, BM, WN, WM, EPI, FMT, 2>(p, smem, tprefix, rtab, sc, cur, coff, soff, claim, nxt);
+        else if constexpr (C::FM > 3) more = run_tile<BN, BM, WN, WM, EPI, FMT, 3>(p, smem, tprefix, rtab, sc, cur, coff, soff, claim, nxt);
       }
     }
     cur = nxt;
