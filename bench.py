@@ -43,7 +43,7 @@ RIDGE = FP16_MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)   # flop per byte
 # each scaled by the ratio of known bytes to the counter's reading for a plain
 # 1 GiB device copy (--copy-calibration).  Reported only while the GEMM
 # sources hash to the value the counters were taken with; otherwise null.
-TRAFFIC = {("prefill", "l1", "nvfp4"): 5403335324, ("prefill", "l2", "nvfp4"): 3252467849}
+TRAFFIC = {("prefill", "l1", "nvfp4"): 5400768264, ("prefill", "l2", "nvfp4"): 3258744262}
 TRAFFIC_SRC_SHA = "e6092826da64e58e"
 
 
