@@ -268,6 +268,33 @@ def test_combine_rounding_exact_ties():
     assert np.array_equal(host(out).view(np.uint16), ref)
 
 
+@pytest.mark.parametrize("H", [7296, 14336])
+def test_combine_wide_rows_bit_exact(H):
+    """Rows wider than one pass of the combine's block (896 vectors of 8 BF16):
+    H = 7296 leaves a partial second vector per thread, H = 14336 two full
+    ones.  Power-of-two weights and values within 2^7 of each other make every
+    fp32 product and three-term sum exact, so the output bits must equal the
+    oracle's; a quarter of the slots point past the valid rows and add
+    nothing."""
+    rng = np.random.default_rng(H)
+    T, k, n_valid = 96, 3, 200                                 # rows >= 200 are never read
+    mant = 1.0 + rng.integers(0, 128, size=(T * k, H)) / 128.0
+    y = (rng.choice([-1.0, 1.0], size=(T * k, H)) * mant
+         * np.exp2(rng.integers(-3, 4, size=(T * k, H)))).astype(np.float32)
+    y_bits = (y.view(np.uint32) >> 16).astype(np.uint16)
+    assert np.array_equal((y_bits.astype(np.uint32) << 16).view(np.float32), y)
+    inv_perm = rng.integers(0, n_valid, size=T * k).astype(np.int32)
+    inv_perm[rng.random(T * k) < 0.25] = n_valid + 7            # invalid expert ids
+    w = np.exp2(rng.integers(-3, 2, size=(T, k))).astype(np.float32)
+    print(f"[case] combine wide rows T={T} H={H} k={k}", flush=True)
+    out = nv.moe_combine(_bits_to_dev(y_bits), torch.from_numpy(inv_perm).to(DEV),
+                         torch.from_numpy(w).to(DEV),
+                         torch.tensor([0, n_valid], dtype=torch.int32, device=DEV))
+    from oracle import moe as O
+    ref = O.combine(y_bits, inv_perm, w, n_valid)
+    assert np.array_equal(host(out).view(np.uint16), ref)
+
+
 @pytest.mark.parametrize("T,H,E,k,invalid", [(37, 256, 8, 3, True), (2048, 7168, 256, 8, False),
                                              (0, 256, 4, 2, False), (5, 128, 1, 1, False)])
 def test_quantize_scatter_bit_exact(T, H, E, k, invalid):
