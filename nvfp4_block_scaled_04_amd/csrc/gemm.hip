@@ -865,12 +865,31 @@ __device__ __forceinline__ bool run_tile(const Params& p, uint8_t* smem, const i
 
   KState<BN, BM, WN, WM, JV> st;
   st.wn = wn; st.wm = wm; st.hf = hf; st.l32 = l32;
+  {
+    // zero accumulators from the matrix pipe, idle until the first stage has
+    // landed: one MFMA of zero operands per block (0 * 0 + 0 = +0) instead of
+    // 16 v_accvgpr_write each.  The zero operands come from asm, so the
+    // compiler neither folds the products nor merges the 16 MFMAs into one
+    half8v za[FN], zb[FM];
 #pragma unroll
-  for (int i = 0; i < FN; ++i)
+    for (int i = 0; i < FN; ++i) {
+      int z;
+      asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+      za[i] = __builtin_bit_cast(half8v, make_int4(z, z, z, z));
+    }
 #pragma unroll
-    for (int j = 0; j < FM; ++j)
+    for (int j = 0; j < FM; ++j) {
+      int z;
+      asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+      zb[j] = __builtin_bit_cast(half8v, make_int4(z, z, z, z));
+    }
+    const float16v c0 = {};
 #pragma unroll
-      for (int r = 0; r < 16; ++r) st.acc[i][j][r] = 0.0f;
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+      for (int j = 0; j < FM; ++j)
+        st.acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(za[i], zb[j], c0, 0, 0, 0);
+  }
 
   // three LDS stage buffers, stage ks in buffer ks % 3 (four with AHEAD 3)
   const int nks = cur.nks;
