@@ -739,18 +739,20 @@ __device__ __forceinline__ void tile_offsets(const Params& p, const Tile& t, int
   };
   // token row of LDS row BN + i: clamped to the tile's last row, gathered.
   // SwiGLU launches (the ones that gather) read the gather index through a
-  // buffer resource that holds no records when there is no gather (an
-  // out-of-range buffer load returns 0 and touches no memory), so the loads
-  // need no branch and go out together: with a branch per row the compiler
-  // waited for each load in turn.
+  // buffer resource over the tile's own entries (based at row0, nrows
+  // records; none when there is no gather, and an out-of-range buffer load
+  // returns 0 and touches no memory), so the loads need no branch and go out
+  // together: with a branch per row the compiler waited for each load in
+  // turn.  Offsets stay below 512 bytes whatever M is.
   const bool gather = p.a_row_src != nullptr;
   const __amdgpu_buffer_rsrc_t grs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<int32_t*>(p.a_row_src), (short)0,
-      EPI == NVFP4_EPI_SWIGLU_NVFP4 && gather ? (int)(p.M * 4) : 0, 0x00020000);
+      const_cast<int32_t*>(gather ? p.a_row_src + t.row0 : nullptr), (short)0,
+      EPI == NVFP4_EPI_SWIGLU_NVFP4 && gather ? t.nrows * 4 : 0, 0x00020000);
   auto trow = [&](int i) -> uint32_t {
-    const int d = t.row0 + (i < t.nrows ? i : t.nrows - 1);
+    const int li = i < t.nrows ? i : t.nrows - 1;
+    const int d = t.row0 + li;
     if constexpr (EPI == NVFP4_EPI_SWIGLU_NVFP4) {
-      const int g = __builtin_amdgcn_raw_buffer_load_b32(grs, d * 4, 0, 0);
+      const int g = __builtin_amdgcn_raw_buffer_load_b32(grs, li * 4, 0, 0);
       // one select and one division for both cases, so no branch sinks the load
       return (uint32_t)((gather ? g : d) / (gather ? p.a_row_div : 1));
     } else {
